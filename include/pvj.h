@@ -1,0 +1,201 @@
+/*
+ * pvj.h -- C ABI of libpvj: packed variable-length joint text+image attention
+ * with per-sample 2D RoPE, for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (Mage-Flow pages):
+ *  - Mage-Flow review page (startedourmission.github.io), section
+ *    "Native-Resolution MMDiT": images of different resolutions become
+ *    variable-length latent token sequences, which are packed with their text
+ *    conditions (no padding) into one contiguous batch; per-sample cumulative
+ *    offsets confine attention to each sample without a block-diagonal mask;
+ *    text and image tokens of a sample are concatenated and processed by joint
+ *    self-attention; classifier-free guidance's conditional and unconditional
+ *    branches share one pack and one forward.
+ *  - same page, section "Mage-VAE": one latent token per 16x16 pixels.
+ *  - Hugging Face paper page (arXiv 2607.19064), "Highlights", and the model
+ *    card "microsoft/Mage-Flow", section "Architecture": per-sample 2D rotary
+ *    embeddings on the packed image+text sequence.
+ *  - Hugging Face model card, section "Python API": per-sample resolutions are
+ *    batched into one packed forward per denoising step.
+ *
+ * Conventions the pages leave open (fixed here, identical in every entry point):
+ *  - a sample is (h_lat, w_lat, l_text); its L = l_text + h_lat*w_lat tokens
+ *    are packed text first, then the image grid row-major; samples keep their
+ *    input order; T = sum of L over samples;
+ *  - RoPE position of text tokens is (0,0) (no rotation); image token p of a
+ *    sample sits at (p / w_lat, p % w_lat);
+ *  - 2D RoPE: dims [0, D/2) rotate by the row, [D/2, D) by the column; pair k
+ *    of an axis is dims (base+2k, base+2k+1) with angle pos*theta^(-k/(D/4));
+ *    (a,b) -> (a cos - b sin, a sin + b cos); V is never rotated;
+ *  - attention is non-causal; softmax_scale <= 0 selects 1/sqrt(D).
+ *
+ * Layout and ownership:
+ *  - every token tensor is contiguous row-major [T, H, D] (token stride H*D,
+ *    head stride D) in the plan's dtype; LSE is fp32 [H, T] (natural log);
+ *    base pointers must be 16-byte aligned; all are device pointers;
+ *  - the caller allocates and owns all device memory (tensors, LSE, the
+ *    metadata buffer, the backward workspace); the library allocates only host
+ *    memory (the plan);
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
+ *    device work is enqueued asynchronously on it; no entry point synchronises.
+ *
+ * Errors: every call returns a status; arguments are validated before anything
+ * is enqueued, so a failing call leaves the stream untouched.  A launch error
+ * reported by the HIP runtime maps to PVJ_ERR_HIP.  pvj_last_error() gives a
+ * human-readable detail of the last failure on the calling thread.
+ */
+#ifndef PVJ_H
+#define PVJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PVJ_API __attribute__((visibility("default")))
+
+typedef enum pvj_status {
+  PVJ_OK = 0,
+  PVJ_ERR_INVALID_ARG = 1,         /* null/misaligned pointer, negative size, bad enum */
+  PVJ_ERR_UNSUPPORTED = 2,         /* head_dim not in {64,128}, unsupported dtype/pairing */
+  PVJ_ERR_OVERFLOW = 3,            /* T or a per-sample length does not fit int32 */
+  PVJ_ERR_NOT_UPLOADED = 4,        /* compute call before pvj_plan_upload */
+  PVJ_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace / metadata buffer smaller than required */
+  PVJ_ERR_HIP = 6                  /* the HIP runtime reported an error */
+} pvj_status_t;
+
+enum { PVJ_BF16 = 0, PVJ_F32 = 1 };          /* pvj_plan_desc_t.dtype */
+enum { PVJ_ROPE_INTERLEAVED = 0 };           /* pvj_plan_desc_t.rope_pairing */
+enum { PVJ_FLAG_ROPE_FUSED = 1u };           /* attention flags */
+
+typedef struct pvj_sample {
+  int32_t h_lat;  /* latent rows    (image pixels / 16), >= 0 */
+  int32_t w_lat;  /* latent columns (image pixels / 16), >= 0 */
+  int32_t l_text; /* text tokens, >= 0 */
+} pvj_sample_t;
+
+typedef struct pvj_plan_desc {
+  int32_t n_heads;      /* H >= 1 */
+  int32_t head_dim;     /* D in {64, 128} */
+  int32_t dtype;        /* PVJ_BF16 or PVJ_F32: element type of every token tensor */
+  float rope_theta;     /* RoPE base, > 0 (10000) */
+  int32_t rope_pairing; /* PVJ_ROPE_INTERLEAVED */
+  int32_t text_first;   /* must be 1: text tokens precede image tokens in a sample */
+} pvj_plan_desc_t;
+
+typedef struct pvj_plan pvj_plan_t;
+
+/* ---- plan (pure host) -------------------------------------------------------
+ * pvj_plan_create: build the per-pack plan from the per-sample latent sizes
+ * (HF model card, "Python API": each sample its own resolution, one packed
+ * forward per step; review page, "Native-Resolution MMDiT": per-sample
+ * cumulative offsets).  It computes cu_seqlens (int32 [B+1], cu[0]=0,
+ * cu[i+1]=cu[i]+L_i), the per-sample metadata, the RoPE cos/sin tables (fp64
+ * math rounded to fp32) and the attention work lists (largest samples first,
+ * (sample, head) groups kept together and spread over the 8 XCDs).
+ * Zero-length samples are allowed.  n_samples may be 0.
+ * On success *out owns a new plan; free it with pvj_plan_destroy.
+ */
+PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samples,
+                                     const pvj_plan_desc_t* desc, pvj_plan_t** out);
+
+/* Sizes of a plan.  Any output pointer may be NULL.  *cu_seqlens_host points
+ * into the plan (B+1 int32, valid until destroy); *meta_bytes is the size of
+ * the device metadata buffer pvj_plan_upload needs. */
+PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* plan, int64_t* n_tokens, int32_t* max_len,
+                                   const int32_t** cu_seqlens_host, size_t* meta_bytes);
+
+/* Copy the plan's metadata into the caller-allocated device buffer `dev_meta`
+ * (>= meta_bytes, 256-byte aligned) on `stream`, and record it in the plan.
+ * Compute calls on this plan then read that buffer; it must stay allocated and
+ * unmodified while they run.  Calling it again re-targets the plan. */
+PVJ_API pvj_status_t pvj_plan_upload(pvj_plan_t* plan, void* dev_meta, size_t bytes, void* stream);
+
+/* Free the plan (host memory only).  Work already enqueued that uses the plan's
+ * device metadata is unaffected (the caller owns that buffer). */
+PVJ_API void pvj_plan_destroy(pvj_plan_t* plan);
+
+/* ---- the two modality streams ----------------------------------------------
+ * Review page, "Native-Resolution MMDiT": modality-specific layers keep text
+ * and image as two streams; their tokens are concatenated per sample for the
+ * joint attention.  text is [sum l_text, H, D], image [sum h*w, H, D], each
+ * stream packed in sample order without padding; joint is [T, H, D] with
+ * sample i's rows [text_i ; image_i].  pvj_unpack is the exact inverse.
+ * Buffers must not overlap.  Pure data movement (bit-exact).
+ */
+PVJ_API pvj_status_t pvj_pack(const pvj_plan_t* plan, const void* text, const void* image,
+                              void* joint, void* stream);
+PVJ_API pvj_status_t pvj_unpack(const pvj_plan_t* plan, const void* joint, void* text,
+                                void* image, void* stream);
+
+/* ---- standalone per-sample 2D RoPE ------------------------------------------
+ * HF paper page "Highlights" / model card "Architecture": per-sample 2D rotary
+ * embedding; review page, "Kernel fusion": RoPE application is one of the
+ * memory-bound ops.  y = R(pos) x on [T, H, D] (inverse != 0: y = R(pos)^T x).
+ * x == y (in place) is allowed; otherwise the buffers must not overlap.
+ * Computed in fp32 from the plan's tables, rounded once to the output dtype.
+ */
+PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* plan, const void* x, void* y,
+                                      int32_t inverse, void* stream);
+
+/* ---- attention forward -------------------------------------------------------
+ * For every sample i and head h: O_i = softmax(s * Q'_i K'_i^T) V_i over the
+ * sample's own L_i keys only (review page, "Native-Resolution MMDiT": joint
+ * self-attention confined by per-sample offsets), with Q' = R Q, K' = R K when
+ * flags has PVJ_FLAG_ROPE_FUSED (the rotation is applied on load) and Q' = Q,
+ * K' = K otherwise.  lse[h, t] = log sum_j exp(s q'_t . k'_j) (natural log,
+ * fp32; may be NULL if not needed).  bf16 inputs use bf16 matrix cores with
+ * fp32 accumulation and fp32 online softmax; fp32 inputs use fp32 matrix cores.
+ * o must not overlap q, k, v.  Deterministic: the same inputs give the same
+ * bits, and a sample's result does not depend on the rest of the pack.
+ */
+PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* plan, const void* q, const void* k,
+                                         const void* v, void* o, float* lse,
+                                         float softmax_scale, uint32_t flags, void* stream);
+
+/* ---- attention backward ------------------------------------------------------
+ * Gradients of sum(O * dO) (training uses forward + backward; review page,
+ * "Kernel fusion": 8-GPU training at ~50K packed tokens per GPU):
+ *   Delta = rowsum(dO * O); P = exp(s Q'K'^T - LSE); dV = P^T dO;
+ *   dS = P * (dO V^T - Delta); dQ' = s dS K'; dK' = s dS^T Q';
+ * with PVJ_FLAG_ROPE_FUSED, dQ = R^T dQ' and dK = R^T dK' (gradients with
+ * respect to the un-rotated Q, K); otherwise dQ = dQ', dK = dK'.
+ * q, k, v, o, lse and the flags/scale must be those of the forward call.
+ * workspace: device memory of at least pvj_varlen_attn_bwd_workspace bytes,
+ * 256-byte aligned, owned by the caller, contents need not be initialised;
+ * it holds the fp32 dQ accumulator and Delta.  dK and dV are deterministic;
+ * dQ is accumulated with fp32 atomics (order-dependent rounding).
+ */
+PVJ_API pvj_status_t pvj_varlen_attn_bwd_workspace(const pvj_plan_t* plan, size_t* bytes);
+PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* plan, const void* q, const void* k,
+                                         const void* v, const void* o, const float* lse,
+                                         const void* dout, void* dq, void* dk, void* dv,
+                                         void* workspace, size_t ws_bytes, float softmax_scale,
+                                         uint32_t flags, void* stream);
+
+/* ---- introspection (pure host; used by tests and tooling) -------------------- */
+
+/* Attention work list of the plan: which = 0 forward, 1 backward.  *items
+ * points to n_items int32 quadruples {sample, head, tile, 0} in launch order
+ * (sample = -1 marks an idle slot); *tile_rows is the rows of one tile
+ * (query rows forward, key rows backward).  Valid until destroy. */
+PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* plan, int32_t which,
+                                         const int32_t** items, int32_t* n_items,
+                                         int32_t* tile_rows);
+
+/* RoPE tables: cos/sin[p * n_freq + k] = cos/sin(p * theta^(-k/n_freq)), for
+ * p in [0, n_pos), k in [0, n_freq = D/4), fp32.  Valid until destroy. */
+PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* plan, const float** cos_tab,
+                                         const float** sin_tab, int32_t* n_pos, int32_t* n_freq);
+
+PVJ_API const char* pvj_status_string(pvj_status_t status);
+PVJ_API const char* pvj_last_error(void);
+PVJ_API const char* pvj_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PVJ_H */

@@ -1,0 +1,309 @@
+"""Python binding of libpvj: packed variable-length joint text+image attention
+with per-sample 2D RoPE on MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libpvj.so`` behind the C ABI declared in ``include/pvj.h``.  PyTorch supplies
+device memory and the current HIP stream.  There is no fallback: if the
+library is missing, importing the compute functions raises.
+
+    plan = Plan(samples=[(64, 64, 256), (64, 64, 16)], n_heads=24, head_dim=128,
+                dtype=torch.bfloat16)
+    plan.upload()                       # metadata -> device (torch buffer)
+    o, lse = varlen_attn_fwd(plan, q, k, v, rope_fused=True)
+    dq, dk, dv = varlen_attn_bwd(plan, q, k, v, o, lse, do, rope_fused=True)
+
+Tensors are contiguous ``[T, H, D]`` (packed tokens, heads, head dim); LSE is
+fp32 ``[H, T]``.  A sample is ``(h_lat, w_lat, l_text)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Optional, Sequence, Tuple
+
+__all__ = ["Plan", "PvjError", "pack", "unpack", "rope2d_apply", "varlen_attn_fwd",
+           "varlen_attn_bwd", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpvj.so")
+
+PVJ_BF16 = 0
+PVJ_F32 = 1
+PVJ_ROPE_INTERLEAVED = 0
+PVJ_FLAG_ROPE_FUSED = 1
+
+
+class PvjError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__("%s (%d): %s" % (name, status, detail))
+        self.status = status
+        self.name = name
+
+
+class _Sample(ctypes.Structure):
+    _fields_ = [("h_lat", ctypes.c_int32), ("w_lat", ctypes.c_int32), ("l_text", ctypes.c_int32)]
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rope_pairing", ctypes.c_int32), ("text_first", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpvj.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libpvj.so not found at %s; build it with "
+                          "`python -m packed_varlen_joint_amd._build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ, U32, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                               ctypes.c_uint32, ctypes.c_float)
+    sigs = {
+        "pvj_plan_create": (I32, [ctypes.POINTER(_Sample), I32, ctypes.POINTER(_Desc),
+                                  ctypes.POINTER(P)]),
+        "pvj_plan_info": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I32),
+                                ctypes.POINTER(ctypes.POINTER(I32)), ctypes.POINTER(SZ)]),
+        "pvj_plan_upload": (I32, [P, P, SZ, P]),
+        "pvj_plan_destroy": (None, [P]),
+        "pvj_pack": (I32, [P, P, P, P, P]),
+        "pvj_unpack": (I32, [P, P, P, P, P]),
+        "pvj_rope2d_apply": (I32, [P, P, P, I32, P]),
+        "pvj_varlen_attn_fwd": (I32, [P, P, P, P, P, P, F, U32, P]),
+        "pvj_varlen_attn_bwd_workspace": (I32, [P, ctypes.POINTER(SZ)]),
+        "pvj_varlen_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, F, U32, P]),
+        "pvj_plan_work_items": (I32, [P, I32, ctypes.POINTER(ctypes.POINTER(I32)),
+                                      ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "pvj_plan_rope_table": (I32, [P, ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
+                                      ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
+                                      ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "pvj_status_string": (ctypes.c_char_p, [I32]),
+        "pvj_last_error": (ctypes.c_char_p, []),
+        "pvj_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise PvjError(status, lib.pvj_status_string(status).decode(),
+                       lib.pvj_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dtype) -> int:
+    torch = _torch()
+    if dtype in (torch.bfloat16, "bf16"):
+        return PVJ_BF16
+    if dtype in (torch.float32, "f32"):
+        return PVJ_F32
+    raise ValueError("dtype must be bfloat16 or float32, got %r" % (dtype,))
+
+
+class Plan:
+    """Per-pack plan: offsets, RoPE tables and work lists (built on the host by
+    ``pvj_plan_create``), plus the device copy of that metadata."""
+
+    def __init__(self, samples: Sequence[Tuple[int, int, int]], n_heads: int, head_dim: int,
+                 dtype="bf16", rope_theta: float = 10000.0):
+        lib = load_library()
+        self.samples = [tuple(int(x) for x in s) for s in samples]
+        arr = (_Sample * max(1, len(self.samples)))(*[_Sample(*s) for s in self.samples])
+        desc = _Desc(int(n_heads), int(head_dim), _dtype_code(dtype), float(rope_theta),
+                     PVJ_ROPE_INTERLEAVED, 1)
+        h = ctypes.c_void_p()
+        _check(lib.pvj_plan_create(arr, len(self.samples), ctypes.byref(desc), ctypes.byref(h)))
+        self._h = h
+        self.n_heads = int(n_heads)
+        self.head_dim = int(head_dim)
+        self.dtype_code = desc.dtype
+        T = ctypes.c_int64()
+        ml = ctypes.c_int32()
+        cu = ctypes.POINTER(ctypes.c_int32)()
+        mb = ctypes.c_size_t()
+        _check(lib.pvj_plan_info(h, ctypes.byref(T), ctypes.byref(ml), ctypes.byref(cu),
+                                 ctypes.byref(mb)))
+        self.n_tokens = T.value
+        self.max_len = ml.value
+        self.cu_seqlens = [cu[i] for i in range(len(self.samples) + 1)]
+        self.meta_bytes = mb.value
+        self.n_text = sum(s[2] for s in self.samples)
+        self.n_image = sum(s[0] * s[1] for s in self.samples)
+        self._meta = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def torch_dtype(self):
+        torch = _torch()
+        return torch.bfloat16 if self.dtype_code == PVJ_BF16 else torch.float32
+
+    def upload(self, device=None, stream=None) -> "Plan":
+        """Copy the metadata into a torch-allocated device buffer on ``device``."""
+        torch = _torch()
+        device = torch.device(device) if device is not None else torch.device(
+            "cuda", torch.cuda.current_device())
+        with torch.cuda.device(device):
+            buf = torch.empty(max(256, self.meta_bytes), dtype=torch.uint8, device=device)
+            s = stream if stream is not None else torch.cuda.current_stream()
+            _check(load_library().pvj_plan_upload(self._h, buf.data_ptr(), buf.numel(),
+                                                  s.cuda_stream))
+        self._meta = buf
+        return self
+
+    def work_items(self, which: int):
+        """(items [n][4] list, tile_rows) of the forward (0) or backward (1) work list."""
+        lib = load_library()
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int32()
+        tr = ctypes.c_int32()
+        _check(lib.pvj_plan_work_items(self._h, which, ctypes.byref(p), ctypes.byref(n),
+                                       ctypes.byref(tr)))
+        return [tuple(p[4 * i + j] for j in range(4)) for i in range(n.value)], tr.value
+
+    def rope_table(self):
+        lib = load_library()
+        c = ctypes.POINTER(ctypes.c_float)()
+        s = ctypes.POINTER(ctypes.c_float)()
+        npos = ctypes.c_int32()
+        nf = ctypes.c_int32()
+        _check(lib.pvj_plan_rope_table(self._h, ctypes.byref(c), ctypes.byref(s),
+                                       ctypes.byref(npos), ctypes.byref(nf)))
+        n = npos.value * nf.value
+        return [c[i] for i in range(n)], [s[i] for i in range(n)], npos.value, nf.value
+
+    def bwd_workspace_bytes(self) -> int:
+        b = ctypes.c_size_t()
+        _check(load_library().pvj_varlen_attn_bwd_workspace(self._h, ctypes.byref(b)))
+        return b.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load_library().pvj_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _check_tokens(plan: Plan, name: str, t, rows: Optional[int] = None):
+    torch = _torch()
+    rows = plan.n_tokens if rows is None else rows
+    want = (rows, plan.n_heads, plan.head_dim)
+    if tuple(t.shape) != want:
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), want))
+    if t.dtype != plan.torch_dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, plan.torch_dtype))
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+
+
+def _empty_tokens(plan: Plan, like, rows=None):
+    torch = _torch()
+    rows = plan.n_tokens if rows is None else rows
+    return torch.empty((rows, plan.n_heads, plan.head_dim), dtype=plan.torch_dtype,
+                       device=like.device)
+
+
+def pack(plan: Plan, text, image, joint=None):
+    """Joint [T,H,D] from the text [sum t,H,D] and image [sum h*w,H,D] streams."""
+    _check_tokens(plan, "text", text, plan.n_text)
+    _check_tokens(plan, "image", image, plan.n_image)
+    joint = _empty_tokens(plan, text) if joint is None else joint
+    _check_tokens(plan, "joint", joint)
+    _check(load_library().pvj_pack(plan.handle, _ptr(text), _ptr(image), _ptr(joint), _stream()))
+    return joint
+
+
+def unpack(plan: Plan, joint, text=None, image=None):
+    """Inverse of ``pack``: (text, image) streams from the joint tensor."""
+    _check_tokens(plan, "joint", joint)
+    text = _empty_tokens(plan, joint, plan.n_text) if text is None else text
+    image = _empty_tokens(plan, joint, plan.n_image) if image is None else image
+    _check_tokens(plan, "text", text, plan.n_text)
+    _check_tokens(plan, "image", image, plan.n_image)
+    _check(load_library().pvj_unpack(plan.handle, _ptr(joint), _ptr(text), _ptr(image),
+                                     _stream()))
+    return text, image
+
+
+def rope2d_apply(plan: Plan, x, y=None, inverse: bool = False):
+    """Per-sample 2D RoPE of x [T,H,D] into y (y is x: in place)."""
+    _check_tokens(plan, "x", x)
+    y = _empty_tokens(plan, x) if y is None else y
+    _check_tokens(plan, "y", y)
+    _check(load_library().pvj_rope2d_apply(plan.handle, _ptr(x), _ptr(y), int(bool(inverse)),
+                                           _stream()))
+    return y
+
+
+def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused: bool = False,
+                    out=None, lse=None, want_lse: bool = True):
+    """Packed varlen joint attention forward; returns (O [T,H,D], LSE fp32 [H,T] or None)."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_tokens(plan, n, t)
+    out = _empty_tokens(plan, q) if out is None else out
+    _check_tokens(plan, "out", out)
+    if lse is None and want_lse:
+        lse = torch.empty((plan.n_heads, plan.n_tokens), dtype=torch.float32, device=q.device)
+    flags = PVJ_FLAG_ROPE_FUSED if rope_fused else 0
+    _check(load_library().pvj_varlen_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                              _ptr(lse), float(softmax_scale), flags, _stream()))
+    return out, lse
+
+
+def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.0,
+                    rope_fused: bool = False, dq=None, dk=None, dv=None, workspace=None):
+    """Packed varlen joint attention backward; returns (dQ, dK, dV)."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tokens(plan, n, t)
+    dq = _empty_tokens(plan, q) if dq is None else dq
+    dk = _empty_tokens(plan, q) if dk is None else dk
+    dv = _empty_tokens(plan, q) if dv is None else dv
+    nbytes = plan.bwd_workspace_bytes()
+    if workspace is None:
+        workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=q.device)
+    flags = PVJ_FLAG_ROPE_FUSED if rope_fused else 0
+    _check(load_library().pvj_varlen_attn_bwd(
+        plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), float(softmax_scale), flags,
+        _stream()))
+    return dq, dk, dv

@@ -1,0 +1,319 @@
+// Packed variable-length joint attention, forward, for gfx950.
+//
+// Mage-Flow review page, section "Native-Resolution MMDiT": joint
+// self-attention over each sample's text+image tokens, confined to the sample
+// by per-sample cumulative offsets (no block-diagonal mask); HF paper page,
+// "Highlights": per-sample 2D RoPE, applied here on load when requested.
+//
+// One workgroup = one work item (sample, head, 128-query tile); 4 waves, each
+// owning 32 queries.  The KV loop streams 64-key tiles of the item's own
+// sample only, through a double-buffered LDS stage.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16; fp32 inputs use eight
+// v_mfma_f32_32x32x2_f32 per k-step of 16):
+//  * scores are computed transposed, S^T = K Q^T: the accumulator of lane l
+//    holds query l % 32 against 16 keys, and lane l ^ 32 the other 16 keys of
+//    the same 32-key block.  Row max and row sum are therefore lane-local plus
+//    one v_permlane32_swap per tile; the running max m and sum l (fp32) live in
+//    registers of the wave that owns the query.
+//  * key k of a tile is stored in LDS row sigma(k) (bits 2 and 3 swapped).
+//    With that order, accumulator register r of lane l holds key
+//    16*(r/8) + 8*(l/32) + r%8 of its 32-key block, so the eight probabilities
+//    of registers 8s..8s+7 are exactly the B operand (P^T, k = keys) of the
+//    output product O^T = V^T P^T, and the matching V^T operand is eight
+//    consecutive keys of one d: a single 16-byte LDS read from V stored
+//    transposed.
+//  * the output accumulator O^T of lane l holds query l % 32, so the online
+//    softmax rescale is lane-local too.
+// Online softmax in base 2: x = s * scale * log2(e); p = 2^(x - m);
+// LSE = (m + log2 l) * ln 2.  Keys at or past the sample end are masked to
+// -inf; their K/V rows are zero-filled, never read.
+
+#include "pvj_device.h"
+#include "pvj_launch.h"
+
+namespace pvj {
+
+constexpr int kFwdBM = 128;  // query rows per workgroup (must match fwd_tile_rows)
+constexpr int kFwdBN = 64;   // keys per KV tile
+constexpr int kFwdThreads = 256;
+
+// key row permutation inside a 32-key block: swap bits 2 and 3
+__device__ __forceinline__ int sigma(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// XOR swizzle of the 8-element units of a V^T row (d): spreads both the
+// transposing writes (8 d-rows 8 apart) and the operand reads (8 consecutive d)
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+template <typename T, int D>
+struct FwdTile {
+  static constexpr int UPR = D / 8;                         // 8-element units per K row
+  static constexpr int NK = kFwdBN * UPR / kFwdThreads;     // K units per thread per tile
+  static constexpr int KPT = NK;                            // keys per thread in the V loader
+  static constexpr int K_ELEMS = kFwdBN * D;
+  static constexpr size_t SMEM = 2 * 2 * (size_t)K_ELEMS * sizeof(T);
+};
+
+template <typename T, int D, bool ROPE>
+__global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* __restrict__ Q,
+                                                               const T* __restrict__ K,
+                                                               const T* __restrict__ V,
+                                                               T* __restrict__ O,
+                                                               float* __restrict__ LSE,
+                                                               float scale_log2) {
+  typedef typename Vec8<T>::type V8;
+  typedef FwdTile<T, D> C;
+  constexpr int KS = D / 16;  // k-steps of 16 over the head dim
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int NK = C::NK;
+  constexpr int KPT = C::KPT;
+  constexpr int UPR = C::UPR;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* const ks_lds = reinterpret_cast<T*>(smem_raw);           // [2][BN][D]
+  T* const vt_lds = ks_lds + 2 * C::K_ELEMS;                  // [2][D][BN]
+
+  const Item it = m.fwd_items[blockIdx.x];
+  if (it.sample < 0) return;
+  const SampleInfo si = m.sinfo[it.sample];
+  const int L = si.len;
+  const size_t RS = (size_t)m.n_heads * D;  // row stride (elements)
+  const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+  const T* Qh = Q + base;
+  const T* Kh = K + base;
+  const T* Vh = V + base;
+  T* Oh = O + base;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qi = it.tile * kFwdBM + wave * 32 + l32;  // this lane's query (local index)
+
+  // ---- Q fragments (B operand of S^T = K Q^T), rotated on load if ROPE ----
+  V8 qf[KS];
+  {
+    int qr = 0, qc = 0;
+    if (ROPE && qi < L) token_pos(qi, si.l_text, si.w_lat, qr, qc);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int unit = 2 * ks + hi;
+      V8 v = {};
+      if (qi < L) {
+        v = load8<T>(Qh + (size_t)qi * RS + unit * 8);
+        if (ROPE)
+          v = from_f32x8<T>(rope_chunk(to_f32x8(v), unit, D, qr, qc, m.cos_tab, m.sin_tab,
+                                       m.n_freq, false));
+      }
+      qf[ks] = v;
+    }
+  }
+
+  // ---- tile loaders: global -> registers (next tile) -> LDS ----
+  const int k_unit = tid % UPR;          // K loader: unit of the row
+  const int k_row0 = tid / UPR;          // rows k_row0 + i * (256 / UPR)
+  constexpr int K_ROW_STEP = kFwdThreads / UPR;
+  const int v_dc = tid % UPR;            // V loader: d-chunk (8 d's)
+  const int v_k0 = (tid / UPR) * KPT;    // V loader: first of KPT keys
+  V8 kreg[NK], vreg[KPT];
+  f32x4 kcs[ROPE ? NK : 1], ksn[ROPE ? NK : 1];
+
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+      V8 z = {};
+      kreg[i] = kk < L ? load8<T>(Kh + (size_t)kk * RS + k_unit * 8) : z;
+      if (ROPE) {
+        int r = 0, c = 0;
+        if (kk < L) token_pos(kk, si.l_text, si.w_lat, r, c);
+        const int half_units = D / 16;
+        const bool col = k_unit >= half_units;
+        const int pos = col ? c : r;
+        const int k0 = (k_unit - (col ? half_units : 0)) * 4;
+        kcs[i] = *reinterpret_cast<const f32x4*>(m.cos_tab + (size_t)pos * m.n_freq + k0);
+        ksn[i] = *reinterpret_cast<const f32x4*>(m.sin_tab + (size_t)pos * m.n_freq + k0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int kk = kv0 + v_k0 + i;
+      V8 z = {};
+      vreg[i] = kk < L ? load8<T>(Vh + (size_t)kk * RS + v_dc * 8) : z;
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    T* kb = ks_lds + buf * C::K_ELEMS;
+    T* vb = vt_lds + buf * C::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      V8 v = kreg[i];
+      if (ROPE) {
+        f32x8 x = to_f32x8(v), y;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a = x[2 * q], b = x[2 * q + 1];
+          y[2 * q] = a * kcs[i][q] - b * ksn[i][q];
+          y[2 * q + 1] = a * ksn[i][q] + b * kcs[i][q];
+        }
+        v = from_f32x8<T>(y);
+      }
+      const int rho = sigma(k_row0 + i * K_ROW_STEP);
+      store8<T>(kb + rho * D + ((k_unit ^ (rho & 7)) * 8), v);
+    }
+    // transpose: for each of the 8 d's of the chunk, KPT consecutive keys
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = v_dc * 8 + j;
+      T* dst = vb + d * kFwdBN + (((v_k0 >> 3) ^ vt_swz(d)) << 3) + (v_k0 & 7);
+      typedef T VK __attribute__((ext_vector_type(KPT)));
+      VK w;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) w[i] = vreg[i][j];
+      *reinterpret_cast<VK*>(dst) = w;
+    }
+  };
+
+  const int nkv = (L + kFwdBN - 1) / kFwdBN;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    const int kv0 = j * kFwdBN;
+    if (j + 1 < nkv) load_tile(kv0 + kFwdBN);
+    const T* kb_lds = ks_lds + buf * C::K_ELEMS;
+    const T* vb_lds = vt_lds + buf * C::K_ELEMS;
+
+    // S^T = K Q^T for the two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const int rho = kb * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const V8 a = load8<T>(kb_lds + rho * D + (((2 * ks + hi) ^ (rho & 7)) << 3));
+        mma16(s[kb], a, qf[ks]);
+      }
+    }
+    // mask keys past the sample end (last tile only)
+    if (kv0 + kFwdBN > L) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+          if (key >= L) s[kb][r] = -INFINITY;
+        }
+    }
+    // online softmax (base 2)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_pair32(mx);
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = fast_exp2(m_run - m_new);
+    float ls = 0.f;
+    V8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_new));
+        ls += p;
+        pf[kb][r >> 3][r & 7] = (T)p;
+      }
+    l_run = fmaf(l_run, alpha, ls);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + l32;
+      const T* vrow = vb_lds + d * kFwdBN;
+      const int sw = vt_swz(d);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const V8 a = load8<T>(vrow + (((4 * kb + 2 * st + hi) ^ sw) << 3));
+          mma16(oacc[db], a, pf[kb][st]);
+        }
+    }
+    if (j + 1 < nkv) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, LSE ----
+  const float l_tot = sum_pair32(l_run);
+  if (qi < L) {
+    const float inv = 1.f / l_tot;
+    T* orow = Oh + (size_t)qi * RS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hi;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[db][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + d) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + d) = w;
+        }
+      }
+    if (hi == 0 && LSE)
+      LSE[(size_t)it.head * m.n_tokens + si.start + qi] =
+          (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+template <typename T, int D, bool ROPE>
+static hipError_t launch_fwd_t(const Meta& m, const void* q, const void* k, const void* v, void* o,
+                               float* lse, float scale_log2, hipStream_t stream) {
+  auto kern = attn_fwd_kernel<T, D, ROPE>;
+  const size_t smem = FwdTile<T, D>::SMEM;
+  static bool attr_set = false;  // per instantiation; idempotent, so a race is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<dim3(m.n_fwd), dim3(kFwdThreads), smem, stream>>>(m, (const T*)q, (const T*)k,
+                                                           (const T*)v, (T*)o, lse, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
+                           const void* v, void* o, float* lse, float scale, bool rope,
+                           hipStream_t stream) {
+  if (m.n_fwd == 0) return hipSuccess;
+  const float sl2 = scale * 1.4426950408889634f;
+  const bool bf = p->desc.dtype == PVJ_BF16;
+  const int D = p->desc.head_dim;
+#define PVJ_FWD(TT, DD)                                                                    \
+  return rope ? launch_fwd_t<TT, DD, true>(m, q, k, v, o, lse, sl2, stream)                \
+              : launch_fwd_t<TT, DD, false>(m, q, k, v, o, lse, sl2, stream)
+  if (bf && D == 128) PVJ_FWD(bf16, 128);
+  if (bf && D == 64) PVJ_FWD(bf16, 64);
+  if (!bf && D == 128) PVJ_FWD(float, 128);
+  PVJ_FWD(float, 64);
+#undef PVJ_FWD
+}
+
+}  // namespace pvj

@@ -1,0 +1,188 @@
+// C-ABI entry points that touch the device: metadata upload, pack/unpack,
+// standalone RoPE, attention forward and backward.  Every argument is
+// validated before anything is enqueued; a failing call leaves the stream
+// untouched.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pvj_internal.h"
+#include "pvj_launch.h"
+
+using namespace pvj;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t elt_size(const pvj_plan* p) { return p->desc.dtype == PVJ_BF16 ? 2 : 4; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+pvj_status_t check_ptr(const void* ptr, const char* name, bool needed) {
+  if (!needed) return PVJ_OK;
+  if (!ptr) return fail(PVJ_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(PVJ_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return PVJ_OK;
+}
+
+pvj_status_t check_plan(const pvj_plan* p) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (!p->dev_meta) return fail(PVJ_ERR_NOT_UPLOADED, "plan metadata not uploaded");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PVJ_ERR_HIP, "hipGetDevice failed");
+  if (dev != p->dev_id)
+    return fail(PVJ_ERR_INVALID_ARG, "plan uploaded on device %d, current device is %d",
+                p->dev_id, dev);
+  return PVJ_OK;
+}
+
+pvj_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PVJ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PVJ_OK;
+}
+
+float resolve_scale(const pvj_plan* p, float s) {
+  return s > 0.f ? s : 1.0f / std::sqrt((float)p->desc.head_dim);
+}
+
+size_t ws_dq_bytes(const pvj_plan* p) {
+  return align256((size_t)p->n_tokens * p->desc.n_heads * p->desc.head_dim * sizeof(float));
+}
+size_t ws_delta_bytes(const pvj_plan* p) {
+  return align256((size_t)p->n_tokens * p->desc.n_heads * sizeof(float));
+}
+
+#define PVJ_TRY(x)                  \
+  do {                              \
+    pvj_status_t st__ = (x);        \
+    if (st__ != PVJ_OK) return st__; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+PVJ_API pvj_status_t pvj_plan_upload(pvj_plan_t* p, void* dev_meta, size_t bytes, void* stream) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (!dev_meta) return fail(PVJ_ERR_INVALID_ARG, "dev_meta is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_meta) % kMetaAlign)
+    return fail(PVJ_ERR_INVALID_ARG, "dev_meta is not %zu-byte aligned", kMetaAlign);
+  if (bytes < p->image_bytes)
+    return fail(PVJ_ERR_WORKSPACE_TOO_SMALL, "metadata buffer %zu < %zu bytes", bytes,
+                p->image_bytes);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PVJ_ERR_HIP, "hipGetDevice failed");
+  hipError_t e = hipMemcpyAsync(dev_meta, p->image, p->image_bytes, hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PVJ_ERR_HIP, "metadata upload: %s", hipGetErrorString(e));
+  p->dev_meta = dev_meta;
+  p->dev_id = dev;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_pack(const pvj_plan_t* p, const void* text, const void* image,
+                              void* joint, void* stream) {
+  PVJ_TRY(check_plan(p));
+  PVJ_TRY(check_ptr(text, "text", p->n_text > 0));
+  PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
+  PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
+  return launched(launch_pack(p, device_meta(p), text, image, joint, false,
+                              static_cast<hipStream_t>(stream)),
+                  "pack");
+}
+
+PVJ_API pvj_status_t pvj_unpack(const pvj_plan_t* p, const void* joint, void* text, void* image,
+                                void* stream) {
+  PVJ_TRY(check_plan(p));
+  PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
+  PVJ_TRY(check_ptr(text, "text", p->n_text > 0));
+  PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
+  return launched(launch_pack(p, device_meta(p), text, image, const_cast<void*>(joint), true,
+                              static_cast<hipStream_t>(stream)),
+                  "unpack");
+}
+
+PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* p, const void* x, void* y,
+                                      int32_t inverse, void* stream) {
+  PVJ_TRY(check_plan(p));
+  PVJ_TRY(check_ptr(x, "x", p->n_tokens > 0));
+  PVJ_TRY(check_ptr(y, "y", p->n_tokens > 0));
+  if (x != y && p->n_tokens > 0) {
+    const size_t n = (size_t)p->n_tokens * p->desc.n_heads * p->desc.head_dim * elt_size(p);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    if (a < b + n && b < a + n) return fail(PVJ_ERR_INVALID_ARG, "x and y partially overlap");
+  }
+  return launched(launch_rope2d(p, device_meta(p), x, y, inverse != 0,
+                                static_cast<hipStream_t>(stream)),
+                  "rope2d_apply");
+}
+
+PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* p, const void* q, const void* k,
+                                         const void* v, void* o, float* lse,
+                                         float softmax_scale, uint32_t flags, void* stream) {
+  PVJ_TRY(check_plan(p));
+  const bool need = p->n_tokens > 0;
+  PVJ_TRY(check_ptr(q, "q", need));
+  PVJ_TRY(check_ptr(k, "k", need));
+  PVJ_TRY(check_ptr(v, "v", need));
+  PVJ_TRY(check_ptr(o, "o", need));
+  if (lse && !aligned16(lse)) return fail(PVJ_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+  if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
+  return launched(launch_attn_fwd(p, device_meta(p), q, k, v, o, lse,
+                                  resolve_scale(p, softmax_scale),
+                                  (flags & PVJ_FLAG_ROPE_FUSED) != 0,
+                                  static_cast<hipStream_t>(stream)),
+                  "varlen_attn_fwd");
+}
+
+PVJ_API pvj_status_t pvj_varlen_attn_bwd_workspace(const pvj_plan_t* p, size_t* bytes) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (!bytes) return fail(PVJ_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_dq_bytes(p) + ws_delta_bytes(p);
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, const void* k,
+                                         const void* v, const void* o, const float* lse,
+                                         const void* dout, void* dq, void* dk, void* dv,
+                                         void* workspace, size_t ws_bytes, float softmax_scale,
+                                         uint32_t flags, void* stream) {
+  PVJ_TRY(check_plan(p));
+  const bool need = p->n_tokens > 0;
+  PVJ_TRY(check_ptr(q, "q", need));
+  PVJ_TRY(check_ptr(k, "k", need));
+  PVJ_TRY(check_ptr(v, "v", need));
+  PVJ_TRY(check_ptr(o, "o", need));
+  PVJ_TRY(check_ptr(lse, "lse", need));
+  PVJ_TRY(check_ptr(dout, "dout", need));
+  PVJ_TRY(check_ptr(dq, "dq", need));
+  PVJ_TRY(check_ptr(dk, "dk", need));
+  PVJ_TRY(check_ptr(dv, "dv", need));
+  if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
+  const size_t need_ws = ws_dq_bytes(p) + ws_delta_bytes(p);
+  if (need) {
+    if (!workspace) return fail(PVJ_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(PVJ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (ws_bytes < need_ws)
+      return fail(PVJ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  }
+  if (!need) return PVJ_OK;
+  const Meta m = device_meta(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool rope = (flags & PVJ_FLAG_ROPE_FUSED) != 0;
+  const float scale = resolve_scale(p, softmax_scale);
+  float* dq_acc = static_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_dq_bytes(p));
+  PVJ_TRY(launched(launch_bwd_pre(p, m, o, dout, delta, dq_acc, s), "bwd preprocess"));
+  PVJ_TRY(launched(launch_attn_bwd(p, m, q, k, v, dout, lse, delta, dq_acc, dk, dv, scale, rope, s),
+                   "varlen_attn_bwd"));
+  return launched(launch_dq_finalize(p, m, dq_acc, dq, rope, s), "dq finalize");
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Device helpers for the gfx950 kernels: vector types, bf16 conversion,
+// matrix-core wrappers, token positions and the per-chunk 2D rotation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pvj_internal.h"
+
+namespace pvj {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Eight consecutive elements of a row: the unit every kernel moves and the
+// operand one lane feeds to one 32x32 matrix-core k-step of 16.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { typedef bf16x8 type; };
+template <> struct Vec8<float> { typedef f32x8 type; };
+
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type load8(const T* p) {
+  return *reinterpret_cast<const typename Vec8<T>::type*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, typename Vec8<T>::type v) {
+  *reinterpret_cast<typename Vec8<T>::type*>(p) = v;
+}
+
+__device__ __forceinline__ f32x8 to_f32x8(bf16x8 v) {
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (float)v[i];
+  return r;
+}
+__device__ __forceinline__ f32x8 to_f32x8(f32x8 v) { return v; }
+
+template <typename T> __device__ __forceinline__ typename Vec8<T>::type from_f32x8(f32x8 v);
+template <> __device__ __forceinline__ bf16x8 from_f32x8<bf16>(f32x8 v) {
+  bf16x8 r;  // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)v[i];
+  return r;
+}
+template <> __device__ __forceinline__ f32x8 from_f32x8<float>(f32x8 v) { return v; }
+
+// acc(32x32) += A(32x16) * B(16x32) on the matrix cores.  Lane l feeds row
+// (A) or column (B) l % 32 with eight k-values; lanes l and l + 32 feed the
+// two k-halves.  bf16: one v_mfma_f32_32x32x16_bf16.  fp32: eight
+// v_mfma_f32_32x32x2_f32, element j of both operands forming k-step j.
+__device__ __forceinline__ void mma16(f32x16& acc, bf16x8 a, bf16x8 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16& acc, f32x8 a, f32x8 b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+// exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max of a value held by lanes l and l ^ 32 (v_permlane32_swap)
+__device__ __forceinline__ float max_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The sample holding packed row `tok`: the i with cu[i] <= tok < cu[i+1].
+__device__ __forceinline__ int find_sample(const int32_t* cu, int n_samples, int tok) {
+  int lo = 1, hi = n_samples;  // first j in [1, n] with cu[j] > tok
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] > tok) hi = mid; else lo = mid + 1;
+  }
+  return lo - 1;
+}
+
+// RoPE position (row, col) of local token j: text tokens first at (0, 0), then
+// the image grid row-major.
+__device__ __forceinline__ void token_pos(int j, int l_text, int w_lat, int& r, int& c) {
+  if (j < l_text) {
+    r = 0;
+    c = 0;
+  } else {
+    int p = j - l_text;
+    r = p / w_lat;
+    c = p - r * w_lat;
+  }
+}
+
+// Rotate the 8-element chunk `chunk` (dims 8*chunk .. 8*chunk+7) of one head
+// row at position (r, c): dims [0, D/2) use the row, [D/2, D) the column;
+// pairs (2k, 2k+1) turn by pos * omega_k, with cos/sin read from the plan's
+// tables.  inverse turns by -angle.
+__device__ __forceinline__ f32x8 rope_chunk(f32x8 x, int chunk, int head_dim, int r, int c,
+                                            const float* cos_tab, const float* sin_tab,
+                                            int n_freq, bool inverse) {
+  const int half_chunks = head_dim / 16;
+  const bool col = chunk >= half_chunks;
+  const int pos = col ? c : r;
+  const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
+  const f32x4 cs = *reinterpret_cast<const f32x4*>(cos_tab + (size_t)pos * n_freq + k0);
+  f32x4 sn = *reinterpret_cast<const f32x4*>(sin_tab + (size_t)pos * n_freq + k0);
+  if (inverse) sn = -sn;
+  f32x8 y;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float a = x[2 * m], b = x[2 * m + 1];
+    y[2 * m] = a * cs[m] - b * sn[m];
+    y[2 * m + 1] = a * sn[m] + b * cs[m];
+  }
+  return y;
+}
+
+}  // namespace pvj

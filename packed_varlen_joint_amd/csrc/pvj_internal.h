@@ -1,0 +1,81 @@
+// Internal declarations shared by the planner, the C-ABI glue and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pvj.h"
+
+namespace pvj {
+
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs; workgroups are dealt round-robin
+constexpr size_t kMetaAlign = 256;  // alignment of every metadata section
+
+// Rows of one attention work item.  Forward: query rows per workgroup.
+// Backward: key rows per workgroup.
+inline int fwd_tile_rows(int dtype, int head_dim) {
+  (void)dtype; (void)head_dim;
+  return 128;
+}
+inline int bwd_tile_rows(int dtype, int head_dim) {
+  (void)dtype; (void)head_dim;
+  return 128;
+}
+
+struct Item {  // one attention work item; sample < 0 marks an idle slot
+  int32_t sample, head, tile, pad;
+};
+
+struct SampleInfo {  // per-sample metadata read by the kernels
+  int32_t start;   // first packed row (cu_seqlens[i])
+  int32_t len;     // L_i
+  int32_t l_text;  // text rows at the start of the sample
+  int32_t w_lat;   // latent grid width (image token p is at (p / w, p % w))
+};
+
+// Device view of an uploaded plan (pointers into the caller's metadata buffer).
+struct Meta {
+  const int32_t* cu;        // [B+1]
+  const int32_t* cu_text;   // [B+1]
+  const int32_t* cu_img;    // [B+1]
+  const SampleInfo* sinfo;  // [B]
+  const float* cos_tab;     // [n_pos][n_freq]
+  const float* sin_tab;     // [n_pos][n_freq]
+  const Item* fwd_items;    // [n_fwd]
+  const Item* bwd_items;    // [n_bwd]
+  int32_t n_samples, n_tokens, n_heads, head_dim;
+  int32_t n_pos, n_freq, n_fwd, n_bwd;
+  int32_t fwd_tile, bwd_tile, n_text, n_img;
+};
+
+}  // namespace pvj
+
+// the plan object behind the opaque C handle
+struct pvj_plan {
+  pvj_plan_desc_t desc;
+  int32_t n_samples;
+  int64_t n_tokens;
+  int32_t max_len;
+  int32_t n_pos, n_freq;
+  int32_t n_text, n_img;
+  int32_t fwd_tile, bwd_tile;
+  int32_t n_fwd, n_bwd;
+  // host image of the device metadata and section offsets into it
+  uint8_t* image;
+  size_t image_bytes;
+  size_t off_cu, off_cu_text, off_cu_img, off_sinfo, off_cos, off_sin, off_fwd, off_bwd;
+  // device copy (set by pvj_plan_upload)
+  void* dev_meta;
+  int dev_id;
+};
+
+namespace pvj {
+// thread-local error detail (pvj_last_error)
+pvj_status_t fail(pvj_status_t st, const char* fmt, ...);
+Meta device_meta(const pvj_plan* p);
+
+template <typename T>
+inline const T* host_section(const pvj_plan* p, size_t off) {
+  return reinterpret_cast<const T*>(p->image + off);
+}
+}  // namespace pvj

@@ -1,0 +1,271 @@
+// Host planner: offsets, per-sample metadata, RoPE tables and attention work
+// lists for one pack.  Pure host code (no device calls), so it is testable on
+// a machine without a GPU.
+//
+// Packing (Mage-Flow review page, section "Native-Resolution MMDiT"): samples
+// of different resolutions become variable-length token runs packed into one
+// contiguous batch, with per-sample cumulative offsets in place of a
+// block-diagonal mask.  Token counts (same page, section "Mage-VAE"): one
+// latent token per 16x16 pixels, so a sample is (h_lat, w_lat, l_text) with
+// l_text + h_lat * w_lat tokens.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "pvj_internal.h"
+
+namespace pvj {
+
+static thread_local char g_err[512] = "";
+
+pvj_status_t fail(pvj_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Work list for one attention pass.  An item is one tile of `tile_rows` rows of
+// one (sample, head); its cost is proportional to the sample length (every
+// item streams the whole sample on the other side).  Groups = (sample, head)
+// are dealt to the 8 XCDs greedily, largest cost first (LPT), so each group's
+// items share one XCD's L2 for the K/V (or Q/dO) they all stream.  Inside an
+// XCD the items run largest sample first.  Launch slot b runs on XCD b % 8,
+// so the per-XCD lists are interleaved, with idle slots (sample = -1) where a
+// list is shorter than the longest one.
+static std::vector<Item> build_items(const std::vector<int32_t>& len, int n_heads, int tile_rows) {
+  struct Group { int32_t sample, head, n_tiles; int64_t cost; };
+  std::vector<Group> groups;
+  for (int32_t i = 0; i < (int32_t)len.size(); ++i) {
+    if (len[i] == 0) continue;
+    int32_t nt = (len[i] + tile_rows - 1) / tile_rows;
+    for (int h = 0; h < n_heads; ++h)
+      groups.push_back({i, h, nt, (int64_t)nt * (int64_t)len[i]});
+  }
+  std::stable_sort(groups.begin(), groups.end(), [&](const Group& a, const Group& b) {
+    if (len[a.sample] != len[b.sample]) return len[a.sample] > len[b.sample];
+    return false;
+  });
+  std::vector<std::vector<Item>> per_xcd(kNumXcd);
+  int64_t load[kNumXcd] = {0};
+  for (const Group& g : groups) {
+    int best = 0;
+    for (int x = 1; x < kNumXcd; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += g.cost;
+    for (int t = 0; t < g.n_tiles; ++t) per_xcd[best].push_back({g.sample, g.head, t, 0});
+  }
+  size_t longest = 0;
+  for (auto& l : per_xcd) longest = std::max(longest, l.size());
+  std::vector<Item> out;
+  out.reserve(longest * kNumXcd);
+  for (size_t s = 0; s < longest; ++s)
+    for (int x = 0; x < kNumXcd; ++x)
+      out.push_back(s < per_xcd[x].size() ? per_xcd[x][s] : Item{-1, 0, 0, 0});
+  return out;
+}
+
+Meta device_meta(const pvj_plan* p) {
+  const uint8_t* b = static_cast<const uint8_t*>(p->dev_meta);
+  Meta m;
+  m.cu = reinterpret_cast<const int32_t*>(b + p->off_cu);
+  m.cu_text = reinterpret_cast<const int32_t*>(b + p->off_cu_text);
+  m.cu_img = reinterpret_cast<const int32_t*>(b + p->off_cu_img);
+  m.sinfo = reinterpret_cast<const SampleInfo*>(b + p->off_sinfo);
+  m.cos_tab = reinterpret_cast<const float*>(b + p->off_cos);
+  m.sin_tab = reinterpret_cast<const float*>(b + p->off_sin);
+  m.fwd_items = reinterpret_cast<const Item*>(b + p->off_fwd);
+  m.bwd_items = reinterpret_cast<const Item*>(b + p->off_bwd);
+  m.n_samples = p->n_samples;
+  m.n_tokens = (int32_t)p->n_tokens;
+  m.n_heads = p->desc.n_heads;
+  m.head_dim = p->desc.head_dim;
+  m.n_pos = p->n_pos;
+  m.n_freq = p->n_freq;
+  m.n_fwd = p->n_fwd;
+  m.n_bwd = p->n_bwd;
+  m.fwd_tile = p->fwd_tile;
+  m.bwd_tile = p->bwd_tile;
+  m.n_text = p->n_text;
+  m.n_img = p->n_img;
+  return m;
+}
+
+}  // namespace pvj
+
+using namespace pvj;
+
+extern "C" {
+
+PVJ_API const char* pvj_version(void) { return "pvj 0.1 (gfx950)"; }
+
+PVJ_API const char* pvj_last_error(void) { return g_err; }
+
+PVJ_API const char* pvj_status_string(pvj_status_t s) {
+  switch (s) {
+    case PVJ_OK: return "PVJ_OK";
+    case PVJ_ERR_INVALID_ARG: return "PVJ_ERR_INVALID_ARG";
+    case PVJ_ERR_UNSUPPORTED: return "PVJ_ERR_UNSUPPORTED";
+    case PVJ_ERR_OVERFLOW: return "PVJ_ERR_OVERFLOW";
+    case PVJ_ERR_NOT_UPLOADED: return "PVJ_ERR_NOT_UPLOADED";
+    case PVJ_ERR_WORKSPACE_TOO_SMALL: return "PVJ_ERR_WORKSPACE_TOO_SMALL";
+    case PVJ_ERR_HIP: return "PVJ_ERR_HIP";
+  }
+  return "PVJ_ERR_UNKNOWN";
+}
+
+PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samples,
+                                     const pvj_plan_desc_t* desc, pvj_plan_t** out) {
+  if (!out) return fail(PVJ_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!desc) return fail(PVJ_ERR_INVALID_ARG, "desc is NULL");
+  if (n_samples < 0) return fail(PVJ_ERR_INVALID_ARG, "n_samples < 0");
+  if (n_samples > 0 && !samples) return fail(PVJ_ERR_INVALID_ARG, "samples is NULL");
+  if (desc->n_heads < 1) return fail(PVJ_ERR_INVALID_ARG, "n_heads must be >= 1");
+  if (desc->n_heads > 4096) return fail(PVJ_ERR_UNSUPPORTED, "n_heads > 4096");
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(PVJ_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", desc->head_dim);
+  if (desc->dtype != PVJ_BF16 && desc->dtype != PVJ_F32)
+    return fail(PVJ_ERR_UNSUPPORTED, "dtype %d unsupported", desc->dtype);
+  if (desc->rope_pairing != PVJ_ROPE_INTERLEAVED)
+    return fail(PVJ_ERR_UNSUPPORTED, "rope_pairing %d unsupported", desc->rope_pairing);
+  if (desc->text_first != 1) return fail(PVJ_ERR_UNSUPPORTED, "text_first must be 1");
+  if (!(desc->rope_theta > 0.0f) || !std::isfinite(desc->rope_theta))
+    return fail(PVJ_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+
+  const int B = n_samples;
+  std::vector<int32_t> len(B), cu(B + 1), cu_text(B + 1), cu_img(B + 1);
+  std::vector<SampleInfo> sinfo(B);
+  int64_t T = 0, nt = 0, ni = 0;
+  int32_t max_len = 0, max_side = 0;
+  cu[0] = cu_text[0] = cu_img[0] = 0;
+  for (int i = 0; i < B; ++i) {
+    const pvj_sample_t& s = samples[i];
+    if (s.h_lat < 0 || s.w_lat < 0 || s.l_text < 0)
+      return fail(PVJ_ERR_INVALID_ARG, "sample %d has a negative size", i);
+    int64_t hw = (int64_t)s.h_lat * (int64_t)s.w_lat;
+    int64_t L = hw + s.l_text;
+    // the kernels index rows with int32 and multiply a row by H*D in int64
+    if (L > INT32_MAX) return fail(PVJ_ERR_OVERFLOW, "sample %d length overflows int32", i);
+    T += L;
+    nt += s.l_text;
+    ni += hw;
+    if (T > INT32_MAX) return fail(PVJ_ERR_OVERFLOW, "packed length T overflows int32");
+    len[i] = (int32_t)L;
+    cu[i + 1] = (int32_t)T;
+    cu_text[i + 1] = (int32_t)nt;
+    cu_img[i + 1] = (int32_t)ni;
+    sinfo[i] = {cu[i], (int32_t)L, s.l_text, s.w_lat};
+    max_len = std::max(max_len, (int32_t)L);
+    if (hw > 0) max_side = std::max(max_side, std::max(s.h_lat, s.w_lat));
+  }
+
+  pvj_plan* p = new (std::nothrow) pvj_plan();
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "out of host memory");
+  p->desc = *desc;
+  p->n_samples = B;
+  p->n_tokens = T;
+  p->max_len = max_len;
+  p->n_text = (int32_t)nt;
+  p->n_img = (int32_t)ni;
+  p->n_pos = std::max(1, max_side);
+  p->n_freq = desc->head_dim / 4;
+  p->fwd_tile = fwd_tile_rows(desc->dtype, desc->head_dim);
+  p->bwd_tile = bwd_tile_rows(desc->dtype, desc->head_dim);
+  p->dev_meta = nullptr;
+  p->dev_id = -1;
+
+  std::vector<Item> fwd = build_items(len, desc->n_heads, p->fwd_tile);
+  std::vector<Item> bwd = build_items(len, desc->n_heads, p->bwd_tile);
+  p->n_fwd = (int32_t)fwd.size();
+  p->n_bwd = (int32_t)bwd.size();
+
+  size_t off = 0;
+  auto section = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + std::max<size_t>(bytes, 1), kMetaAlign);
+    return o;
+  };
+  const size_t tab = (size_t)p->n_pos * p->n_freq * sizeof(float);
+  p->off_cu = section((B + 1) * sizeof(int32_t));
+  p->off_cu_text = section((B + 1) * sizeof(int32_t));
+  p->off_cu_img = section((B + 1) * sizeof(int32_t));
+  p->off_sinfo = section(B * sizeof(SampleInfo));
+  p->off_cos = section(tab);
+  p->off_sin = section(tab);
+  p->off_fwd = section(fwd.size() * sizeof(Item));
+  p->off_bwd = section(bwd.size() * sizeof(Item));
+  p->image_bytes = off;
+  p->image = static_cast<uint8_t*>(std::calloc(off, 1));
+  if (!p->image) {
+    delete p;
+    return fail(PVJ_ERR_INVALID_ARG, "out of host memory");
+  }
+  std::memcpy(p->image + p->off_cu, cu.data(), (B + 1) * sizeof(int32_t));
+  std::memcpy(p->image + p->off_cu_text, cu_text.data(), (B + 1) * sizeof(int32_t));
+  std::memcpy(p->image + p->off_cu_img, cu_img.data(), (B + 1) * sizeof(int32_t));
+  if (B) std::memcpy(p->image + p->off_sinfo, sinfo.data(), B * sizeof(SampleInfo));
+  // RoPE tables: angle p * theta^(-k / (D/4)) in double, rounded to float once
+  float* ct = reinterpret_cast<float*>(p->image + p->off_cos);
+  float* st = reinterpret_cast<float*>(p->image + p->off_sin);
+  for (int k = 0; k < p->n_freq; ++k) {
+    const double omega = std::pow((double)desc->rope_theta, -(double)k / (double)p->n_freq);
+    for (int pos = 0; pos < p->n_pos; ++pos) {
+      const double phi = (double)pos * omega;
+      ct[(size_t)pos * p->n_freq + k] = (float)std::cos(phi);
+      st[(size_t)pos * p->n_freq + k] = (float)std::sin(phi);
+    }
+  }
+  if (!fwd.empty()) std::memcpy(p->image + p->off_fwd, fwd.data(), fwd.size() * sizeof(Item));
+  if (!bwd.empty()) std::memcpy(p->image + p->off_bwd, bwd.data(), bwd.size() * sizeof(Item));
+  *out = p;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* p, int64_t* n_tokens, int32_t* max_len,
+                                   const int32_t** cu_seqlens_host, size_t* meta_bytes) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (n_tokens) *n_tokens = p->n_tokens;
+  if (max_len) *max_len = p->max_len;
+  if (cu_seqlens_host) *cu_seqlens_host = host_section<int32_t>(p, p->off_cu);
+  if (meta_bytes) *meta_bytes = p->image_bytes;
+  return PVJ_OK;
+}
+
+PVJ_API void pvj_plan_destroy(pvj_plan_t* p) {
+  if (!p) return;
+  std::free(p->image);
+  delete p;
+}
+
+PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* p, int32_t which,
+                                         const int32_t** items, int32_t* n_items,
+                                         int32_t* tile_rows) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (which != 0 && which != 1) return fail(PVJ_ERR_INVALID_ARG, "which must be 0 or 1");
+  if (items) *items = host_section<int32_t>(p, which == 0 ? p->off_fwd : p->off_bwd);
+  if (n_items) *n_items = which == 0 ? p->n_fwd : p->n_bwd;
+  if (tile_rows) *tile_rows = which == 0 ? p->fwd_tile : p->bwd_tile;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* p, const float** cos_tab,
+                                         const float** sin_tab, int32_t* n_pos, int32_t* n_freq) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (cos_tab) *cos_tab = host_section<float>(p, p->off_cos);
+  if (sin_tab) *sin_tab = host_section<float>(p, p->off_sin);
+  if (n_pos) *n_pos = p->n_pos;
+  if (n_freq) *n_freq = p->n_freq;
+  return PVJ_OK;
+}
+
+}  // extern "C"

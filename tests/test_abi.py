@@ -1,0 +1,176 @@
+"""C-ABI library checks that need no GPU: the library loads, exports every
+symbol the header declares, and its pure-host planner is right (offsets, RoPE
+tables, work-list coverage and order, error codes).  No compute call is made.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from pvj_inputs import WORKLOADS, workload, random_small_pack
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pvj = pytest.importorskip("packed_varlen_joint_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pvj.library_path()):
+        pytest.fail("libpvj.so is not built (python -m packed_varlen_joint_amd._build)")
+    return pvj.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "pvj.h")).read()
+    declared = re.findall(r"PVJ_API\s+[\w\s\*]+?\b(pvj_\w+)\s*\(", header)
+    assert len(declared) >= 15
+    raw = ctypes.CDLL(pvj.library_path())
+    for name in declared:
+        assert hasattr(raw, name), name
+    assert lib.pvj_version().decode().startswith("pvj")
+
+
+def _plan(samples, H=2, D=64, dtype="f32"):
+    return pvj.Plan(samples, H, D, dtype)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_plan_offsets_match_oracle(lib, name):
+    wl = workload(name)
+    p = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
+    assert p.cu_seqlens == oracle.cu_seqlens(wl.samples).tolist()
+    assert p.n_tokens == wl.n_tokens
+    assert p.max_len == max(oracle.sample_lengths(wl.samples))
+
+
+def _check_work_list(p, samples, which):
+    items, tile = p.work_items(which)
+    lens = oracle.sample_lengths(samples)
+    assert len(items) % 8 == 0
+    seen = {}
+    group_xcd = {}
+    for b, (s, h, t, pad) in enumerate(items):
+        if s < 0:
+            continue
+        assert 0 <= s < len(samples) and 0 <= h < p.n_heads and pad == 0
+        assert 0 <= t * tile < lens[s]
+        key = (s, h, t)
+        assert key not in seen, key
+        seen[key] = b
+        # every tile of a (sample, head) lands on the same XCD (slot % 8)
+        assert group_xcd.setdefault((s, h), b % 8) == b % 8
+    want = {(s, h, t) for s in range(len(samples)) for h in range(p.n_heads)
+            for t in range(int(math.ceil(lens[s] / tile)))}
+    assert set(seen) == want
+    # inside each XCD, longer samples run first (LPT)
+    for x in range(8):
+        ls = [lens[s] for (s, h, t, _) in items[x::8] if s >= 0]
+        assert all(a >= b for a, b in zip(ls, ls[1:]))
+        # idle slots only at the end of an XCD's list
+        flags = [s >= 0 for (s, _, _, _) in items[x::8]]
+        assert flags == sorted(flags, reverse=True)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_work_lists_cover_every_tile_once(lib, name):
+    wl = workload(name)
+    p = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
+    _check_work_list(p, wl.samples, 0)
+    _check_work_list(p, wl.samples, 1)
+
+
+def test_work_lists_random_packs(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        samples = random_small_pack(rng, int(rng.integers(0, 12)), max_side=40, max_text=300)
+        p = _plan(samples, int(rng.integers(1, 5)), 128, "bf16")
+        _check_work_list(p, samples, 0)
+        _check_work_list(p, samples, 1)
+
+
+def test_work_list_xcd_balance(lib):
+    # the (sample, head) groups are dealt so no XCD carries much more than its share
+    wl = workload("train_64k", 3)
+    p = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
+    items, tile = p.work_items(0)
+    lens = oracle.sample_lengths(wl.samples)
+    load = [sum(int(lens[s]) for (s, h, t, _) in items[x::8] if s >= 0) for x in range(8)]
+    assert max(load) <= 1.10 * (sum(load) / 8)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_tables(lib, D):
+    samples = [(37, 5, 3), (2, 90, 1)]
+    p = _plan(samples, 1, D)
+    cos_t, sin_t, npos, nf = p.rope_table()
+    assert npos == 90 and nf == D // 4
+    omega = oracle.rope_frequencies(D)
+    for pos in (0, 1, 17, 89):
+        for k in range(nf):
+            assert abs(cos_t[pos * nf + k] - math.cos(pos * omega[k])) <= 6e-8
+            assert abs(sin_t[pos * nf + k] - math.sin(pos * omega[k])) <= 6e-8
+
+
+def test_empty_and_degenerate_packs(lib):
+    p = _plan([])
+    assert p.n_tokens == 0 and p.cu_seqlens == [0]
+    assert p.work_items(0)[0] == [] and p.work_items(1)[0] == []
+    p = _plan([(0, 0, 0), (3, 0, 2), (0, 5, 0), (1, 1, 0)])
+    assert p.cu_seqlens == [0, 0, 2, 2, 3]
+    _check_work_list(p, [(0, 0, 0), (3, 0, 2), (0, 5, 0), (1, 1, 0)], 0)
+
+
+def _create(lib, samples, H=2, D=64, dtype=0, theta=1e4, pairing=0, text_first=1):
+    arr = (pvj._Sample * max(1, len(samples)))(*[pvj._Sample(*s) for s in samples])
+    desc = pvj._Desc(H, D, dtype, theta, pairing, text_first)
+    h = ctypes.c_void_p()
+    st = lib.pvj_plan_create(arr, len(samples), ctypes.byref(desc), ctypes.byref(h))
+    if st == 0:
+        lib.pvj_plan_destroy(h)
+    return st
+
+
+def test_error_codes(lib):
+    INVALID, UNSUP, OVERFLOW = 1, 2, 3
+    assert _create(lib, [(1, 1, 1)]) == 0
+    assert _create(lib, [(-1, 1, 1)]) == INVALID
+    assert _create(lib, [(1, 1, -3)]) == INVALID
+    assert _create(lib, [(1, 1, 1)], H=0) == INVALID
+    assert _create(lib, [(1, 1, 1)], D=96) == UNSUP
+    assert _create(lib, [(1, 1, 1)], dtype=7) == UNSUP
+    assert _create(lib, [(1, 1, 1)], pairing=1) == UNSUP
+    assert _create(lib, [(1, 1, 1)], text_first=0) == UNSUP
+    assert _create(lib, [(1, 1, 1)], theta=-1.0) == INVALID
+    assert _create(lib, [(50000, 50000, 0)]) == OVERFLOW           # one sample > int32
+    assert _create(lib, [(40000, 40000, 0)] * 2) == OVERFLOW       # T > int32
+    h = ctypes.c_void_p()
+    assert lib.pvj_plan_create(None, 1, None, ctypes.byref(h)) == INVALID
+    assert lib.pvj_status_string(5).decode() == "PVJ_ERR_WORKSPACE_TOO_SMALL"
+    assert "int32" in lib.pvj_last_error().decode() or lib.pvj_last_error()
+
+
+def test_compute_before_upload_is_rejected(lib):
+    # validation happens before any device call: NOT_UPLOADED without touching HIP
+    p = _plan([(2, 2, 1)], 1, 64, "f32")
+    st = lib.pvj_varlen_attn_fwd(p.handle, 16, 16, 16, 16, None, 0.0, 0, None)
+    assert st == 4
+    assert lib.pvj_rope2d_apply(p.handle, 16, 16, 0, None) == 4
+    assert lib.pvj_pack(p.handle, 16, 16, 16, None) == 4
+    assert lib.pvj_unpack(p.handle, 16, 16, 16, None) == 4
+    st = lib.pvj_varlen_attn_bwd(p.handle, 16, 16, 16, 16, 16, 16, 16, 16, 16, 256, 1 << 20,
+                                 0.0, 0, None)
+    assert st == 4
+    assert lib.pvj_plan_upload(p.handle, None, 0, None) == 1
+    assert lib.pvj_plan_upload(p.handle, 8, 1 << 20, None) == 1      # misaligned
+
+
+def test_bwd_workspace_size(lib):
+    p = _plan([(3, 3, 2)], 3, 64)
+    T, H, D = 11, 3, 64
+    al = lambda x: (x + 255) // 256 * 256
+    assert p.bwd_workspace_bytes() == al(T * H * D * 4) + al(T * H * 4)
