@@ -1,0 +1,245 @@
+#!/usr/bin/env python
+"""Throughput of the packed variable-length joint-attention hot path on one MI355X.
+
+One step = the whole path over one synthetic pack, with every input already
+resident in HBM when the timed region starts:
+  plan (host planner + metadata upload) -> pack Q, K, V from the text/image
+  streams -> attention forward with 2D RoPE fused on load -> unpack O ->
+  pack dO -> attention backward (Delta preprocess, main kernel, dQ finalize
+  with the inverse rotation) -> unpack dQ, dK, dV.
+
+Default workload: the native-resolution training pack (65,536-token budget,
+seed 0: 7 samples, 55,151 tokens, 24 heads, head_dim 128, bf16), the pack on
+which forward + backward is measured.  FLOPs are algorithmic, per sample
+(never T^2): forward 4*H*D*sum(L_i^2), backward 10*H*D*sum(L_i^2) (five
+products including the score recompute), so a step is 14*H*D*sum(L_i^2).
+
+Prints one JSON line.  `--gpus N` with N > 1 is refused: this path is
+measured on one GPU (the pack is one GPU's data-parallel share).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed varlen attn TFLOP/s (fwd, fwd+bwd) + % bf16 MFMA peak; tokens/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "packed_varlen_joint_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "attn_fwd": ("k_attn_fwd.hip", "pvj_device.h"),
+    "attn_bwd": ("k_attn_bwd.hip", "pvj_device.h"),
+}
+
+
+def _traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except Exception:
+        return None
+    if not rec or rec.get("src_hash") != _src_hash(*KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class PackStep:
+    def __init__(self, wl, seed):
+        import torch
+        import packed_varlen_joint_amd as pvj
+        self.pvj = pvj
+        self.wl = wl
+        H, D = wl.n_heads, wl.head_dim
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        nt = sum(t for (_, _, t) in wl.samples)
+        ni = sum(h * w for (h, w, _) in wl.samples)
+        T = wl.n_tokens
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        mk = lambda n: torch.randn(n, H, D, device="cuda", generator=g).to(dt)
+        # the two modality streams (text, image) of Q, K, V and the output gradient
+        self.streams = {x: (mk(nt), mk(ni)) for x in ("q", "k", "v", "do")}
+        self.joint = {x: torch.empty(T, H, D, device="cuda", dtype=dt)
+                      for x in ("q", "k", "v", "do", "o", "dq", "dk", "dv")}
+        self.out_streams = {x: (torch.empty(nt, H, D, device="cuda", dtype=dt),
+                                torch.empty(ni, H, D, device="cuda", dtype=dt))
+                            for x in ("o", "dq", "dk", "dv")}
+        self.lse = torch.empty(H, T, device="cuda", dtype=torch.float32)
+        probe = pvj.Plan(wl.samples, H, D, wl.dtype)
+        self.ws = torch.empty(max(256, probe.bwd_workspace_bytes()), device="cuda",
+                              dtype=torch.uint8)
+        self.plan = None
+
+    def __call__(self):
+        pvj, wl, j = self.pvj, self.wl, self.joint
+        plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+        for x in ("q", "k", "v"):
+            pvj.pack(plan, *self.streams[x], joint=j[x])
+        pvj.varlen_attn_fwd(plan, j["q"], j["k"], j["v"], rope_fused=True, out=j["o"],
+                            lse=self.lse)
+        pvj.unpack(plan, j["o"], *self.out_streams["o"])
+        if wl.backward:
+            pvj.pack(plan, *self.streams["do"], joint=j["do"])
+            pvj.varlen_attn_bwd(plan, j["q"], j["k"], j["v"], j["o"], self.lse, j["do"],
+                                rope_fused=True, dq=j["dq"], dk=j["dk"], dv=j["dv"],
+                                workspace=self.ws)
+            for x in ("dq", "dk", "dv"):
+                pvj.unpack(plan, j[x], *self.out_streams[x])
+        self.plan = plan
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle (fp64 NumPy, as it stands) on a bounded sample of the workload:
+    forward + backward of (sample, head) slices, smallest samples first, until
+    about `seconds` of CPU work."""
+    import numpy as np
+    import oracle
+    from pvj_inputs import draw_tensors
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    order = sorted(range(len(wl.samples)), key=lambda i: wl.samples[i][2] + wl.samples[i][0] *
+                   wl.samples[i][1])
+    flops = 0.0
+    done = []
+    t0 = time.perf_counter()
+    for i in order:
+        s = wl.samples[i]
+        L = s[2] + s[0] * s[1]
+        if L == 0:
+            continue
+        for h in range(wl.n_heads):
+            q, k, v, do = draw_tensors(L, 1, wl.head_dim, wl.dtype, 7 + i * 100 + h, n=4)
+            oracle.attn_fwd(q, k, v, [s], rope=True)
+            oracle.attn_bwd(q, k, v, do, [s], rope=True)
+            flops += 14.0 * wl.head_dim * L * L
+            done.append((i, h, L))
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    lens = sorted({L for (_, _, L) in done})
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle forward+backward (RoPE) of %d (sample, head) slices of the "
+                      "workload pack, sample lengths %s, %.1f s" % (len(done), lens, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train_64k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the pack is one GPU's data-parallel share "
+              "(--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import packed_varlen_joint_amd as pvj
+    from pvj_inputs import workload
+
+    torch.cuda.set_device(0)
+    wl = workload(args.workload, args.seed)
+    H, D = wl.n_heads, wl.head_dim
+    lens = [t + h * w for (h, w, t) in wl.samples]
+    S2 = float(sum(L * L for L in lens))
+    f_fwd = 4.0 * H * D * S2
+    f_bwd = 10.0 * H * D * S2
+    f_step = f_fwd + (f_bwd if wl.backward else 0.0)
+
+    step = PackStep(wl, args.seed)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    pvj.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = {}
+    for name in pvj.KERNELS:
+        ms, n = pvj.profile_read(name)
+        if n:
+            kern[name] = {"avg_ms": ms / n, "launches_per_step": n / args.steps,
+                          "ms_per_step": ms / args.steps}
+    pvj.profile_enable(False)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = f_step / (ms_step * 1e-3) / 1e12
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    per_launch = {"attn_fwd": f_fwd, "attn_bwd": f_bwd}
+    roof = None
+    if dom in per_launch:
+        ach = per_launch[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic(dom)}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seed": args.seed, "n_samples": len(wl.samples),
+                   "n_tokens": wl.n_tokens, "heads": H, "head_dim": D,
+                   "sum_len_sq": int(S2), "backward": wl.backward, "rope": "fused on load",
+                   "step": "plan+pack+attn fwd+unpack" + ("+pack dO+attn bwd+unpack grads"
+                                                           if wl.backward else "")},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(wl.n_tokens / (ms_step * 1e-3), 1),
+        "tflops_step_no_recompute": round((f_fwd + (8.0 * H * D * S2 if wl.backward else 0)) /
+                                          (ms_step * 1e-3) / 1e12, 2),
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
+        "roofline": roof,
+    }
+    if "attn_fwd" in kern:
+        out["fwd_tflops"] = round(f_fwd / (kern["attn_fwd"]["avg_ms"] * 1e-3) / 1e12, 2)
+    if "attn_bwd" in kern:
+        out["bwd_tflops"] = round(f_bwd / (kern["attn_bwd"]["avg_ms"] * 1e-3) / 1e12, 2)
+        out["fwd_bwd_kernel_tflops"] = round(
+            (f_fwd + f_bwd) / ((kern["attn_fwd"]["avg_ms"] + kern["attn_bwd"]["avg_ms"]) * 1e-3)
+            / 1e12, 2)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -190,6 +190,26 @@ PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* plan, int32_t which,
 PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* plan, const float** cos_tab,
                                          const float** sin_tab, int32_t* n_pos, int32_t* n_freq);
 
+/* ---- per-kernel timing (tracing) ---------------------------------------------
+ * When enabled, every kernel the library launches is bracketed by two HIP
+ * events recorded on the stream it is launched on; pvj_profile_read waits for
+ * the recorded events of one kernel kind and returns their summed duration and
+ * count since the last enable.  Disabled by default (no events, no overhead).
+ * pvj_profile_enable(1) clears the record; (0) stops recording.  Not
+ * thread-safe against concurrent launches from several host threads. */
+enum {
+  PVJ_KERNEL_PACK = 0,
+  PVJ_KERNEL_UNPACK = 1,
+  PVJ_KERNEL_ROPE = 2,
+  PVJ_KERNEL_ATTN_FWD = 3,
+  PVJ_KERNEL_BWD_PRE = 4,
+  PVJ_KERNEL_ATTN_BWD = 5,
+  PVJ_KERNEL_DQ_FINALIZE = 6,
+  PVJ_KERNEL_COUNT = 7
+};
+PVJ_API pvj_status_t pvj_profile_enable(int32_t on);
+PVJ_API pvj_status_t pvj_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
+
 PVJ_API const char* pvj_status_string(pvj_status_t status);
 PVJ_API const char* pvj_last_error(void);
 PVJ_API const char* pvj_version(void);

@@ -22,7 +22,7 @@ import os
 from typing import Iterable, Optional, Sequence, Tuple
 
 __all__ = ["Plan", "PvjError", "pack", "unpack", "rope2d_apply", "varlen_attn_fwd",
-           "varlen_attn_bwd", "library_path", "load_library"]
+           "varlen_attn_bwd", "library_path", "load_library", "profile_enable", "profile_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpvj.so")
@@ -31,6 +31,9 @@ PVJ_BF16 = 0
 PVJ_F32 = 1
 PVJ_ROPE_INTERLEAVED = 0
 PVJ_FLAG_ROPE_FUSED = 1
+
+KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
+           "dq_finalize": 6}
 
 
 class PvjError(RuntimeError):
@@ -86,6 +89,8 @@ def load_library():
         "pvj_plan_rope_table": (I32, [P, ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
                                       ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
                                       ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "pvj_profile_enable": (I32, [I32]),
+        "pvj_profile_read": (I32, [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "pvj_status_string": (ctypes.c_char_p, [I32]),
         "pvj_last_error": (ctypes.c_char_p, []),
         "pvj_version": (ctypes.c_char_p, []),
@@ -213,6 +218,19 @@ class Plan:
 # ---------------------------------------------------------------------------
 # marshalling helpers
 # ---------------------------------------------------------------------------
+
+def profile_enable(on: bool = True):
+    """Start (clearing earlier records) or stop per-kernel event timing in the library."""
+    _check(load_library().pvj_profile_enable(1 if on else 0))
+
+
+def profile_read(kernel: str):
+    """(total milliseconds, launches) of one kernel kind since profile_enable(True)."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(load_library().pvj_profile_read(KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()

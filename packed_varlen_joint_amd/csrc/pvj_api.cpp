@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "pvj_internal.h"
 #include "pvj_launch.h"
@@ -55,6 +56,38 @@ size_t ws_delta_bytes(const pvj_plan* p) {
   return align256((size_t)p->n_tokens * p->desc.n_heads * sizeof(float));
 }
 
+// ---- optional per-kernel event timing ----
+struct EventPair {
+  int kernel;
+  hipEvent_t start, stop;
+};
+bool g_prof_on = false;
+std::vector<EventPair> g_prof_pending;
+double g_prof_ms[PVJ_KERNEL_COUNT] = {0};
+int64_t g_prof_n[PVJ_KERNEL_COUNT] = {0};
+
+// brackets one launch with events on `stream` when timing is enabled
+struct KernelTimer {
+  int kernel;
+  hipStream_t stream;
+  hipEvent_t a = nullptr, b = nullptr;
+  KernelTimer(int k, hipStream_t s) : kernel(k), stream(s) {
+    if (!g_prof_on) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      a = b = nullptr;
+      return;
+    }
+    hipEventRecord(a, stream);
+  }
+  hipError_t done(hipError_t launch_status) {
+    if (a && b) {
+      hipEventRecord(b, stream);
+      g_prof_pending.push_back({kernel, a, b});
+    }
+    return launch_status;
+  }
+};
+
 #define PVJ_TRY(x)                  \
   do {                              \
     pvj_status_t st__ = (x);        \
@@ -89,8 +122,9 @@ PVJ_API pvj_status_t pvj_pack(const pvj_plan_t* p, const void* text, const void*
   PVJ_TRY(check_ptr(text, "text", p->n_text > 0));
   PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
   PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
-  return launched(launch_pack(p, device_meta(p), text, image, joint, false,
-                              static_cast<hipStream_t>(stream)),
+  KernelTimer t(PVJ_KERNEL_PACK, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_pack(p, device_meta(p), text, image, joint, false,
+                                     static_cast<hipStream_t>(stream))),
                   "pack");
 }
 
@@ -100,8 +134,9 @@ PVJ_API pvj_status_t pvj_unpack(const pvj_plan_t* p, const void* joint, void* te
   PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
   PVJ_TRY(check_ptr(text, "text", p->n_text > 0));
   PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
-  return launched(launch_pack(p, device_meta(p), text, image, const_cast<void*>(joint), true,
-                              static_cast<hipStream_t>(stream)),
+  KernelTimer t(PVJ_KERNEL_UNPACK, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_pack(p, device_meta(p), text, image, const_cast<void*>(joint),
+                                     true, static_cast<hipStream_t>(stream))),
                   "unpack");
 }
 
@@ -115,8 +150,9 @@ PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* p, const void* x, void* 
     const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
     if (a < b + n && b < a + n) return fail(PVJ_ERR_INVALID_ARG, "x and y partially overlap");
   }
-  return launched(launch_rope2d(p, device_meta(p), x, y, inverse != 0,
-                                static_cast<hipStream_t>(stream)),
+  KernelTimer t(PVJ_KERNEL_ROPE, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_rope2d(p, device_meta(p), x, y, inverse != 0,
+                                       static_cast<hipStream_t>(stream))),
                   "rope2d_apply");
 }
 
@@ -132,10 +168,11 @@ PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* p, const void* q, con
   if (lse && !aligned16(lse)) return fail(PVJ_ERR_INVALID_ARG, "lse is not 16-byte aligned");
   if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
-  return launched(launch_attn_fwd(p, device_meta(p), q, k, v, o, lse,
-                                  resolve_scale(p, softmax_scale),
-                                  (flags & PVJ_FLAG_ROPE_FUSED) != 0,
-                                  static_cast<hipStream_t>(stream)),
+  KernelTimer t(PVJ_KERNEL_ATTN_FWD, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_attn_fwd(p, device_meta(p), q, k, v, o, lse,
+                                         resolve_scale(p, softmax_scale),
+                                         (flags & PVJ_FLAG_ROPE_FUSED) != 0,
+                                         static_cast<hipStream_t>(stream))),
                   "varlen_attn_fwd");
 }
 
@@ -179,10 +216,57 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   const float scale = resolve_scale(p, softmax_scale);
   float* dq_acc = static_cast<float*>(workspace);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_dq_bytes(p));
-  PVJ_TRY(launched(launch_bwd_pre(p, m, o, dout, delta, dq_acc, s), "bwd preprocess"));
-  PVJ_TRY(launched(launch_attn_bwd(p, m, q, k, v, dout, lse, delta, dq_acc, dk, dv, scale, rope, s),
-                   "varlen_attn_bwd"));
-  return launched(launch_dq_finalize(p, m, dq_acc, dq, rope, s), "dq finalize");
+  {
+    KernelTimer t(PVJ_KERNEL_BWD_PRE, s);
+    PVJ_TRY(launched(t.done(launch_bwd_pre(p, m, o, dout, delta, dq_acc, s)), "bwd preprocess"));
+  }
+  {
+    KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
+    PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, q, k, v, dout, lse, delta, dq_acc, dk, dv,
+                                            scale, rope, s)),
+                     "varlen_attn_bwd"));
+  }
+  KernelTimer t(PVJ_KERNEL_DQ_FINALIZE, s);
+  return launched(t.done(launch_dq_finalize(p, m, dq_acc, dq, rope, s)), "dq finalize");
+}
+
+PVJ_API pvj_status_t pvj_profile_enable(int32_t on) {
+  for (auto& e : g_prof_pending) {
+    hipEventSynchronize(e.stop);
+    hipEventDestroy(e.start);
+    hipEventDestroy(e.stop);
+  }
+  g_prof_pending.clear();
+  for (int i = 0; i < PVJ_KERNEL_COUNT; ++i) {
+    g_prof_ms[i] = 0;
+    g_prof_n[i] = 0;
+  }
+  g_prof_on = on != 0;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= PVJ_KERNEL_COUNT)
+    return fail(PVJ_ERR_INVALID_ARG, "kernel id %d out of range", kernel);
+  std::vector<EventPair> keep;
+  for (auto& e : g_prof_pending) {
+    if (e.kernel != kernel) {
+      keep.push_back(e);
+      continue;
+    }
+    if (hipEventSynchronize(e.stop) != hipSuccess) return fail(PVJ_ERR_HIP, "event sync");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess)
+      return fail(PVJ_ERR_HIP, "event elapsed time");
+    g_prof_ms[kernel] += ms;
+    g_prof_n[kernel] += 1;
+    hipEventDestroy(e.start);
+    hipEventDestroy(e.stop);
+  }
+  g_prof_pending.swap(keep);
+  if (total_ms) *total_ms = g_prof_ms[kernel];
+  if (launches) *launches = g_prof_n[kernel];
+  return PVJ_OK;
 }
 
 }  // extern "C"
