@@ -153,6 +153,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 512 MiB device copy (3 times), the reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the pack is one GPU's data-parallel share "
@@ -164,6 +167,15 @@ def main():
     from pvj_inputs import workload
 
     torch.cuda.set_device(0)
+    if args.copy_calib:
+        n = 512 * 1024 * 1024
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": 3}), flush=True)
+        return
     wl = workload(args.workload, args.seed)
     H, D = wl.n_heads, wl.head_dim
     lens = [t + h * w for (h, w, t) in wl.samples]

@@ -26,7 +26,8 @@
 //  * the output accumulator O^T of lane l holds query l % 32, so the online
 //    softmax rescale is lane-local too.
 // Online softmax in base 2: x = s * scale * log2(e); p = 2^(x - m);
-// LSE = (m + log2 l) * ln 2.  Keys at or past the sample end are masked to
+// LSE = (m + log2 l) * ln 2; the reference max m is only moved (and O, l
+// rescaled) when a tile raises some row max by more than 8 (a factor 256).  Keys at or past the sample end are masked to
 // -inf; their K/V rows are zero-filled, never read.
 
 #include "pvj_device.h"
@@ -53,8 +54,11 @@ struct FwdTile {
   static constexpr size_t SMEM = 2 * 2 * (size_t)K_ELEMS * sizeof(T);
 };
 
+// bf16 tiles fit two waves per SIMD (256 registers), so two workgroups share a
+// CU and one's softmax VALU work overlaps the other's matrix-core work.
 template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* __restrict__ Q,
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
+    sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(Meta m, const T* __restrict__ Q,
                                                                const T* __restrict__ K,
                                                                const T* __restrict__ V,
                                                                T* __restrict__ O,
@@ -114,7 +118,11 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* 
   const int v_dc = tid % UPR;            // V loader: d-chunk (8 d's)
   const int v_k0 = (tid / UPR) * KPT;    // V loader: first of KPT keys
   V8 kreg[NK], vreg[KPT];
-  f32x4 kcs[ROPE ? NK : 1], ksn[ROPE ? NK : 1];
+  // RoPE: this thread always handles the same unit of the head dim, so its
+  // axis and frequency offset are fixed; only the key position varies
+  const int half_units = D / 16;
+  const bool k_col = k_unit >= half_units;
+  const int k_f0 = (k_unit - (k_col ? half_units : 0)) * 4;
 
   auto load_tile = [&](int kv0) {
 #pragma unroll
@@ -122,16 +130,6 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* 
       const int kk = kv0 + k_row0 + i * K_ROW_STEP;
       V8 z = {};
       kreg[i] = kk < L ? load8<T>(Kh + (size_t)kk * RS + k_unit * 8) : z;
-      if (ROPE) {
-        int r = 0, c = 0;
-        if (kk < L) token_pos(kk, si.l_text, si.w_lat, r, c);
-        const int half_units = D / 16;
-        const bool col = k_unit >= half_units;
-        const int pos = col ? c : r;
-        const int k0 = (k_unit - (col ? half_units : 0)) * 4;
-        kcs[i] = *reinterpret_cast<const f32x4*>(m.cos_tab + (size_t)pos * m.n_freq + k0);
-        ksn[i] = *reinterpret_cast<const f32x4*>(m.sin_tab + (size_t)pos * m.n_freq + k0);
-      }
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -141,19 +139,25 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* 
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int kv0) {
     T* kb = ks_lds + buf * C::K_ELEMS;
     T* vb = vt_lds + buf * C::K_ELEMS;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       V8 v = kreg[i];
       if (ROPE) {
+        const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+        int r = 0, c = 0;
+        if (kk < L) token_pos(kk, si.l_text, si.w_lat, r, c);
+        const size_t toff = (size_t)(k_col ? c : r) * m.n_freq + k_f0;
+        const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + toff);
+        const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + toff);
         f32x8 x = to_f32x8(v), y;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float a = x[2 * q], b = x[2 * q + 1];
-          y[2 * q] = a * kcs[i][q] - b * ksn[i][q];
-          y[2 * q + 1] = a * ksn[i][q] + b * kcs[i][q];
+          y[2 * q] = a * cs[q] - b * sn[q];
+          y[2 * q + 1] = a * sn[q] + b * cs[q];
         }
         v = from_f32x8<T>(y);
       }
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* 
 
   const int nkv = (L + kFwdBN - 1) / kFwdBN;
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
 
   f32x16 oacc[DB];
@@ -218,23 +222,29 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_pair32(mx);
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = fast_exp2(m_run - m_new);
+    mx = max_pair32(mx) * scale_log2;
+    // Rescale only when some query's max grew by more than 2^8: otherwise keep
+    // the stale reference max (p <= 256, far from overflow).  O / l is exact
+    // for any common reference, so this only skips work.
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
     float ls = 0.f;
     V8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_new));
+        const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
         ls += p;
         pf[kb][r >> 3][r & 7] = (T)p;
       }
-    l_run = fmaf(l_run, alpha, ls);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    l_run += ls;
 
     // O^T += V^T P^T
 #pragma unroll
@@ -250,7 +260,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_kernel(Meta m, const T* 
           mma16(oacc[db], a, pf[kb][st]);
         }
     }
-    if (j + 1 < nkv) store_tile(buf ^ 1);
+    if (j + 1 < nkv) store_tile(buf ^ 1, kv0 + kFwdBN);
     __syncthreads();
   }
 
