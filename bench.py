@@ -43,6 +43,7 @@ def _src_hash(*names):
 KERNEL_SOURCES = {
     "attn_fwd": ("k_attn_fwd.hip", "pvj_device.h"),
     "attn_bwd": ("k_attn_bwd.hip", "pvj_device.h"),
+    "attn_bwd_dq": ("k_attn_bwd.hip", "pvj_device.h"),
 }
 
 
@@ -207,13 +208,22 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = f_step / (ms_step * 1e-3) / 1e12
     dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
-    per_launch = {"attn_fwd": f_fwd, "attn_bwd": f_bwd}
+    # algorithmic FLOP per launch: the forward's two products; the dK/dV kernel's
+    # score recompute, dP, dV and dK (8 of the backward's 10); the dQ kernel's
+    # dQ product only (its second score/dP recompute is not counted)
+    hd = H * D * S2
+    per_launch = {"attn_fwd": 4.0 * hd, "attn_bwd": 8.0 * hd, "attn_bwd_dq": 2.0 * hd}
+    executed = {"attn_fwd": 4.0 * hd, "attn_bwd": 8.0 * hd, "attn_bwd_dq": 6.0 * hd}
     roof = None
     if dom in per_launch:
         ach = per_launch[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": _traffic(dom)}
+    for k in kern:
+        if k in per_launch:
+            kern[k]["algorithmic_tflops"] = per_launch[k] / (kern[k]["avg_ms"] * 1e-3) / 1e12
+            kern[k]["executed_tflops"] = executed[k] / (kern[k]["avg_ms"] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -241,11 +251,11 @@ def main():
     }
     if "attn_fwd" in kern:
         out["fwd_tflops"] = round(f_fwd / (kern["attn_fwd"]["avg_ms"] * 1e-3) / 1e12, 2)
-    if "attn_bwd" in kern:
-        out["bwd_tflops"] = round(f_bwd / (kern["attn_bwd"]["avg_ms"] * 1e-3) / 1e12, 2)
+    if "attn_bwd" in kern and "attn_bwd_dq" in kern:
+        t_bwd = kern["attn_bwd"]["avg_ms"] + kern["attn_bwd_dq"]["avg_ms"]
+        out["bwd_tflops"] = round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)
         out["fwd_bwd_kernel_tflops"] = round(
-            (f_fwd + f_bwd) / ((kern["attn_fwd"]["avg_ms"] + kern["attn_bwd"]["avg_ms"]) * 1e-3)
-            / 1e12, 2)
+            (f_fwd + f_bwd) / ((kern["attn_fwd"]["avg_ms"] + t_bwd) * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:

@@ -165,8 +165,9 @@ PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* plan, const void* q, 
  * q, k, v, o, lse and the flags/scale must be those of the forward call.
  * workspace: device memory of at least pvj_varlen_attn_bwd_workspace bytes,
  * 256-byte aligned, owned by the caller, contents need not be initialised;
- * it holds the fp32 dQ accumulator and Delta.  dK and dV are deterministic;
- * dQ is accumulated with fp32 atomics (order-dependent rounding).
+ * it holds Delta (fp32 [H, T]) and, with PVJ_FLAG_ROPE_FUSED, the rotated
+ * Q' and K' (two [T, H, D] tensors in the plan dtype).  No atomics: dQ, dK
+ * and dV are deterministic (the same inputs give the same bits).
  */
 PVJ_API pvj_status_t pvj_varlen_attn_bwd_workspace(const pvj_plan_t* plan, size_t* bytes);
 PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* plan, const void* q, const void* k,
@@ -203,8 +204,8 @@ enum {
   PVJ_KERNEL_ROPE = 2,
   PVJ_KERNEL_ATTN_FWD = 3,
   PVJ_KERNEL_BWD_PRE = 4,
-  PVJ_KERNEL_ATTN_BWD = 5,
-  PVJ_KERNEL_DQ_FINALIZE = 6,
+  PVJ_KERNEL_ATTN_BWD = 5,         /* dK, dV */
+  PVJ_KERNEL_ATTN_BWD_DQ = 6,
   PVJ_KERNEL_COUNT = 7
 };
 PVJ_API pvj_status_t pvj_profile_enable(int32_t on);

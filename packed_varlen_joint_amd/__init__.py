@@ -25,7 +25,8 @@ __all__ = ["Plan", "PvjError", "pack", "unpack", "rope2d_apply", "varlen_attn_fw
            "varlen_attn_bwd", "library_path", "load_library", "profile_enable", "profile_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpvj.so")
+# PVJ_LIBRARY may point at another build of the same library (same ABI)
+_LIB_PATH = os.environ.get("PVJ_LIBRARY") or os.path.join(_HERE, "libpvj.so")
 
 PVJ_BF16 = 0
 PVJ_F32 = 1
@@ -33,7 +34,7 @@ PVJ_ROPE_INTERLEAVED = 0
 PVJ_FLAG_ROPE_FUSED = 1
 
 KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
-           "dq_finalize": 6}
+           "attn_bwd_dq": 6}
 
 
 class PvjError(RuntimeError):

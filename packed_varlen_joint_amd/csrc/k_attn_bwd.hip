@@ -4,84 +4,114 @@
 // review page, section "Kernel fusion": 8-GPU training at ~50K packed tokens
 // per GPU).  Gradients of sum(O * dO), per sample and head:
 //   P = exp(s Q'K'^T - LSE); dV = P^T dO; dP = dO V^T; dS = P * (dP - Delta);
-//   dK' = s dS^T Q'; dQ' = s dS K'; with RoPE on load, dK = R^T dK' here and
-//   dQ = R^T dQ' in the finalize kernel.
+//   dK' = s dS^T Q'; dQ' = s dS K'; with RoPE, dK = R^T dK' and dQ = R^T dQ'.
 //
-// One workgroup = one work item (sample, head, 128-key tile); 4 waves, each
-// owning 32 keys.  The loop walks the sample's query tiles (64 rows for bf16,
-// 32 for fp32) through LDS.  Matrix-core mapping (32x32 MFMA, k-step 16):
-//  * S = Q' K'^T and dP = dO V^T: A = Q' / dO rows from LDS (stored in row
-//    order sigma, bits 2 and 3 swapped, as in the forward), B = K' / V rows
-//    held in registers.  The accumulator of lane l holds key l % 32, and
-//    register r of q-block b holds query 32b + 16(r/8) + 8(l/32) + r%8.
-//  * dV += P^T dO and dK' += dS^T Q': the accumulators of P and dS are the A
-//    operand directly (rows = keys, k = 16 consecutive queries); B = dO / Q'
-//    from transposed LDS copies ([d][query]), one 16-byte read per fragment.
-//  * dQ': dS (bf16, [query][key]) goes through LDS once; each wave then
-//    computes a 32-wide d-slice of dQ' for the tile's queries over all 128
-//    keys (B = K' transposed in LDS) and adds it to the fp32 accumulator with
-//    one coalesced atomic per element per workgroup.
-//  * LSE and Delta of the tile's queries are staged in LDS.  Keys and queries
-//    past the sample end are zero-filled and masked (P = 0).
+// Two kernels, no atomics, fully deterministic:
+//  * attn_bwd_dkdv_kernel: one workgroup per (sample, head, 128-key tile);
+//    4 waves x 32 keys with K' and V in registers; walks the sample's query
+//    tiles (64 rows bf16, 32 rows fp32) through double-buffered LDS.
+//    S = Q'K'^T and dP = dO V^T put one key per lane (A = Q' / dO rows stored
+//    in LDS in sigma row order, bits 2 and 3 swapped), so the accumulators of
+//    P and dS are directly the A operands (rows = keys, k = 16 consecutive
+//    queries) of dV += P^T dO and dK' += dS^T Q'.  Their B operands (k =
+//    queries, n = d) are read from the same row-major LDS tiles with the
+//    transposing ds_read_b64_tr_b16.
+//  * attn_bwd_dq_kernel: one workgroup per (sample, head, 128-query tile);
+//    4 waves x 32 queries with Q' and dO in registers; streams 64-key tiles of
+//    K' and V through double-buffered LDS like the forward.  S^T = K'Q'^T and
+//    dP^T = V dO^T put one query per lane (LSE and Delta are per-lane scalars);
+//    dQ'^T += K'^T dS^T takes dS^T straight from the accumulators and K'^T by
+//    transposing reads.  The epilogue scales, applies R^T (rotation pairs are
+//    in one lane) and stores dQ in the output dtype.
+// With RoPE, the preprocess kernel writes Q' = R Q and K' = R K once into the
+// workspace, so both kernels read pre-rotated operands.
 
 #include "pvj_device.h"
 #include "pvj_launch.h"
 
 namespace pvj {
 
-constexpr int kBwdBN = 128;  // keys per workgroup (must match bwd_tile_rows)
+constexpr int kBwdBN = 128;   // keys per dK/dV workgroup (must match bwd_tile_rows)
+constexpr int kDqBM = 128;    // queries per dQ workgroup (= forward tile, uses fwd_items)
+constexpr int kDqBN = 64;     // keys per streamed tile in the dQ kernel
 constexpr int kBwdThreads = 256;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int bsigma(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
+// element offset of (row, col) in a row-major LDS tile of D columns whose
+// 8-element units are XOR-swizzled by (row & 7)
+template <int D>
+__device__ __forceinline__ int toff(int row, int col) {
+  return row * D + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
+
+// The 8-slot 32x32x16 operand fragment F[j] = M[kb8 + j][n] of a row-major
+// LDS tile M (rows = k, columns = n), where kb8 = kbase + 8*(lane/32) and
+// n = nbase + lane%32; `row_of` maps a logical k row to its LDS row.
+// bf16: two ds_read_b64_tr_b16.  Inside each 16-lane group, source lane
+// s = 4j + c reads row k0 + j, columns n0 + 4c .. n0 + 4c + 3, and lane i
+// receives M[k0 .. k0+3][n0 + i] (measured layout of the instruction).
+// fp32 (no transposing read for 32-bit data): eight scalar reads.
+template <int D, typename RowOf>
+__device__ __forceinline__ bf16x8 frag_t(const bf16* M, int kbase, int nbase, RowOf row_of) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, s = lane & 15;
+  bf16x8 f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = row_of(kbase + 8 * (g >> 1) + 4 * t + (s >> 2));
+    const int col = nbase + 16 * (g & 1) + 4 * (s & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(M + toff<D>(row, col)));
+    const bf16x4 b = __builtin_bit_cast(bf16x4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * t + e] = b[e];
+  }
+  return f;
+}
+template <int D, typename RowOf>
+__device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, RowOf row_of) {
+  const int lane = threadIdx.x & 63;
+  const int kb8 = kbase + 8 * (lane >> 5), n = nbase + (lane & 31);
+  f32x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = M[toff<D>(row_of(kb8 + j), n)];
+  return f;
+}
+
+// ===========================================================================
+// dK, dV
+// ===========================================================================
 template <typename T, int D>
-struct BwdCfg {
+struct DkdvCfg {
   static constexpr int QB = sizeof(T) == 2 ? 2 : 1;  // 32-query blocks per tile
-  static constexpr int BQ = 32 * QB;                 // queries per tile
-  static constexpr int UPR = D / 8;                  // 8-element units per row
-  static constexpr int KS = D / 16;                  // k-steps over d
-  static constexpr int DB = D / 32;                  // 32-wide d blocks
-  static constexpr int QU = BQ / 8;                  // units per transposed row
-  static constexpr int KPQ = BQ * UPR / kBwdThreads; // rows per thread in the Q/dO loader
-  static constexpr int KPK = kBwdBN * UPR / kBwdThreads;  // keys per thread in the K^T loader
-  // LDS element offsets
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_DO = OFF_Q + BQ * D;
-  static constexpr int OFF_QT = OFF_DO + BQ * D;
-  static constexpr int OFF_DOT = OFF_QT + D * BQ;
-  static constexpr int OFF_DS = OFF_DOT + D * BQ;
-  static constexpr int OFF_KT = OFF_DS + BQ * kBwdBN;
-  static constexpr int ELEMS = OFF_KT + D * kBwdBN;
-  static constexpr size_t SMEM = (size_t)ELEMS * sizeof(T) + 2 * BQ * sizeof(float);
+  static constexpr int BQ = 32 * QB;
+  static constexpr int UPR = D / 8;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int KPQ = BQ * UPR / kBwdThreads;  // rows per thread in the tile loader
+  static constexpr int TILE = BQ * D;                 // elements of one Q (or dO) tile
+  static constexpr size_t BUF = 2 * (size_t)TILE * sizeof(T) + 2 * BQ * sizeof(float);
+  static constexpr size_t STAGE = (size_t)kBwdBN * D * sizeof(float);
+  static constexpr size_t SMEM = 2 * BUF > STAGE ? 2 * BUF : STAGE;
 };
 
-// swizzles of 8-element units
-__device__ __forceinline__ int swz_rows(int row) { return row & 7; }             // row-major tiles
-__device__ __forceinline__ int swz_t8(int d) { return (d ^ (d >> 3)) & 7; }      // [d][64]
-__device__ __forceinline__ int swz_t4(int d) { return (d ^ (d >> 2)) & 3; }      // [d][32]
-__device__ __forceinline__ int swz_t16(int d) { return (d ^ (d >> 3)) & 15; }    // [d][128]
-
-template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
     Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    float* __restrict__ dQacc, T* __restrict__ dK, T* __restrict__ dV, float scale,
-    float scale_log2) {
+    T* __restrict__ dK, T* __restrict__ dV, float scale, float scale_log2, int rope) {
   typedef typename Vec8<T>::type V8;
-  typedef BwdCfg<T, D> C;
-  constexpr int QB = C::QB, BQ = C::BQ, UPR = C::UPR, KS = C::KS, DB = C::DB, QU = C::QU;
-  constexpr int KPQ = C::KPQ, KPK = C::KPK;
+  typedef DkdvCfg<T, D> C;
+  constexpr int QB = C::QB, BQ = C::BQ, UPR = C::UPR, KS = C::KS, DB = C::DB, KPQ = C::KPQ;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* const lds = reinterpret_cast<T*>(smem_raw);
-  T* const Qs = lds + C::OFF_Q;
-  T* const dOs = lds + C::OFF_DO;
-  T* const QTs = lds + C::OFF_QT;
-  T* const dOTs = lds + C::OFF_DOT;
-  T* const dSs = lds + C::OFF_DS;
-  T* const KTs = lds + C::OFF_KT;
-  float* const lse2_s = reinterpret_cast<float*>(lds + C::ELEMS);
-  float* const delta_s = lse2_s + BQ;
+  auto qs_of = [&](int b) { return reinterpret_cast<T*>(smem_raw + b * C::BUF); };
+  auto dos_of = [&](int b) { return qs_of(b) + C::TILE; };
+  auto lse_of = [&](int b) { return reinterpret_cast<float*>(dos_of(b) + C::TILE); };
+  auto del_of = [&](int b) { return lse_of(b) + BQ; };
 
   const Item it = m.bwd_items[blockIdx.x];
   if (it.sample < 0) return;
@@ -95,47 +125,54 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // rotate one 8-element unit of local row `row` (RoPE on load)
-  auto rot = [&](V8 v, int row, int unit) -> V8 {
-    if (!ROPE || row >= L) return v;
-    int r, c;
-    token_pos(row, si.l_text, si.w_lat, r, c);
-    return from_f32x8<T>(rope_chunk(to_f32x8(v), unit, D, r, c, m.cos_tab, m.sin_tab, m.n_freq,
-                                    false));
-  };
-
-  // ---- this wave's 32 keys: K' and V rows as B operands (registers) ----
+  // this wave's 32 keys as B operands (registers)
   const int my_key = kv0 + wave * 32 + l32;
   V8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int unit = 2 * ks + hi;
     V8 z = {};
-    V8 kv = my_key < L ? load8<T>(K + base + (size_t)my_key * RS + unit * 8) : z;
-    kf[ks] = rot(kv, my_key, unit);
+    kf[ks] = my_key < L ? load8<T>(K + base + (size_t)my_key * RS + unit * 8) : z;
     vf[ks] = my_key < L ? load8<T>(V + base + (size_t)my_key * RS + unit * 8) : z;
   }
-  // ---- K'^T for the whole 128-key tile into LDS ([d][key]) ----
-  {
-    const int dc = tid % UPR;
-    const int k0 = (tid / UPR) * KPK;
-    V8 kr[KPK];
+
+  // query-tile loader: rows r0 .. r0+KPQ-1, one 8-element unit each
+  const int ld_unit = tid % UPR;
+  const int ld_r0 = (tid / UPR) * KPQ;
+  V8 qr[KPQ], gr[KPQ];
+  float lr = 0.f, dr = 0.f;
+  const float* lse_h = LSE + (size_t)it.head * m.n_tokens + si.start;
+  const float* del_h = DELTA + (size_t)it.head * m.n_tokens + si.start;
+  auto load_q = [&](int q0) {
 #pragma unroll
-    for (int i = 0; i < KPK; ++i) {
-      const int kk = kv0 + k0 + i;
+    for (int i = 0; i < KPQ; ++i) {
+      const int qq = q0 + ld_r0 + i;
       V8 z = {};
-      kr[i] = rot(kk < L ? load8<T>(K + base + (size_t)kk * RS + dc * 8) : z, kk, dc);
+      qr[i] = qq < L ? load8<T>(Q + base + (size_t)qq * RS + ld_unit * 8) : z;
+      gr[i] = qq < L ? load8<T>(dO + base + (size_t)qq * RS + ld_unit * 8) : z;
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = dc * 8 + j;
-      typedef T VK __attribute__((ext_vector_type(KPK)));
-      VK w;
-#pragma unroll
-      for (int i = 0; i < KPK; ++i) w[i] = kr[i][j];
-      *reinterpret_cast<VK*>(KTs + d * kBwdBN + (((k0 >> 3) ^ swz_t16(d)) << 3) + (k0 & 7)) = w;
+    if (tid < BQ) {
+      const int qq = q0 + tid;
+      // queries past the end: LSE = +inf makes P = 0
+      lr = qq < L ? lse_h[qq] * 1.4426950408889634f : INFINITY;
+      dr = qq < L ? del_h[qq] : 0.f;
     }
-  }
+  };
+  auto store_q = [&](int b) {
+    T* qs = qs_of(b);
+    T* ds = dos_of(b);
+#pragma unroll
+    for (int i = 0; i < KPQ; ++i) {
+      const int rho = bsigma(ld_r0 + i);
+      store8<T>(qs + toff<D>(rho, ld_unit * 8), qr[i]);
+      store8<T>(ds + toff<D>(rho, ld_unit * 8), gr[i]);
+    }
+    if (tid < BQ) {
+      lse_of(b)[tid] = lr;
+      del_of(b)[tid] = dr;
+    }
+  };
+  auto sig = [](int q) { return bsigma(q); };
 
   f32x16 dk_acc[DB], dv_acc[DB];
 #pragma unroll
@@ -145,72 +182,35 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
   }
 
   const int nq = (L + BQ - 1) / BQ;
-  const float* lse_h = LSE + (size_t)it.head * m.n_tokens + si.start;
-  const float* delta_h = DELTA + (size_t)it.head * m.n_tokens + si.start;
-
+  load_q(0);
+  store_q(0);
+  __syncthreads();
   for (int qt = 0; qt < nq; ++qt) {
-    const int q0 = qt * BQ;
-    // ---- load the query tile: Q' and dO, row-major (sigma rows) and transposed ----
-    {
-      const int dc = tid % UPR;
-      const int r0 = (tid / UPR) * KPQ;
-      V8 qr[KPQ], gr[KPQ];
-#pragma unroll
-      for (int i = 0; i < KPQ; ++i) {
-        const int qq = q0 + r0 + i;
-        V8 z = {};
-        qr[i] = rot(qq < L ? load8<T>(Q + base + (size_t)qq * RS + dc * 8) : z, qq, dc);
-        gr[i] = qq < L ? load8<T>(dO + base + (size_t)qq * RS + dc * 8) : z;
-      }
-#pragma unroll
-      for (int i = 0; i < KPQ; ++i) {
-        const int rho = (r0 + i) ^ (bsigma((r0 + i) & 31) ^ ((r0 + i) & 31));
-        store8<T>(Qs + rho * D + ((dc ^ swz_rows(rho)) << 3), qr[i]);
-        store8<T>(dOs + rho * D + ((dc ^ swz_rows(rho)) << 3), gr[i]);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = dc * 8 + j;
-        const int sw = QU == 8 ? swz_t8(d) : swz_t4(d);
-        const int off = d * BQ + (((r0 >> 3) ^ sw) << 3) + (r0 & 7);
-        typedef T VQ __attribute__((ext_vector_type(KPQ)));
-        VQ a, b;
-#pragma unroll
-        for (int i = 0; i < KPQ; ++i) {
-          a[i] = qr[i][j];
-          b[i] = gr[i][j];
-        }
-        *reinterpret_cast<VQ*>(QTs + off) = a;
-        *reinterpret_cast<VQ*>(dOTs + off) = b;
-      }
-      if (tid < BQ) {
-        const int qq = q0 + tid;
-        // queries past the end: LSE = +inf makes P = 0
-        lse2_s[tid] = qq < L ? lse_h[qq] * 1.4426950408889634f : INFINITY;
-        delta_s[tid] = qq < L ? delta_h[qq] : 0.f;
-      }
-    }
-    __syncthreads();
+    const int b = qt & 1;
+    if (qt + 1 < nq) load_q((qt + 1) * BQ);
+    const T* qs = qs_of(b);
+    const T* ds = dos_of(b);
+    const float* l2 = lse_of(b);
+    const float* dl = del_of(b);
 
-    // ---- S = Q' K'^T and dP = dO V^T, then P and dS (lane = key) ----
-    V8 pf[QB][2], sf[QB][2];  // A operands of dV / dK: [q-block][k-step of 16 queries]
+    V8 pf[QB][2], sf[QB][2];  // A operands of dV and dK: [q-block][16-query step]
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 s = {}, dp = {};
       const int rho = qb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int u = ((2 * ks + hi) ^ swz_rows(rho)) << 3;
-        mma16(s, load8<T>(Qs + rho * D + u), kf[ks]);
-        mma16(dp, load8<T>(dOs + rho * D + u), vf[ks]);
+        const int off = toff<D>(rho, (2 * ks + hi) * 8);
+        mma16(s, load8<T>(qs + off), kf[ks]);
+        mma16(dp, load8<T>(ds + off), vf[ks]);
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int qbase = qb * 32 + 16 * st + 8 * hi;  // this lane's 8 queries
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2_s + qbase);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2_s + qbase + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(delta_s + qbase);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(delta_s + qbase + 4);
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(l2 + qbase);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(l2 + qbase + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dl + qbase);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dl + qbase + 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * st + j;
@@ -218,66 +218,28 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
           const float dj = j < 4 ? d0[j] : d1[j - 4];
           float p = fast_exp2(fmaf(s[r], scale_log2, -lj));
           if (my_key >= L) p = 0.f;
-          const float ds = p * (dp[r] - dj);
           pf[qb][st][j] = (T)p;
-          sf[qb][st][j] = (T)ds;
+          sf[qb][st][j] = (T)(p * (dp[r] - dj));
         }
       }
     }
-    // ---- dV += P^T dO, dK' += dS^T Q' ----
+    // dV += P^T dO, dK' += dS^T Q'  (B operands: dO / Q' columns by transposing reads)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + l32;
-      const int sw = QU == 8 ? swz_t8(d) : swz_t4(d);
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const int off = d * BQ + (((4 * qb + 2 * st + hi) ^ sw) << 3);
-          mma16(dv_acc[db], pf[qb][st], load8<T>(dOTs + off));
-          mma16(dk_acc[db], sf[qb][st], load8<T>(QTs + off));
+          const int kbase = qb * 32 + 16 * st;
+          mma16(dv_acc[db], pf[qb][st], frag_t<D>(ds, kbase, db * 32, sig));
+          mma16(dk_acc[db], sf[qb][st], frag_t<D>(qs, kbase, db * 32, sig));
         }
-    }
-    // ---- dS -> LDS as [query][key] ----
-    {
-      const int key = wave * 32 + l32;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int q = qb * 32 + 16 * st + 8 * hi + j;
-            dSs[q * kBwdBN + (((key >> 3) ^ (q & 15)) << 3) + (key & 7)] = sf[qb][st][j];
-          }
-    }
-    __syncthreads();
-    // ---- dQ' (queries x one 32-wide d block) over the 128 keys; atomics ----
-    for (int wu = wave; wu < QB * DB; wu += 4) {
-      const int qb = wu / DB, db = wu % DB;
-      f32x16 acc = {};
-      const int q = qb * 32 + l32;
-      const int d = db * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < kBwdBN / 16; ++ks) {
-        const int u = 2 * ks + hi;
-        const V8 a = load8<T>(dSs + q * kBwdBN + ((u ^ (q & 15)) << 3));
-        const V8 b = load8<T>(KTs + d * kBwdBN + ((u ^ swz_t16(d)) << 3));
-        mma16(acc, a, b);
-      }
-      // acc register r: query qb*32 + 8(r/4) + 4 hi + r%4, column d
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = q0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (qq < L) unsafeAtomicAdd(dQacc + base + (size_t)qq * RS + d, acc[r] * scale);
-      }
-    }
+    if (qt + 1 < nq) store_q(b ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: dK = R^T (s dK'), dV; staged through LDS for row-major stores ----
-  float* const stage = reinterpret_cast<float*>(smem_raw);  // [128][D] fp32 fits in the tile LDS
-  static_assert((size_t)kBwdBN * D * sizeof(float) <= C::SMEM, "epilogue staging");
+  float* const stage = reinterpret_cast<float*>(smem_raw);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     f32x16* acc = pass == 0 ? dk_acc : dv_acc;
@@ -296,7 +258,7 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
       const int kk = kv0 + row;
       if (kk < L) {
         f32x8 x = *reinterpret_cast<const f32x8*>(stage + row * D + unit * 8);
-        if (ROPE && pass == 0) {
+        if (rope && pass == 0) {
           int r, c;
           token_pos(kk, si.l_text, si.w_lat, r, c);
           x = rope_chunk(x, unit, D, r, c, m.cos_tab, m.sin_tab, m.n_freq, true);
@@ -308,38 +270,209 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
   }
 }
 
-template <typename T, int D, bool ROPE>
-static hipError_t launch_bwd_t(const Meta& m, const void* q, const void* k, const void* v,
-                               const void* dout, const float* lse, const float* delta,
-                               float* dq_acc, void* dk, void* dv, float scale,
-                               hipStream_t stream) {
-  auto kern = attn_bwd_kernel<T, D, ROPE>;
-  const size_t smem = BwdCfg<T, D>::SMEM;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+// ===========================================================================
+// dQ
+// ===========================================================================
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int UPR = D / 8;
+  static constexpr int NK = kDqBN * UPR / kBwdThreads;  // units per thread per tile (K and V)
+  static constexpr int TILE = kDqBN * D;
+  static constexpr size_t SMEM = 2 * 2 * (size_t)TILE * sizeof(T);
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
+    Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
+    T* __restrict__ dQ, float scale, float scale_log2, int rope) {
+  typedef typename Vec8<T>::type V8;
+  typedef DqCfg<T, D> C;
+  constexpr int KS = D / 16, DB = D / 32, UPR = C::UPR, NK = C::NK;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* const lds = reinterpret_cast<T*>(smem_raw);
+  auto ks_of = [&](int b) { return lds + b * 2 * C::TILE; };
+  auto vs_of = [&](int b) { return lds + b * 2 * C::TILE + C::TILE; };
+
+  const Item it = m.fwd_items[blockIdx.x];
+  if (it.sample < 0) return;
+  const SampleInfo si = m.sinfo[it.sample];
+  const int L = si.len;
+  const size_t RS = (size_t)m.n_heads * D;
+  const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qi = it.tile * kDqBM + wave * 32 + l32;  // this lane's query
+
+  V8 qf[KS], gf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int unit = 2 * ks + hi;
+    V8 z = {};
+    qf[ks] = qi < L ? load8<T>(Q + base + (size_t)qi * RS + unit * 8) : z;
+    gf[ks] = qi < L ? load8<T>(dO + base + (size_t)qi * RS + unit * 8) : z;
   }
-  kern<<<dim3(m.n_bwd), dim3(kBwdThreads), smem, stream>>>(
-      m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, dq_acc, (T*)dk,
-      (T*)dv, scale, scale * 1.4426950408889634f);
+  const float lse2 = qi < L ? LSE[(size_t)it.head * m.n_tokens + si.start + qi] *
+                                  1.4426950408889634f : INFINITY;
+  const float delta = qi < L ? DELTA[(size_t)it.head * m.n_tokens + si.start + qi] : 0.f;
+
+  const int k_unit = tid % UPR;
+  const int k_row0 = tid / UPR;
+  constexpr int K_ROW_STEP = kBwdThreads / UPR;
+  V8 kreg[NK], vreg[NK];
+  auto load_kv = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+      V8 z = {};
+      kreg[i] = kk < L ? load8<T>(K + base + (size_t)kk * RS + k_unit * 8) : z;
+      vreg[i] = kk < L ? load8<T>(V + base + (size_t)kk * RS + k_unit * 8) : z;
+    }
+  };
+  auto store_kv = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int rho = bsigma(k_row0 + i * K_ROW_STEP);
+      store8<T>(ks_of(b) + toff<D>(rho, k_unit * 8), kreg[i]);
+      store8<T>(vs_of(b) + toff<D>(rho, k_unit * 8), vreg[i]);
+    }
+  };
+  auto sig = [](int k) { return bsigma(k); };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  const int nkv = (L + kDqBN - 1) / kDqBN;
+  load_kv(0);
+  store_kv(0);
+  __syncthreads();
+  for (int j = 0; j < nkv; ++j) {
+    const int b = j & 1;
+    const int kv0 = j * kDqBN;
+    if (j + 1 < nkv) load_kv(kv0 + kDqBN);
+    const T* ks = ks_of(b);
+    const T* vs = vs_of(b);
+    V8 sfr[2][2];  // dS^T fragments [32-key block][16-key step]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = {}, dp = {};
+      const int rho = kb * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int off = toff<D>(rho, (2 * kk + hi) * 8);
+        mma16(s, load8<T>(ks + off), qf[kk]);
+        mma16(dp, load8<T>(vs + off), gf[kk]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+        float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+        if (key >= L) p = 0.f;
+        sfr[kb][r >> 3][r & 7] = (T)(p * (dp[r] - delta));
+      }
+    }
+    // dQ'^T += K'^T dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          mma16(acc[db], frag_t<D>(ks, kb * 32 + 16 * st, db * 32, sig), sfr[kb][st]);
+    if (j + 1 < nkv) store_kv(b ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dQ = R^T (s dQ'); lane holds query qi, d = 32db + 8g + 4hi + e ----
+  if (qi < L) {
+    int pr = 0, pc = 0;
+    if (rope) token_pos(qi, si.l_text, si.w_lat, pr, pc);
+    T* row = dQ + base + (size_t)qi * RS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hi;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * scale;
+        if (rope) {
+          const bool col = d0 >= D / 2;
+          const int k0 = (d0 - (col ? D / 2 : 0)) / 2;  // pairs (d0, d0+1), (d0+2, d0+3)
+          const size_t to = (size_t)(col ? pc : pr) * m.n_freq + k0;
+          const f32x2 cs = *reinterpret_cast<const f32x2*>(m.cos_tab + to);
+          const f32x2 sn = *reinterpret_cast<const f32x2*>(m.sin_tab + to);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float a = x[2 * q], bb = x[2 * q + 1];
+            x[2 * q] = a * cs[q] + bb * sn[q];        // rotate by -angle
+            x[2 * q + 1] = -a * sn[q] + bb * cs[q];
+          }
+        }
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)x[e];
+          *reinterpret_cast<bf16x4*>(row + d0) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = x[e];
+          *reinterpret_cast<f32x4*>(row + d0) = w;
+        }
+      }
+  }
+}
+
+template <typename K>
+static hipError_t set_smem(K kern, size_t smem, bool& done) {
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)smem);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const Meta& m, int which, const void* q, const void* k,
+                               const void* v, const void* dout, const float* lse,
+                               const float* delta, void* dq, void* dk, void* dv, float scale,
+                               bool rope, hipStream_t stream) {
+  const float sl2 = scale * 1.4426950408889634f;
+  if (which == 0) {
+    auto ka = attn_bwd_dkdv_kernel<T, D>;
+    static bool a_set = false;
+    hipError_t e = set_smem(ka, DkdvCfg<T, D>::SMEM, a_set);
+    if (e != hipSuccess) return e;
+    if (m.n_bwd > 0)
+      ka<<<dim3(m.n_bwd), dim3(kBwdThreads), DkdvCfg<T, D>::SMEM, stream>>>(
+          m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dk, (T*)dv,
+          scale, sl2, rope ? 1 : 0);
+  } else {
+    auto kb = attn_bwd_dq_kernel<T, D>;
+    static bool b_set = false;
+    hipError_t e = set_smem(kb, DqCfg<T, D>::SMEM, b_set);
+    if (e != hipSuccess) return e;
+    if (m.n_fwd > 0)
+      kb<<<dim3(m.n_fwd), dim3(kBwdThreads), DqCfg<T, D>::SMEM, stream>>>(
+          m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
+          sl2, rope ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
-                           const void* v, const void* dout, const float* lse,
-                           const float* delta, float* dq_acc, void* dk, void* dv, float scale,
+hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const void* q,
+                           const void* k, const void* v, const void* dout, const float* lse,
+                           const float* delta, void* dq, void* dk, void* dv, float scale,
                            bool rope, hipStream_t stream) {
-  if (m.n_bwd == 0) return hipSuccess;
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int D = p->desc.head_dim;
-#define PVJ_BWD(TT, DD)                                                                     \
-  return rope ? launch_bwd_t<TT, DD, true>(m, q, k, v, dout, lse, delta, dq_acc, dk, dv,    \
-                                           scale, stream)                                   \
-              : launch_bwd_t<TT, DD, false>(m, q, k, v, dout, lse, delta, dq_acc, dk, dv,   \
-                                            scale, stream)
+#define PVJ_BWD(TT, DD) \
+  return launch_bwd_t<TT, DD>(m, which, q, k, v, dout, lse, delta, dq, dk, dv, scale, rope, stream)
   if (bf && D == 128) PVJ_BWD(bf16, 128);
   if (bf && D == 64) PVJ_BWD(bf16, 64);
   if (!bf && D == 128) PVJ_BWD(float, 128);

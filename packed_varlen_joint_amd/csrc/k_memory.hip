@@ -1,5 +1,5 @@
-// HBM-bound kernels: modality pack/unpack, standalone per-sample 2D RoPE,
-// the attention-backward preprocess (Delta) and the dQ finalize.
+// HBM-bound kernels: modality pack/unpack, standalone per-sample 2D RoPE and
+// the attention-backward preprocess (Delta, pre-rotated Q' and K').
 //
 // Every kernel walks blocks of whole packed rows.  A row is H*D contiguous
 // elements; the unit of work is 8 consecutive elements (one 16-byte bf16 or
@@ -98,8 +98,7 @@ hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const
 
 // ---------------------------------------------------------------------------
 // standalone 2D RoPE (HF paper page "Highlights": per-sample 2D RoPE; review
-// page, "Kernel fusion": RoPE application is a memory-bound op).  TIn -> TOut
-// so the same kernel finalizes the fp32 dQ accumulator (inverse rotation).
+// page, "Kernel fusion": RoPE application is a memory-bound op).
 // ---------------------------------------------------------------------------
 template <typename TIn, typename TOut, bool ROTATE>
 __global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const TIn* x, TOut* y, int rpb,
@@ -165,44 +164,34 @@ hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_dq_finalize(const pvj_plan* p, const Meta& m, const float* dq_acc, void* dq,
-                              bool rope, hipStream_t stream) {
-  if (m.n_tokens == 0) return hipSuccess;
-  const bool bf = p->desc.dtype == PVJ_BF16;
-  const int rpb = rows_per_block(m, 4);
-  const dim3 grid((m.n_tokens + rpb - 1) / rpb);
-  if (bf) {
-    if (rope)
-      rope_kernel<float, bf16, true><<<grid, kThreads, 0, stream>>>(m, dq_acc, (bf16*)dq, rpb, 1);
-    else
-      rope_kernel<float, bf16, false><<<grid, kThreads, 0, stream>>>(m, dq_acc, (bf16*)dq, rpb, 0);
-  } else {
-    if (rope)
-      rope_kernel<float, float, true><<<grid, kThreads, 0, stream>>>(m, dq_acc, (float*)dq, rpb, 1);
-    else
-      rope_kernel<float, float, false><<<grid, kThreads, 0, stream>>>(m, dq_acc, (float*)dq, rpb,
-                                                                      0);
-  }
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // backward preprocess: Delta[h, t] = sum_d dO[t,h,d] * O[t,h,d] (the row term
-// of the softmax backward), and zero the fp32 dQ accumulator.  The D/8 lanes
-// of one (token, head) are consecutive and reduce with xor shuffles.
+// of the softmax backward).  With RoPE it also writes Q' = R Q and K' = R K
+// once, so the backward kernels stream pre-rotated operands instead of
+// rotating every tile again.  The D/8 lanes of one (token, head) are
+// consecutive and reduce with xor shuffles.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool ROPE>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __restrict__ o,
                                                            const T* __restrict__ dout,
+                                                           const T* __restrict__ q,
+                                                           const T* __restrict__ k,
                                                            float* __restrict__ delta,
-                                                           float* __restrict__ dq_acc, int rpb) {
+                                                           T* __restrict__ qr,
+                                                           T* __restrict__ kr, int rpb) {
   const int cpr = m.head_dim / 8;
   const int upr = m.n_heads * cpr;
+  const int chunk = threadIdx.x % cpr;  // fixed for this thread (cpr | kThreads)
+  const int half_chunks = m.head_dim / 16;
+  const bool col = chunk >= half_chunks;
+  const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
   const int total = nrows * upr;
   int e = threadIdx.x;
   int row = e / upr, u = e - (e / upr) * upr;
+  int cur = -1;
+  f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
   for (; e < total; e += kThreads) {
     const size_t off = ((size_t)(row0 + row) * upr + u) * 8;
     const f32x8 a = to_f32x8(load8<T>(o + off));
@@ -212,8 +201,30 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __re
     for (int i = 0; i < 8; ++i) s += a[i] * b[i];
     for (int w = 1; w < cpr; w <<= 1) s += __shfl_xor(s, w, 64);
     if ((u % cpr) == 0) delta[(size_t)(u / cpr) * m.n_tokens + row0 + row] = s;
-    const f32x8 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    store8<float>(dq_acc + off, z);
+    if (ROPE) {
+      if (row != cur) {
+        cur = row;
+        const int tok = row0 + row;
+        const SampleInfo si = m.sinfo[find_sample(m.cu, m.n_samples, tok)];
+        int pr, pc;
+        token_pos(tok - si.start, si.l_text, si.w_lat, pr, pc);
+        const size_t to = (size_t)(col ? pc : pr) * m.n_freq + k0;
+        cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
+        sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
+      }
+      const f32x8 x = to_f32x8(load8<T>(q + off));
+      const f32x8 y = to_f32x8(load8<T>(k + off));
+      f32x8 xr, yr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xr[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
+        xr[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
+        yr[2 * i] = y[2 * i] * cs[i] - y[2 * i + 1] * sn[i];
+        yr[2 * i + 1] = y[2 * i] * sn[i] + y[2 * i + 1] * cs[i];
+      }
+      store8<T>(qr + off, from_f32x8<T>(xr));
+      store8<T>(kr + off, from_f32x8<T>(yr));
+    }
     u += kThreads;
     while (u >= upr) {
       u -= upr;
@@ -223,17 +234,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __re
 }
 
 hipError_t launch_bwd_pre(const pvj_plan* p, const Meta& m, const void* o, const void* dout,
-                          float* delta, float* dq_acc, hipStream_t stream) {
+                          const void* q, const void* k, float* delta, void* qr, void* kr,
+                          bool rope, hipStream_t stream) {
   if (m.n_tokens == 0) return hipSuccess;
   const bool bf = p->desc.dtype == PVJ_BF16;
-  const int rpb = rows_per_block(m, 4);
+  const int rpb = rows_per_block(m, bf ? 2 : 4);
   const dim3 grid((m.n_tokens + rpb - 1) / rpb);
-  if (bf)
-    bwd_pre_kernel<bf16><<<grid, kThreads, 0, stream>>>(m, (const bf16*)o, (const bf16*)dout, delta,
-                                                        dq_acc, rpb);
-  else
-    bwd_pre_kernel<float><<<grid, kThreads, 0, stream>>>(m, (const float*)o, (const float*)dout,
-                                                         delta, dq_acc, rpb);
+#define PVJ_PRE(TT, RR)                                                                      \
+  bwd_pre_kernel<TT, RR><<<grid, kThreads, 0, stream>>>(m, (const TT*)o, (const TT*)dout,    \
+                                                        (const TT*)q, (const TT*)k, delta,   \
+                                                        (TT*)qr, (TT*)kr, rpb)
+  if (bf) {
+    if (rope) PVJ_PRE(bf16, true); else PVJ_PRE(bf16, false);
+  } else {
+    if (rope) PVJ_PRE(float, true); else PVJ_PRE(float, false);
+  }
+#undef PVJ_PRE
   return hipGetLastError();
 }
 

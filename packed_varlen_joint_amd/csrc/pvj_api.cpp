@@ -49,12 +49,15 @@ float resolve_scale(const pvj_plan* p, float s) {
   return s > 0.f ? s : 1.0f / std::sqrt((float)p->desc.head_dim);
 }
 
-size_t ws_dq_bytes(const pvj_plan* p) {
-  return align256((size_t)p->n_tokens * p->desc.n_heads * p->desc.head_dim * sizeof(float));
-}
+// backward workspace: Delta fp32 [H, T], then the pre-rotated Q' and K' (used
+// only with PVJ_FLAG_ROPE_FUSED; always counted so one size serves both)
 size_t ws_delta_bytes(const pvj_plan* p) {
   return align256((size_t)p->n_tokens * p->desc.n_heads * sizeof(float));
 }
+size_t ws_rot_bytes(const pvj_plan* p) {
+  return align256((size_t)p->n_tokens * p->desc.n_heads * p->desc.head_dim * elt_size(p));
+}
+size_t ws_total(const pvj_plan* p) { return ws_delta_bytes(p) + 2 * ws_rot_bytes(p); }
 
 // ---- optional per-kernel event timing ----
 struct EventPair {
@@ -77,11 +80,11 @@ struct KernelTimer {
       a = b = nullptr;
       return;
     }
-    hipEventRecord(a, stream);
+    (void)hipEventRecord(a, stream);
   }
   hipError_t done(hipError_t launch_status) {
     if (a && b) {
-      hipEventRecord(b, stream);
+      (void)hipEventRecord(b, stream);
       g_prof_pending.push_back({kernel, a, b});
     }
     return launch_status;
@@ -179,7 +182,7 @@ PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* p, const void* q, con
 PVJ_API pvj_status_t pvj_varlen_attn_bwd_workspace(const pvj_plan_t* p, size_t* bytes) {
   if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
   if (!bytes) return fail(PVJ_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = ws_dq_bytes(p) + ws_delta_bytes(p);
+  *bytes = ws_total(p);
   return PVJ_OK;
 }
 
@@ -201,7 +204,7 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   PVJ_TRY(check_ptr(dv, "dv", need));
   if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
-  const size_t need_ws = ws_dq_bytes(p) + ws_delta_bytes(p);
+  const size_t need_ws = ws_total(p);
   if (need) {
     if (!workspace) return fail(PVJ_ERR_INVALID_ARG, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -214,27 +217,34 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool rope = (flags & PVJ_FLAG_ROPE_FUSED) != 0;
   const float scale = resolve_scale(p, softmax_scale);
-  float* dq_acc = static_cast<float*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_dq_bytes(p));
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws);
+  void* qr = ws + ws_delta_bytes(p);
+  void* kr = ws + ws_delta_bytes(p) + ws_rot_bytes(p);
   {
     KernelTimer t(PVJ_KERNEL_BWD_PRE, s);
-    PVJ_TRY(launched(t.done(launch_bwd_pre(p, m, o, dout, delta, dq_acc, s)), "bwd preprocess"));
+    PVJ_TRY(launched(t.done(launch_bwd_pre(p, m, o, dout, q, k, delta, qr, kr, rope, s)),
+                     "bwd preprocess"));
   }
+  const void* qq = rope ? qr : q;
+  const void* kk = rope ? kr : k;
   {
     KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
-    PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, q, k, v, dout, lse, delta, dq_acc, dk, dv,
+    PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, 0, qq, kk, v, dout, lse, delta, dq, dk, dv,
                                             scale, rope, s)),
-                     "varlen_attn_bwd"));
+                     "varlen_attn_bwd dK/dV"));
   }
-  KernelTimer t(PVJ_KERNEL_DQ_FINALIZE, s);
-  return launched(t.done(launch_dq_finalize(p, m, dq_acc, dq, rope, s)), "dq finalize");
+  KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
+  return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
+                                         rope, s)),
+                  "varlen_attn_bwd dQ");
 }
 
 PVJ_API pvj_status_t pvj_profile_enable(int32_t on) {
   for (auto& e : g_prof_pending) {
-    hipEventSynchronize(e.stop);
-    hipEventDestroy(e.start);
-    hipEventDestroy(e.stop);
+    (void)hipEventSynchronize(e.stop);
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
   }
   g_prof_pending.clear();
   for (int i = 0; i < PVJ_KERNEL_COUNT; ++i) {
@@ -260,8 +270,8 @@ PVJ_API pvj_status_t pvj_profile_read(int32_t kernel, double* total_ms, int64_t*
       return fail(PVJ_ERR_HIP, "event elapsed time");
     g_prof_ms[kernel] += ms;
     g_prof_n[kernel] += 1;
-    hipEventDestroy(e.start);
-    hipEventDestroy(e.stop);
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
   }
   g_prof_pending.swap(keep);
   if (total_ms) *total_ms = g_prof_ms[kernel];

@@ -15,15 +15,16 @@ hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* 
 hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
                            const void* v, void* o, float* lse, float scale, bool rope,
                            hipStream_t stream);
-// Delta = rowsum(dO * O) into delta [H, T], and zero the fp32 dQ accumulator
+// Delta = rowsum(dO * O) into delta [H, T]; with rope also Q' = R Q -> qr and
+// K' = R K -> kr (same layout as q, k)
 hipError_t launch_bwd_pre(const pvj_plan* p, const Meta& m, const void* o, const void* dout,
-                          float* delta, float* dq_acc, hipStream_t stream);
-hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
-                           const void* v, const void* dout, const float* lse,
-                           const float* delta, float* dq_acc, void* dk, void* dv, float scale,
+                          const void* q, const void* k, float* delta, void* qr, void* kr,
+                          bool rope, hipStream_t stream);
+// dK, dV (kernel 0) and dQ (kernel 1) from Q', K' (already rotated when rope),
+// V, dO, LSE, Delta; with rope the stored dK, dQ are rotated back by R^T
+hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const void* q,
+                           const void* k, const void* v, const void* dout, const float* lse,
+                           const float* delta, void* dq, void* dk, void* dv, float scale,
                            bool rope, hipStream_t stream);
-// dQ = (inverse RoPE of) the fp32 accumulator, rounded to the plan dtype
-hipError_t launch_dq_finalize(const pvj_plan* p, const Meta& m, const float* dq_acc, void* dq,
-                              bool rope, hipStream_t stream);
 
 }  // namespace pvj

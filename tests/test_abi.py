@@ -170,7 +170,9 @@ def test_compute_before_upload_is_rejected(lib):
 
 
 def test_bwd_workspace_size(lib):
-    p = _plan([(3, 3, 2)], 3, 64)
+    # Delta fp32 [H, T], then room for the rotated Q' and K' in the plan dtype
     T, H, D = 11, 3, 64
     al = lambda x: (x + 255) // 256 * 256
-    assert p.bwd_workspace_bytes() == al(T * H * D * 4) + al(T * H * 4)
+    for dt, elt in (("f32", 4), ("bf16", 2)):
+        p = _plan([(3, 3, 2)], H, D, dt)
+        assert p.bwd_workspace_bytes() == al(T * H * 4) + 2 * al(T * H * D * elt)
