@@ -36,51 +36,6 @@ constexpr int kDqBM = 128;    // queries per dQ workgroup (= forward tile, uses 
 constexpr int kDqBN = 64;     // keys per streamed tile in the dQ kernel
 constexpr int kBwdThreads = 256;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int bsigma(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
-// element offset of (row, col) in a row-major LDS tile of D columns whose
-// 8-element units are XOR-swizzled by (row & 7)
-template <int D>
-__device__ __forceinline__ int toff(int row, int col) {
-  return row * D + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
-}
-
-// The 8-slot 32x32x16 operand fragment F[j] = M[kb8 + j][n] of a row-major
-// LDS tile M (rows = k, columns = n), where kb8 = kbase + 8*(lane/32) and
-// n = nbase + lane%32; `row_of` maps a logical k row to its LDS row.
-// bf16: two ds_read_b64_tr_b16.  Inside each 16-lane group, source lane
-// s = 4j + c reads row k0 + j, columns n0 + 4c .. n0 + 4c + 3, and lane i
-// receives M[k0 .. k0+3][n0 + i] (measured layout of the instruction).
-// fp32 (no transposing read for 32-bit data): eight scalar reads.
-template <int D, typename RowOf>
-__device__ __forceinline__ bf16x8 frag_t(const bf16* M, int kbase, int nbase, RowOf row_of) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, s = lane & 15;
-  bf16x8 f;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = row_of(kbase + 8 * (g >> 1) + 4 * t + (s >> 2));
-    const int col = nbase + 16 * (g & 1) + 4 * (s & 3);
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(M + toff<D>(row, col)));
-    const bf16x4 b = __builtin_bit_cast(bf16x4, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[4 * t + e] = b[e];
-  }
-  return f;
-}
-template <int D, typename RowOf>
-__device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, RowOf row_of) {
-  const int lane = threadIdx.x & 63;
-  const int kb8 = kbase + 8 * (lane >> 5), n = nbase + (lane & 31);
-  f32x8 f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = M[toff<D>(row_of(kb8 + j), n)];
-  return f;
-}
-
 // ===========================================================================
 // dK, dV
 // ===========================================================================
@@ -91,11 +46,8 @@ struct DkdvCfg {
   static constexpr int UPR = D / 8;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KPQ = BQ * UPR / kBwdThreads;  // rows per thread in the tile loader
+  static constexpr int KPQ = BQ * UPR / kBwdThreads;  // rows per thread in the staged loader
   static constexpr int TILE = BQ * D;                 // elements of one Q (or dO) tile
-  static constexpr size_t BUF = 2 * (size_t)TILE * sizeof(T) + 2 * BQ * sizeof(float);
-  static constexpr size_t STAGE = (size_t)kBwdBN * D * sizeof(float);
-  static constexpr size_t SMEM = 2 * BUF > STAGE ? 2 * BUF : STAGE;
 };
 
 template <typename T, int D>
@@ -106,12 +58,13 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   typedef typename Vec8<T>::type V8;
   typedef DkdvCfg<T, D> C;
   constexpr int QB = C::QB, BQ = C::BQ, UPR = C::UPR, KS = C::KS, DB = C::DB, KPQ = C::KPQ;
+  constexpr bool DMA = sizeof(T) == 2;
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  auto qs_of = [&](int b) { return reinterpret_cast<T*>(smem_raw + b * C::BUF); };
-  auto dos_of = [&](int b) { return qs_of(b) + C::TILE; };
-  auto lse_of = [&](int b) { return reinterpret_cast<float*>(dos_of(b) + C::TILE); };
-  auto del_of = [&](int b) { return lse_of(b) + BQ; };
+  // separate static buffers, so the compiler can tell the next tile's
+  // direct-to-LDS copies from the current tile's reads
+  __shared__ __align__(16) T q_b0[C::TILE], q_b1[C::TILE], g_b0[C::TILE], g_b1[C::TILE];
+  __shared__ __align__(16) float l_b0[2 * BQ], l_b1[2 * BQ];  // LSE*log2(e), then Delta
+  __shared__ __align__(16) float stage[kBwdBN * D];           // epilogue staging
 
   const Item it = m.bwd_items[blockIdx.x];
   if (it.sample < 0) return;
@@ -125,7 +78,9 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // this wave's 32 keys as B operands (registers)
+  // this wave's 32 keys as B operands (registers); rows past the end are zero
+  // and need no mask: their dK, dV rows are never stored, and dS feeds only
+  // dK of its own key
   const int my_key = kv0 + wave * 32 + l32;
   V8 kf[KS], vf[KS];
 #pragma unroll
@@ -136,40 +91,49 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
     vf[ks] = my_key < L ? load8<T>(V + base + (size_t)my_key * RS + unit * 8) : z;
   }
 
-  // query-tile loader: rows r0 .. r0+KPQ-1, one 8-element unit each
+  // ---- query-tile loader ----
   const int ld_unit = tid % UPR;
   const int ld_r0 = (tid / UPR) * KPQ;
-  V8 qr[KPQ], gr[KPQ];
+  V8 qr[DMA ? 1 : KPQ], gr[DMA ? 1 : KPQ];
   float lr = 0.f, dr = 0.f;
   const float* lse_h = LSE + (size_t)it.head * m.n_tokens + si.start;
   const float* del_h = DELTA + (size_t)it.head * m.n_tokens + si.start;
-  auto load_q = [&](int q0) {
-#pragma unroll
-    for (int i = 0; i < KPQ; ++i) {
-      const int qq = q0 + ld_r0 + i;
-      V8 z = {};
-      qr[i] = qq < L ? load8<T>(Q + base + (size_t)qq * RS + ld_unit * 8) : z;
-      gr[i] = qq < L ? load8<T>(dO + base + (size_t)qq * RS + ld_unit * 8) : z;
-    }
+  auto load_q = [&](int q0, int b) {
+    // LSE and Delta first: the wait for them (in-order counter) then leaves the
+    // tile copies in flight
     if (tid < BQ) {
       const int qq = q0 + tid;
-      // queries past the end: LSE = +inf makes P = 0
-      lr = qq < L ? lse_h[qq] * 1.4426950408889634f : INFINITY;
+      // queries past the end: LSE = +inf makes P = 0 (their rows are re-read data)
+      lr = qq < L ? lse_h[qq] : INFINITY;
       dr = qq < L ? del_h[qq] : 0.f;
+    }
+    if constexpr (DMA) {
+      dma_tile<D, BQ>(b ? q_b1 : q_b0, Q + base, RS, q0, L);
+      dma_tile<D, BQ>(b ? g_b1 : g_b0, dO + base, RS, q0, L);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPQ; ++i) {
+        const int qq = q0 + ld_r0 + i;
+        V8 z = {};
+        qr[i] = qq < L ? load8<T>(Q + base + (size_t)qq * RS + ld_unit * 8) : z;
+        gr[i] = qq < L ? load8<T>(dO + base + (size_t)qq * RS + ld_unit * 8) : z;
+      }
     }
   };
   auto store_q = [&](int b) {
-    T* qs = qs_of(b);
-    T* ds = dos_of(b);
+    if constexpr (DMA) {
+      wait_dma();
+    } else {
 #pragma unroll
-    for (int i = 0; i < KPQ; ++i) {
-      const int rho = bsigma(ld_r0 + i);
-      store8<T>(qs + toff<D>(rho, ld_unit * 8), qr[i]);
-      store8<T>(ds + toff<D>(rho, ld_unit * 8), gr[i]);
+      for (int i = 0; i < KPQ; ++i) {
+        const int rho = bsigma(ld_r0 + i);
+        store8<T>((b ? q_b1 : q_b0) + toff<D>(rho, ld_unit * 8), qr[i]);
+        store8<T>((b ? g_b1 : g_b0) + toff<D>(rho, ld_unit * 8), gr[i]);
+      }
     }
     if (tid < BQ) {
-      lse_of(b)[tid] = lr;
-      del_of(b)[tid] = dr;
+      (b ? l_b1 : l_b0)[tid] = lr * 1.4426950408889634f;
+      (b ? l_b1 : l_b0)[BQ + tid] = dr;
     }
   };
   auto sig = [](int q) { return bsigma(q); };
@@ -181,65 +145,93 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
     dv_acc[db] = f32x16{};
   }
 
+  // S and dP of one 32-query block (A = Q', dO rows from LDS; B = K', V registers)
+  auto sdp = [&](const T* qs, const T* gs, int qb, f32x16& s, f32x16& dp) {
+    const int rho = qb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = toff<D>(rho, (2 * ks + hi) * 8);
+      mma16(s, load8<T>(qs + off), kf[ks]);
+      mma16(dp, load8<T>(gs + off), vf[ks]);
+    }
+    // keep six operand reads in flight ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // P = 2^(s*scale*log2e - LSE*log2e) and dS = P (dP - Delta) for element r
+  // (query qb*32 + 16(r/8) + 8 hi + r%8) into the A fragments of dV and dK
+  auto elem = [&](const float* lb, int qb, int r, const f32x16& s, const f32x16& dp,
+                  V8 (&pf)[2], V8 (&sf)[2]) {
+    const int q = qb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+    const float p = fast_exp2(fmaf(s[r], scale_log2, -lb[q]));
+    pf[r >> 3][r & 7] = (T)p;
+    sf[r >> 3][r & 7] = (T)(p * (dp[r] - lb[BQ + q]));
+  };
+  // dV += P^T dO and dK' += dS^T Q' for one block (B = transposing reads); the
+  // optional `fill` runs between the products (independent VALU work)
+  auto dvdk = [&](const T* qs, const T* gs, int qb, V8 (&pf)[2], V8 (&sf)[2], auto fill) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kbase = qb * 32 + 16 * st;
+        mma16(dv_acc[db], pf[st], frag_t<D>(gs, kbase, db * 32, sig));
+        fill(4 * db + 2 * st);
+        mma16(dk_acc[db], sf[st], frag_t<D>(qs, kbase, db * 32, sig));
+        fill(4 * db + 2 * st + 1);
+      }
+  };
+
   const int nq = (L + BQ - 1) / BQ;
-  load_q(0);
+  load_q(0, 0);
   store_q(0);
   __syncthreads();
   for (int qt = 0; qt < nq; ++qt) {
     const int b = qt & 1;
-    if (qt + 1 < nq) load_q((qt + 1) * BQ);
-    const T* qs = qs_of(b);
-    const T* ds = dos_of(b);
-    const float* l2 = lse_of(b);
-    const float* dl = del_of(b);
-
-    V8 pf[QB][2], sf[QB][2];  // A operands of dV and dK: [q-block][16-query step]
+    if (qt + 1 < nq) load_q((qt + 1) * BQ, b ^ 1);
+    const T* qs = b ? q_b1 : q_b0;
+    const T* gs = b ? g_b1 : g_b0;
+    const float* lb = b ? l_b1 : l_b0;
+    if constexpr (QB == 2) {
+      // software pipeline over the two query blocks: the softmax VALU work of
+      // one block sits between the matrix products of the other
+      f32x16 s0 = {}, dp0 = {}, s1 = {}, dp1 = {};
+      V8 pf0[2], sf0[2], pf1[2], sf1[2];
+      sdp(qs, gs, 0, s0, dp0);
+      {
+        const int rho = 32 + l32;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s = {}, dp = {};
-      const int rho = qb * 32 + l32;
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = toff<D>(rho, (2 * ks + hi) * 8);
+          mma16(s1, load8<T>(qs + off), kf[ks]);
+          mma16(dp1, load8<T>(gs + off), vf[ks]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = toff<D>(rho, (2 * ks + hi) * 8);
-        mma16(s, load8<T>(qs + off), kf[ks]);
-        mma16(dp, load8<T>(ds + off), vf[ks]);
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int qbase = qb * 32 + 16 * st + 8 * hi;  // this lane's 8 queries
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(l2 + qbase);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(l2 + qbase + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dl + qbase);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dl + qbase + 4);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * st + j;
-          const float lj = j < 4 ? l0[j] : l1[j - 4];
-          const float dj = j < 4 ? d0[j] : d1[j - 4];
-          float p = fast_exp2(fmaf(s[r], scale_log2, -lj));
-          if (my_key >= L) p = 0.f;
-          pf[qb][st][j] = (T)p;
-          sf[qb][st][j] = (T)(p * (dp[r] - dj));
+          for (int e = 0; e < 16 / KS; ++e) elem(lb, 0, (16 / KS) * ks + e, s0, dp0, pf0, sf0);
         }
       }
+      dvdk(qs, gs, 0, pf0, sf0, [&](int slot) {
+        constexpr int PER = 16 / (4 * DB);  // elements of block 1 per product slot
+#pragma unroll
+        for (int e = 0; e < PER; ++e) elem(lb, 1, PER * slot + e, s1, dp1, pf1, sf1);
+      });
+      dvdk(qs, gs, 1, pf1, sf1, [](int) {});
+    } else {
+      f32x16 s0 = {}, dp0 = {};
+      V8 pf0[2], sf0[2];
+      sdp(qs, gs, 0, s0, dp0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) elem(lb, 0, r, s0, dp0, pf0, sf0);
+      dvdk(qs, gs, 0, pf0, sf0, [](int) {});
     }
-    // dV += P^T dO, dK' += dS^T Q'  (B operands: dO / Q' columns by transposing reads)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int kbase = qb * 32 + 16 * st;
-          mma16(dv_acc[db], pf[qb][st], frag_t<D>(ds, kbase, db * 32, sig));
-          mma16(dk_acc[db], sf[qb][st], frag_t<D>(qs, kbase, db * 32, sig));
-        }
     if (qt + 1 < nq) store_q(b ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: dK = R^T (s dK'), dV; staged through LDS for row-major stores ----
-  float* const stage = reinterpret_cast<float*>(smem_raw);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     f32x16* acc = pass == 0 ? dk_acc : dv_acc;
@@ -278,11 +270,12 @@ struct DqCfg {
   static constexpr int UPR = D / 8;
   static constexpr int NK = kDqBN * UPR / kBwdThreads;  // units per thread per tile (K and V)
   static constexpr int TILE = kDqBN * D;
-  static constexpr size_t SMEM = 2 * 2 * (size_t)TILE * sizeof(T);
 };
 
+// bf16 fits two waves per SIMD (two workgroups per CU, 64 KB of LDS each)
 template <typename T, int D>
-__global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
+    sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_bwd_dq_kernel(
     Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     T* __restrict__ dQ, float scale, float scale_log2, int rope) {
@@ -290,10 +283,10 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
   typedef DqCfg<T, D> C;
   constexpr int KS = D / 16, DB = D / 32, UPR = C::UPR, NK = C::NK;
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* const lds = reinterpret_cast<T*>(smem_raw);
-  auto ks_of = [&](int b) { return lds + b * 2 * C::TILE; };
-  auto vs_of = [&](int b) { return lds + b * 2 * C::TILE + C::TILE; };
+  // separate static buffers (see the dK/dV kernel)
+  __shared__ __align__(16) T k_b0[C::TILE], k_b1[C::TILE], v_b0[C::TILE], v_b1[C::TILE];
+  auto ks_of = [&](int b) { return b ? k_b1 : k_b0; };
+  auto vs_of = [&](int b) { return b ? v_b1 : v_b0; };
 
   const Item it = m.fwd_items[blockIdx.x];
   if (it.sample < 0) return;
@@ -322,22 +315,32 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
   const int k_unit = tid % UPR;
   const int k_row0 = tid / UPR;
   constexpr int K_ROW_STEP = kBwdThreads / UPR;
-  V8 kreg[NK], vreg[NK];
-  auto load_kv = [&](int kv0) {
+  constexpr bool DMA = sizeof(T) == 2;
+  V8 kreg[DMA ? 1 : NK], vreg[DMA ? 1 : NK];
+  auto load_kv = [&](int kv0, int b) {
+    if constexpr (DMA) {
+      dma_tile<D, kDqBN>(ks_of(b), K + base, RS, kv0, L);
+      dma_tile<D, kDqBN>(vs_of(b), V + base, RS, kv0, L);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int kk = kv0 + k_row0 + i * K_ROW_STEP;
-      V8 z = {};
-      kreg[i] = kk < L ? load8<T>(K + base + (size_t)kk * RS + k_unit * 8) : z;
-      vreg[i] = kk < L ? load8<T>(V + base + (size_t)kk * RS + k_unit * 8) : z;
+      for (int i = 0; i < NK; ++i) {
+        const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+        V8 z = {};
+        kreg[i] = kk < L ? load8<T>(K + base + (size_t)kk * RS + k_unit * 8) : z;
+        vreg[i] = kk < L ? load8<T>(V + base + (size_t)kk * RS + k_unit * 8) : z;
+      }
     }
   };
   auto store_kv = [&](int b) {
+    if constexpr (DMA) {
+      wait_dma();
+    } else {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int rho = bsigma(k_row0 + i * K_ROW_STEP);
-      store8<T>(ks_of(b) + toff<D>(rho, k_unit * 8), kreg[i]);
-      store8<T>(vs_of(b) + toff<D>(rho, k_unit * 8), vreg[i]);
+      for (int i = 0; i < NK; ++i) {
+        const int rho = bsigma(k_row0 + i * K_ROW_STEP);
+        store8<T>(ks_of(b) + toff<D>(rho, k_unit * 8), kreg[i]);
+        store8<T>(vs_of(b) + toff<D>(rho, k_unit * 8), vreg[i]);
+      }
     }
   };
   auto sig = [](int k) { return bsigma(k); };
@@ -347,13 +350,14 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
   const int nkv = (L + kDqBN - 1) / kDqBN;
-  load_kv(0);
+  load_kv(0, 0);
   store_kv(0);
   __syncthreads();
   for (int j = 0; j < nkv; ++j) {
     const int b = j & 1;
     const int kv0 = j * kDqBN;
-    if (j + 1 < nkv) load_kv(kv0 + kDqBN);
+    if (j + 1 < nkv) load_kv(kv0 + kDqBN, b ^ 1);
+    const bool tail = kv0 + kDqBN > L;
     const T* ks = ks_of(b);
     const T* vs = vs_of(b);
     V8 sfr[2][2];  // dS^T fragments [32-key block][16-key step]
@@ -369,9 +373,9 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
         float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-        if (key >= L) p = 0.f;
+        // the last tile's rows past the sample end hold re-read data: zero weight
+        if (tail && kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7) >= L) p = 0.f;
         sfr[kb][r >> 3][r & 7] = (T)(p * (dp[r] - delta));
       }
     }
@@ -428,15 +432,6 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
   }
 }
 
-template <typename K>
-static hipError_t set_smem(K kern, size_t smem, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)smem);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 template <typename T, int D>
 static hipError_t launch_bwd_t(const Meta& m, int which, const void* q, const void* k,
                                const void* v, const void* dout, const float* lse,
@@ -445,20 +440,14 @@ static hipError_t launch_bwd_t(const Meta& m, int which, const void* q, const vo
   const float sl2 = scale * 1.4426950408889634f;
   if (which == 0) {
     auto ka = attn_bwd_dkdv_kernel<T, D>;
-    static bool a_set = false;
-    hipError_t e = set_smem(ka, DkdvCfg<T, D>::SMEM, a_set);
-    if (e != hipSuccess) return e;
     if (m.n_bwd > 0)
-      ka<<<dim3(m.n_bwd), dim3(kBwdThreads), DkdvCfg<T, D>::SMEM, stream>>>(
+      ka<<<dim3(m.n_bwd), dim3(kBwdThreads), 0, stream>>>(
           m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dk, (T*)dv,
           scale, sl2, rope ? 1 : 0);
   } else {
     auto kb = attn_bwd_dq_kernel<T, D>;
-    static bool b_set = false;
-    hipError_t e = set_smem(kb, DqCfg<T, D>::SMEM, b_set);
-    if (e != hipSuccess) return e;
     if (m.n_fwd > 0)
-      kb<<<dim3(m.n_fwd), dim3(kBwdThreads), DqCfg<T, D>::SMEM, stream>>>(
+      kb<<<dim3(m.n_fwd), dim3(kBwdThreads), 0, stream>>>(
           m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
           sl2, rope ? 1 : 0);
   }

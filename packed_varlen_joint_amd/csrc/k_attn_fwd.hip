@@ -7,7 +7,7 @@
 //
 // One workgroup = one work item (sample, head, 128-query tile); 4 waves, each
 // owning 32 queries.  The KV loop streams 64-key tiles of the item's own
-// sample only, through a double-buffered LDS stage.
+// sample only, through double-buffered LDS (separate static buffers).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16; fp32 inputs use eight
 // v_mfma_f32_32x32x2_f32 per k-step of 16):
@@ -16,19 +16,21 @@
 //    the same 32-key block.  Row max and row sum are therefore lane-local plus
 //    one v_permlane32_swap per tile; the running max m and sum l (fp32) live in
 //    registers of the wave that owns the query.
-//  * key k of a tile is stored in LDS row sigma(k) (bits 2 and 3 swapped).
-//    With that order, accumulator register r of lane l holds key
-//    16*(r/8) + 8*(l/32) + r%8 of its 32-key block, so the eight probabilities
+//  * K rows are stored in LDS in the sigma order (bits 2 and 3 of the row
+//    swapped), so accumulator register r of lane l holds key
+//    16*(r/8) + 8*(l/32) + r%8 of its 32-key block and the eight probabilities
 //    of registers 8s..8s+7 are exactly the B operand (P^T, k = keys) of the
-//    output product O^T = V^T P^T, and the matching V^T operand is eight
-//    consecutive keys of one d: a single 16-byte LDS read from V stored
-//    transposed.
+//    output product O^T = V^T P^T.  Its A operand (V^T: rows = d, k = keys) is
+//    read from the row-major V tile with two transposing ds_read_b64_tr_b16.
 //  * the output accumulator O^T of lane l holds query l % 32, so the online
 //    softmax rescale is lane-local too.
+//  * bf16 tiles arrive by direct global -> LDS copies (no register round
+//    trip), except K with RoPE on load, which is rotated in registers between
+//    its global load and its LDS store.
 // Online softmax in base 2: x = s * scale * log2(e); p = 2^(x - m);
 // LSE = (m + log2 l) * ln 2; the reference max m is only moved (and O, l
-// rescaled) when a tile raises some row max by more than 8 (a factor 256).  Keys at or past the sample end are masked to
-// -inf; their K/V rows are zero-filled, never read.
+// rescaled) when a tile raises some row max by more than 8 (a factor 256).
+// Keys at or past the sample end are masked to -inf.
 
 #include "pvj_device.h"
 #include "pvj_launch.h"
@@ -37,44 +39,32 @@ namespace pvj {
 
 constexpr int kFwdBM = 128;  // query rows per workgroup (must match fwd_tile_rows)
 constexpr int kFwdBN = 64;   // keys per KV tile
-constexpr int kFwdThreads = 256;
-
-// key row permutation inside a 32-key block: swap bits 2 and 3
-__device__ __forceinline__ int sigma(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
-// XOR swizzle of the 8-element units of a V^T row (d): spreads both the
-// transposing writes (8 d-rows 8 apart) and the operand reads (8 consecutive d)
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+constexpr int kFwdThreads = kTileThreads;
 
 template <typename T, int D>
 struct FwdTile {
-  static constexpr int UPR = D / 8;                         // 8-element units per K row
-  static constexpr int NK = kFwdBN * UPR / kFwdThreads;     // K units per thread per tile
-  static constexpr int KPT = NK;                            // keys per thread in the V loader
-  static constexpr int K_ELEMS = kFwdBN * D;
-  static constexpr size_t SMEM = 2 * 2 * (size_t)K_ELEMS * sizeof(T);
+  static constexpr int UPR = D / 8;                      // 8-element units per row
+  static constexpr int NK = kFwdBN * UPR / kFwdThreads;  // units per thread per tile (staged)
+  static constexpr int TILE = kFwdBN * D;
 };
 
-// bf16 tiles fit two waves per SIMD (256 registers), so two workgroups share a
-// CU and one's softmax VALU work overlaps the other's matrix-core work.
+// bf16 tiles fit two waves per SIMD, so two workgroups share a CU and one's
+// softmax VALU work overlaps the other's matrix-core work.
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
-    sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(Meta m, const T* __restrict__ Q,
-                                                               const T* __restrict__ K,
-                                                               const T* __restrict__ V,
-                                                               T* __restrict__ O,
-                                                               float* __restrict__ LSE,
-                                                               float scale_log2) {
+    sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(
+    Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    T* __restrict__ O, float* __restrict__ LSE, float scale_log2) {
   typedef typename Vec8<T>::type V8;
   typedef FwdTile<T, D> C;
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int NK = C::NK;
-  constexpr int KPT = C::KPT;
   constexpr int UPR = C::UPR;
+  constexpr bool DMA = sizeof(T) == 2;
+  constexpr bool K_DMA = DMA && !ROPE;
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* const ks_lds = reinterpret_cast<T*>(smem_raw);           // [2][BN][D]
-  T* const vt_lds = ks_lds + 2 * C::K_ELEMS;                  // [2][D][BN]
+  __shared__ __align__(16) T k_b0[C::TILE], k_b1[C::TILE], v_b0[C::TILE], v_b1[C::TILE];
 
   const Item it = m.fwd_items[blockIdx.x];
   if (it.sample < 0) return;
@@ -111,74 +101,80 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  // ---- tile loaders: global -> registers (next tile) -> LDS ----
-  const int k_unit = tid % UPR;          // K loader: unit of the row
-  const int k_row0 = tid / UPR;          // rows k_row0 + i * (256 / UPR)
+  // ---- tile loaders ----
+  // staged path (K with RoPE, fp32): rows k_row0 + i * K_ROW_STEP, one unit each
+  const int k_unit = tid % UPR;
+  const int k_row0 = tid / UPR;
   constexpr int K_ROW_STEP = kFwdThreads / UPR;
-  const int v_dc = tid % UPR;            // V loader: d-chunk (8 d's)
-  const int v_k0 = (tid / UPR) * KPT;    // V loader: first of KPT keys
-  V8 kreg[NK], vreg[KPT];
+  constexpr int NKR = K_DMA ? 1 : NK;
+  constexpr int NVR = DMA ? 1 : NK;
+  V8 kreg[NKR], vreg[NVR];
   // RoPE: this thread always handles the same unit of the head dim, so its
   // axis and frequency offset are fixed; only the key position varies
   const int half_units = D / 16;
   const bool k_col = k_unit >= half_units;
   const int k_f0 = (k_unit - (k_col ? half_units : 0)) * 4;
 
-  auto load_tile = [&](int kv0) {
+  auto load_tile = [&](int kv0, int b) {
+    if constexpr (K_DMA) {
+      dma_tile<D, kFwdBN>(b ? k_b1 : k_b0, Kh, RS, kv0, L);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int kk = kv0 + k_row0 + i * K_ROW_STEP;
-      V8 z = {};
-      kreg[i] = kk < L ? load8<T>(Kh + (size_t)kk * RS + k_unit * 8) : z;
+      for (int i = 0; i < NK; ++i) {
+        const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+        V8 z = {};
+        kreg[i] = kk < L ? load8<T>(Kh + (size_t)kk * RS + k_unit * 8) : z;
+      }
     }
+    if constexpr (DMA) {
+      dma_tile<D, kFwdBN>(b ? v_b1 : v_b0, Vh, RS, kv0, L);
+    } else {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int kk = kv0 + v_k0 + i;
-      V8 z = {};
-      vreg[i] = kk < L ? load8<T>(Vh + (size_t)kk * RS + v_dc * 8) : z;
+      for (int i = 0; i < NK; ++i) {
+        const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+        V8 z = {};
+        vreg[i] = kk < L ? load8<T>(Vh + (size_t)kk * RS + k_unit * 8) : z;
+      }
     }
   };
 
-  auto store_tile = [&](int buf, int kv0) {
-    T* kb = ks_lds + buf * C::K_ELEMS;
-    T* vb = vt_lds + buf * C::K_ELEMS;
+  auto store_tile = [&](int b, int kv0) {
+    if constexpr (!K_DMA) {
+      T* kb = b ? k_b1 : k_b0;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      V8 v = kreg[i];
-      if (ROPE) {
-        const int kk = kv0 + k_row0 + i * K_ROW_STEP;
-        int r = 0, c = 0;
-        if (kk < L) token_pos(kk, si.l_text, si.w_lat, r, c);
-        const size_t toff = (size_t)(k_col ? c : r) * m.n_freq + k_f0;
-        const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + toff);
-        const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + toff);
-        f32x8 x = to_f32x8(v), y;
+      for (int i = 0; i < NK; ++i) {
+        V8 v = kreg[i];
+        if (ROPE) {
+          const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+          int r = 0, c = 0;
+          if (kk < L) token_pos(kk, si.l_text, si.w_lat, r, c);
+          const size_t toffs = (size_t)(k_col ? c : r) * m.n_freq + k_f0;
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + toffs);
+          const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + toffs);
+          f32x8 x = to_f32x8(v), y;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a = x[2 * q], b = x[2 * q + 1];
-          y[2 * q] = a * cs[q] - b * sn[q];
-          y[2 * q + 1] = a * sn[q] + b * cs[q];
+          for (int q = 0; q < 4; ++q) {
+            const float a = x[2 * q], bb = x[2 * q + 1];
+            y[2 * q] = a * cs[q] - bb * sn[q];
+            y[2 * q + 1] = a * sn[q] + bb * cs[q];
+          }
+          v = from_f32x8<T>(y);
         }
-        v = from_f32x8<T>(y);
+        store8<T>(kb + toff<D>(bsigma(k_row0 + i * K_ROW_STEP), k_unit * 8), v);
       }
-      const int rho = sigma(k_row0 + i * K_ROW_STEP);
-      store8<T>(kb + rho * D + ((k_unit ^ (rho & 7)) * 8), v);
     }
-    // transpose: for each of the 8 d's of the chunk, KPT consecutive keys
+    if constexpr (!DMA) {
+      T* vb = b ? v_b1 : v_b0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = v_dc * 8 + j;
-      T* dst = vb + d * kFwdBN + (((v_k0 >> 3) ^ vt_swz(d)) << 3) + (v_k0 & 7);
-      typedef T VK __attribute__((ext_vector_type(KPT)));
-      VK w;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) w[i] = vreg[i][j];
-      *reinterpret_cast<VK*>(dst) = w;
+      for (int i = 0; i < NK; ++i)
+        store8<T>(vb + toff<D>(bsigma(k_row0 + i * K_ROW_STEP), k_unit * 8), vreg[i]);
     }
+    if constexpr (DMA) wait_dma();
   };
+  auto sig = [](int k) { return bsigma(k); };
 
   const int nkv = (L + kFwdBN - 1) / kFwdBN;
-  load_tile(0);
+  load_tile(0, 0);
   store_tile(0, 0);
   __syncthreads();
 
@@ -188,11 +184,11 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   float m_run = -INFINITY, l_run = 0.f;
 
   for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
+    const int b = j & 1;
     const int kv0 = j * kFwdBN;
-    if (j + 1 < nkv) load_tile(kv0 + kFwdBN);
-    const T* kb_lds = ks_lds + buf * C::K_ELEMS;
-    const T* vb_lds = vt_lds + buf * C::K_ELEMS;
+    if (j + 1 < nkv) load_tile(kv0 + kFwdBN, b ^ 1);
+    const T* ks = b ? k_b1 : k_b0;
+    const T* vs = b ? v_b1 : v_b0;
 
     // S^T = K Q^T for the two 32-key blocks
     f32x16 s[2];
@@ -201,12 +197,10 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       s[kb] = f32x16{};
       const int rho = kb * 32 + l32;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const V8 a = load8<T>(kb_lds + rho * D + (((2 * ks + hi) ^ (rho & 7)) << 3));
-        mma16(s[kb], a, qf[ks]);
-      }
+      for (int kk = 0; kk < KS; ++kk)
+        mma16(s[kb], load8<T>(ks + toff<D>(rho, (2 * kk + hi) * 8)), qf[kk]);
     }
-    // mask keys past the sample end (last tile only)
+    // mask keys past the sample end (last tile only; their rows hold re-read data)
     if (kv0 + kFwdBN > L) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -246,21 +240,15 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       }
     l_run += ls;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T (A = V^T by transposing reads of the row-major V tile)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + l32;
-      const T* vrow = vb_lds + d * kFwdBN;
-      const int sw = vt_swz(d);
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const V8 a = load8<T>(vrow + (((4 * kb + 2 * st + hi) ^ sw) << 3));
-          mma16(oacc[db], a, pf[kb][st]);
-        }
-    }
-    if (j + 1 < nkv) store_tile(buf ^ 1, kv0 + kFwdBN);
+        for (int st = 0; st < 2; ++st)
+          mma16(oacc[db], frag_t<D>(vs, kb * 32 + 16 * st, db * 32, sig), pf[kb][st]);
+    if (j + 1 < nkv) store_tile(b ^ 1, kv0 + kFwdBN);
     __syncthreads();
   }
 
@@ -295,17 +283,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
 template <typename T, int D, bool ROPE>
 static hipError_t launch_fwd_t(const Meta& m, const void* q, const void* k, const void* v, void* o,
                                float* lse, float scale_log2, hipStream_t stream) {
-  auto kern = attn_fwd_kernel<T, D, ROPE>;
-  const size_t smem = FwdTile<T, D>::SMEM;
-  static bool attr_set = false;  // per instantiation; idempotent, so a race is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  kern<<<dim3(m.n_fwd), dim3(kFwdThreads), smem, stream>>>(m, (const T*)q, (const T*)k,
-                                                           (const T*)v, (T*)o, lse, scale_log2);
+  attn_fwd_kernel<T, D, ROPE><<<dim3(m.n_fwd), dim3(kFwdThreads), 0, stream>>>(
+      m, (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, scale_log2);
   return hipGetLastError();
 }
 

@@ -122,4 +122,94 @@ __device__ __forceinline__ f32x8 rope_chunk(f32x8 x, int chunk, int head_dim, in
   return y;
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles shared by the attention kernels (all use 256-thread workgroups)
+// ---------------------------------------------------------------------------
+constexpr int kTileThreads = 256;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Row order sigma inside every 32-row block: bits 2 and 3 of the row swapped.
+// Tiles whose rows feed the A operand of a 32x32 product are stored in this
+// order so that accumulator register r of lane l holds row
+// 16(r/8) + 8(l/32) + r%8 of the block: the eight registers 8s..8s+7 then
+// cover eight consecutive rows, which is exactly one 16-wide k-step operand of
+// a following product over those rows.  (sigma is its own inverse.)
+__device__ __forceinline__ int bsigma(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// XOR swizzle of the 8-element (16-byte) units of an LDS tile row.  It is a
+// permutation of row & 7, so 8 consecutive rows read at one unit hit 8
+// different units; and the 4 consecutive rows x 2 adjacent units that a
+// 16-lane group touches in one transposing read also land on 8 different
+// units (the low bit of the XOR comes from row bit 2, the rest from bits 0-1).
+__device__ __forceinline__ int tsw(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// element offset of (row, col) in a row-major LDS tile of D columns
+template <int D>
+__device__ __forceinline__ int toff(int row, int col) {
+  return row * D + (((col >> 3) ^ tsw(row)) << 3) + (col & 7);
+}
+
+// The 8-slot 32x32x16 operand fragment F[j] = M[kb8 + j][n] of a row-major
+// LDS tile M (rows = k, columns = n), where kb8 = kbase + 8*(lane/32) and
+// n = nbase + lane%32; `row_of` maps a logical k row to its LDS row.
+// bf16: two ds_read_b64_tr_b16.  Inside each 16-lane group, source lane
+// s = 4j + c reads row k0 + j, columns n0 + 4c .. n0 + 4c + 3, and lane i
+// receives M[k0 .. k0+3][n0 + i] (measured layout of the instruction).
+// fp32 (no transposing read for 32-bit data): eight scalar reads.
+template <int D, typename RowOf>
+__device__ __forceinline__ bf16x8 frag_t(const bf16* M, int kbase, int nbase, RowOf row_of) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, s = lane & 15;
+  bf16x8 f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = row_of(kbase + 8 * (g >> 1) + 4 * t + (s >> 2));
+    const int col = nbase + 16 * (g & 1) + 4 * (s & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(M + toff<D>(row, col)));
+    const bf16x4 b = __builtin_bit_cast(bf16x4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * t + e] = b[e];
+  }
+  return f;
+}
+template <int D, typename RowOf>
+__device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, RowOf row_of) {
+  const int lane = threadIdx.x & 63;
+  const int kb8 = kbase + 8 * (lane >> 5), n = nbase + (lane & 31);
+  f32x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = M[toff<D>(row_of(kb8 + j), n)];
+  return f;
+}
+
+// Direct global -> LDS copy (global_load_lds_dwordx4, no VGPR round trip) of a
+// [ROWS][D] bf16 tile: rows row0 .. row0+ROWS-1 of one (sample, head), stored
+// in LDS row sigma(r) with the tsw swizzle.  Each instruction writes one
+// wave's 64 consecutive 16-byte LDS slots in lane order, so every lane loads
+// the global unit that belongs in its slot.  Rows at or past the sample end
+// re-read row L-1 (finite data; the kernels give them zero weight).  The
+// copies complete asynchronously: wait_dma() before the barrier that
+// publishes the tile.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(bf16* tile, const bf16* g, size_t RS, int row0, int L) {
+  constexpr int UPR = D / 8;
+  constexpr int PER = ROWS * UPR / kTileThreads;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = i * (kTileThreads / 64) + wave;
+    const int slot = blk * 64 + lane;
+    const int rho = slot / UPR;
+    const int u = (slot % UPR) ^ tsw(rho);
+    int r = row0 + bsigma(rho);
+    r = r < L ? r : L - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)r * RS + u * 8),
+                                     (__attribute__((address_space(3))) void*)(tile + blk * 512),
+                                     16, 0, 0);
+  }
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+
 }  // namespace pvj
