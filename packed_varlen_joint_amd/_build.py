@@ -36,12 +36,22 @@ def _run(cmd):
     return out
 
 
+# per-file code-generation options: the backward kernels' loops interleave many
+# independent LDS reads with matrix-core ops, which the ILP-oriented machine
+# scheduler orders better (measured: dK/dV kernel 18.1 -> 14.2 ms on the
+# 64K-token training pack); the forward keeps the default scheduler
+PER_FILE = {
+    "k_attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith("pvj_plan.cpp"):
         cmd = ["g++"] + COMMON + ["-Wall", "-c", src, "-o", obj]  # pure host code
     else:
-        cmd = [HIPCC] + COMMON + DEVICE + ["-c", src, "-o", obj]
+        cmd = [HIPCC] + COMMON + DEVICE + PER_FILE.get(os.path.basename(src), []) + \
+            ["-c", src, "-o", obj]
     out = _run(cmd)
     return obj, out
 
