@@ -59,7 +59,8 @@ extern "C" {
 typedef enum pvj_status {
   PVJ_OK = 0,
   PVJ_ERR_INVALID_ARG = 1,         /* null/misaligned pointer, negative size, bad enum */
-  PVJ_ERR_UNSUPPORTED = 2,         /* head_dim not in {64,128}, unsupported dtype/pairing */
+  PVJ_ERR_UNSUPPORTED = 2,         /* head_dim not in {64,128}, unsupported dtype/pairing,
+                                      latent side above 32767 */
   PVJ_ERR_OVERFLOW = 3,            /* T or a per-sample length does not fit int32 */
   PVJ_ERR_NOT_UPLOADED = 4,        /* compute call before pvj_plan_upload */
   PVJ_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace / metadata buffer smaller than required */
@@ -71,8 +72,8 @@ enum { PVJ_ROPE_INTERLEAVED = 0 };           /* pvj_plan_desc_t.rope_pairing */
 enum { PVJ_FLAG_ROPE_FUSED = 1u };           /* attention flags */
 
 typedef struct pvj_sample {
-  int32_t h_lat;  /* latent rows    (image pixels / 16), >= 0 */
-  int32_t w_lat;  /* latent columns (image pixels / 16), >= 0 */
+  int32_t h_lat;  /* latent rows    (image pixels / 16), 0 .. 32767 */
+  int32_t w_lat;  /* latent columns (image pixels / 16), 0 .. 32767 */
   int32_t l_text; /* text tokens, >= 0 */
 } pvj_sample_t;
 

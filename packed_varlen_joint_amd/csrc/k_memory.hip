@@ -1,13 +1,16 @@
 // HBM-bound kernels: modality pack/unpack, standalone per-sample 2D RoPE and
 // the attention-backward preprocess (Delta, pre-rotated Q' and K').
 //
-// Every kernel walks blocks of whole packed rows.  A row is H*D contiguous
-// elements; the unit of work is 8 consecutive elements (one 16-byte bf16 or
-// 32-byte fp32 access).  Consecutive lanes take consecutive units, so every
-// wave reads and writes contiguous spans.  Because D/8 divides the block size,
-// a thread always sees the same chunk of the head dimension, and the per-row
-// bookkeeping (owning sample, RoPE position, cos/sin) is redone only when the
-// thread's row changes.
+// Every kernel walks a block of whole packed rows.  A row is H*D contiguous
+// elements and the unit of work is 8 consecutive elements (one 16-byte bf16 or
+// 32-byte fp32 access).  The per-row bookkeeping (owning sample, position in
+// the text or image stream, RoPE position) is computed once per row into LDS
+// at block start.  Each thread then moves four units per batch, issuing the
+// four loads before any store, so every thread keeps four independent memory
+// requests in flight; consecutive lanes take consecutive units, so every wave
+// touches contiguous spans.  Because D/8 divides the block size, a thread's
+// unit always covers the same 8 dims of the head, so its RoPE axis and
+// frequencies are fixed.
 
 #include "pvj_device.h"
 #include "pvj_launch.h"
@@ -15,12 +18,20 @@
 namespace pvj {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 4;          // units in flight per thread
+constexpr int kMaxRowsPerBlock = 64;
 
 // rows per block: about 48 KB of bf16 data (6 KB rows at H=24, D=128)
 static int rows_per_block(const Meta& m, size_t elt) {
   const size_t row_bytes = (size_t)m.n_heads * m.head_dim * elt;
   size_t r = (48 * 1024) / row_bytes;
-  return (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
+  return (int)(r < 1 ? 1 : (r > (size_t)kMaxRowsPerBlock ? kMaxRowsPerBlock : r));
+}
+
+// RoPE position (row, col) of packed row `tok`
+__device__ __forceinline__ void packed_pos(const Meta& m, int tok, int& r, int& c) {
+  const SampleInfo si = m.sinfo[find_sample(m.cu, m.n_samples, tok)];
+  token_pos(tok - si.start, si.l_text, si.w_lat, r, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -36,36 +47,42 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(Meta m, const T* __restr
                                                         T* __restrict__ dst_text,
                                                         T* __restrict__ dst_img, int rpb,
                                                         int unpack) {
+  __shared__ int s_row[kMaxRowsPerBlock];  // stream row; text rows are stored as -1 - row
   const int upr = m.n_heads * m.head_dim / 8;  // units per row
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
+  if ((int)threadIdx.x < nrows) {
+    const int tok = row0 + threadIdx.x;
+    const int i = find_sample(m.cu, m.n_samples, tok);
+    const SampleInfo si = m.sinfo[i];
+    const int j = tok - si.start;
+    s_row[threadIdx.x] = j < si.l_text ? -1 - (m.cu_text[i] + j) : m.cu_img[i] + j - si.l_text;
+  }
+  __syncthreads();
   const int total = nrows * upr;
-  int e = threadIdx.x;
-  int row = e / upr, u = e - (e / upr) * upr;
-  int cur = -1;
-  size_t other = 0;  // element offset of the row in the text or image stream
-  bool is_text = false;
-  for (; e < total; e += kThreads) {
-    if (row != cur) {
-      cur = row;
-      const int tok = row0 + row;
-      const int i = find_sample(m.cu, m.n_samples, tok);
-      const SampleInfo si = m.sinfo[i];
-      const int j = tok - si.start;
-      is_text = j < si.l_text;
-      other = (size_t)(is_text ? m.cu_text[i] + j : m.cu_img[i] + j - si.l_text) * upr * 8;
+  for (int e0 = threadIdx.x; e0 < total; e0 += kBatch * kThreads) {
+    typename Vec8<T>::type v[kBatch];
+    size_t jo[kBatch], so[kBatch];
+    bool txt[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = e0 + b * kThreads;
+      const int row = e / upr, u = e - row * upr;
+      const int sr = e < total ? s_row[row] : 0;
+      txt[b] = sr < 0;
+      jo[b] = ((size_t)(row0 + row) * upr + u) * 8;
+      so[b] = ((size_t)(sr < 0 ? -1 - sr : sr) * upr + u) * 8;
+      if (e < total)
+        v[b] = unpack ? load8<T>(joint_in + jo[b]) : load8<T>((txt[b] ? src_text : src_img) + so[b]);
     }
-    const size_t jo = ((size_t)(row0 + row) * upr + u) * 8;
-    const size_t so = other + (size_t)u * 8;
-    if (!unpack) {
-      store8<T>(joint_out + jo, load8<T>((is_text ? src_text : src_img) + so));
-    } else {
-      store8<T>((is_text ? dst_text : dst_img) + so, load8<T>(joint_in + jo));
-    }
-    u += kThreads;
-    while (u >= upr) {
-      u -= upr;
-      ++row;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (e0 + b * kThreads < total) {
+        if (unpack)
+          store8<T>((txt[b] ? dst_text : dst_img) + so[b], v[b]);
+        else
+          store8<T>(joint_out + jo[b], v[b]);
+      }
     }
   }
 }
@@ -96,55 +113,63 @@ hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const
   return hipGetLastError();
 }
 
+// rotate 4 pairs of x by (cs, sn)
+__device__ __forceinline__ f32x8 rot4(f32x8 x, f32x4 cs, f32x4 sn) {
+  f32x8 y;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = x[2 * q], b = x[2 * q + 1];
+    y[2 * q] = a * cs[q] - b * sn[q];
+    y[2 * q + 1] = a * sn[q] + b * cs[q];
+  }
+  return y;
+}
+
 // ---------------------------------------------------------------------------
 // standalone 2D RoPE (HF paper page "Highlights": per-sample 2D RoPE; review
 // page, "Kernel fusion": RoPE application is a memory-bound op).
 // ---------------------------------------------------------------------------
-template <typename TIn, typename TOut, bool ROTATE>
-__global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const TIn* x, TOut* y, int rpb,
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const T* x, T* y, int rpb,
                                                         int inverse) {
-  const int cpr = m.head_dim / 8;              // chunks per head row
-  const int upr = m.n_heads * cpr;             // units per packed row
-  const int chunk = threadIdx.x % cpr;         // fixed for this thread (cpr | kThreads)
+  __shared__ int s_pos[kMaxRowsPerBlock];  // (row << 16) | col of each row's position
+  const int cpr = m.head_dim / 8;           // units per head row
+  const int upr = m.n_heads * cpr;          // units per packed row
+  const int chunk = threadIdx.x % cpr;      // fixed for this thread (cpr | kThreads)
   const int half_chunks = m.head_dim / 16;
   const bool col = chunk >= half_chunks;
   const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
+  if ((int)threadIdx.x < nrows) {
+    int r, c;
+    packed_pos(m, row0 + threadIdx.x, r, c);
+    s_pos[threadIdx.x] = (r << 16) | c;
+  }
+  __syncthreads();
   const int total = nrows * upr;
-  int e = threadIdx.x;
-  int row = e / upr, u = e - (e / upr) * upr;
-  int cur = -1;
-  f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
-  for (; e < total; e += kThreads) {
-    if (ROTATE && row != cur) {
-      cur = row;
-      const int tok = row0 + row;
-      const SampleInfo si = m.sinfo[find_sample(m.cu, m.n_samples, tok)];
-      int r, c;
-      token_pos(tok - si.start, si.l_text, si.w_lat, r, c);
-      const int pos = col ? c : r;
-      cs = *reinterpret_cast<const f32x4*>(m.cos_tab + (size_t)pos * m.n_freq + k0);
-      sn = *reinterpret_cast<const f32x4*>(m.sin_tab + (size_t)pos * m.n_freq + k0);
-      if (inverse) sn = -sn;
-    }
-    const size_t off = ((size_t)(row0 + row) * upr + u) * 8;
-    f32x8 v = to_f32x8(load8<TIn>(x + off));
-    if (ROTATE) {
-      f32x8 w;
+  for (int e0 = threadIdx.x; e0 < total; e0 += kBatch * kThreads) {
+    f32x8 v[kBatch];
+    size_t off[kBatch];
+    int pos[kBatch];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = v[2 * q], b = v[2 * q + 1];
-        w[2 * q] = a * cs[q] - b * sn[q];
-        w[2 * q + 1] = a * sn[q] + b * cs[q];
-      }
-      v = w;
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = e0 + b * kThreads;
+      const int row = e / upr, u = e - row * upr;
+      off[b] = ((size_t)(row0 + row) * upr + u) * 8;
+      const int pp = e < total ? s_pos[row] : 0;
+      pos[b] = col ? (pp & 0xffff) : (pp >> 16);
+      if (e < total) v[b] = to_f32x8(load8<T>(x + off[b]));
     }
-    store8<TOut>(y + off, from_f32x8<TOut>(v));
-    u += kThreads;
-    while (u >= upr) {
-      u -= upr;
-      ++row;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (e0 + b * kThreads < total) {
+        const size_t to = (size_t)pos[b] * m.n_freq + k0;
+        const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
+        f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
+        if (inverse) sn = -sn;
+        store8<T>(y + off[b], from_f32x8<T>(rot4(v[b], cs, sn)));
+      }
     }
   }
 }
@@ -156,11 +181,9 @@ hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* 
   const int rpb = rows_per_block(m, bf ? 2 : 4);
   const dim3 grid((m.n_tokens + rpb - 1) / rpb);
   if (bf)
-    rope_kernel<bf16, bf16, true><<<grid, kThreads, 0, stream>>>(m, (const bf16*)x, (bf16*)y, rpb,
-                                                                 inverse);
+    rope_kernel<bf16><<<grid, kThreads, 0, stream>>>(m, (const bf16*)x, (bf16*)y, rpb, inverse);
   else
-    rope_kernel<float, float, true><<<grid, kThreads, 0, stream>>>(m, (const float*)x, (float*)y,
-                                                                   rpb, inverse);
+    rope_kernel<float><<<grid, kThreads, 0, stream>>>(m, (const float*)x, (float*)y, rpb, inverse);
   return hipGetLastError();
 }
 
@@ -169,7 +192,9 @@ hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* 
 // of the softmax backward).  With RoPE it also writes Q' = R Q and K' = R K
 // once, so the backward kernels stream pre-rotated operands instead of
 // rotating every tile again.  The D/8 lanes of one (token, head) are
-// consecutive and reduce with xor shuffles.
+// consecutive and reduce with xor shuffles (all lanes of a group are in or
+// out of range together: totals are multiples of D/8 and batches start at
+// multiples of the block size).
 // ---------------------------------------------------------------------------
 template <typename T, bool ROPE>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __restrict__ o,
@@ -179,56 +204,58 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __re
                                                            float* __restrict__ delta,
                                                            T* __restrict__ qr,
                                                            T* __restrict__ kr, int rpb) {
+  __shared__ int s_pos[kMaxRowsPerBlock];
   const int cpr = m.head_dim / 8;
   const int upr = m.n_heads * cpr;
-  const int chunk = threadIdx.x % cpr;  // fixed for this thread (cpr | kThreads)
+  const int chunk = threadIdx.x % cpr;
   const int half_chunks = m.head_dim / 16;
   const bool col = chunk >= half_chunks;
   const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
+  if (ROPE && (int)threadIdx.x < nrows) {
+    int r, c;
+    packed_pos(m, row0 + threadIdx.x, r, c);
+    s_pos[threadIdx.x] = (r << 16) | c;
+  }
+  if (ROPE) __syncthreads();
   const int total = nrows * upr;
-  int e = threadIdx.x;
-  int row = e / upr, u = e - (e / upr) * upr;
-  int cur = -1;
-  f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
-  for (; e < total; e += kThreads) {
-    const size_t off = ((size_t)(row0 + row) * upr + u) * 8;
-    const f32x8 a = to_f32x8(load8<T>(o + off));
-    const f32x8 b = to_f32x8(load8<T>(dout + off));
-    float s = 0.f;
+  for (int e0 = threadIdx.x; e0 < total; e0 += kBatch * kThreads) {
+    f32x8 a[kBatch], g[kBatch], x[kBatch], y[kBatch];
+    size_t off[kBatch];
+    int rows[kBatch], us[kBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += a[i] * b[i];
-    for (int w = 1; w < cpr; w <<= 1) s += __shfl_xor(s, w, 64);
-    if ((u % cpr) == 0) delta[(size_t)(u / cpr) * m.n_tokens + row0 + row] = s;
-    if (ROPE) {
-      if (row != cur) {
-        cur = row;
-        const int tok = row0 + row;
-        const SampleInfo si = m.sinfo[find_sample(m.cu, m.n_samples, tok)];
-        int pr, pc;
-        token_pos(tok - si.start, si.l_text, si.w_lat, pr, pc);
-        const size_t to = (size_t)(col ? pc : pr) * m.n_freq + k0;
-        cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
-        sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = e0 + b * kThreads;
+      rows[b] = e / upr;
+      us[b] = e - rows[b] * upr;
+      off[b] = ((size_t)(row0 + rows[b]) * upr + us[b]) * 8;
+      if (e < total) {
+        a[b] = to_f32x8(load8<T>(o + off[b]));
+        g[b] = to_f32x8(load8<T>(dout + off[b]));
+        if (ROPE) {
+          x[b] = to_f32x8(load8<T>(q + off[b]));
+          y[b] = to_f32x8(load8<T>(k + off[b]));
+        }
       }
-      const f32x8 x = to_f32x8(load8<T>(q + off));
-      const f32x8 y = to_f32x8(load8<T>(k + off));
-      f32x8 xr, yr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xr[2 * i] = x[2 * i] * cs[i] - x[2 * i + 1] * sn[i];
-        xr[2 * i + 1] = x[2 * i] * sn[i] + x[2 * i + 1] * cs[i];
-        yr[2 * i] = y[2 * i] * cs[i] - y[2 * i + 1] * sn[i];
-        yr[2 * i + 1] = y[2 * i] * sn[i] + y[2 * i + 1] * cs[i];
-      }
-      store8<T>(qr + off, from_f32x8<T>(xr));
-      store8<T>(kr + off, from_f32x8<T>(yr));
     }
-    u += kThreads;
-    while (u >= upr) {
-      u -= upr;
-      ++row;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (e0 + b * kThreads >= total) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += a[b][i] * g[b][i];
+      for (int w = 1; w < cpr; w <<= 1) s += __shfl_xor(s, w, 64);
+      if ((us[b] % cpr) == 0)
+        delta[(size_t)(us[b] / cpr) * m.n_tokens + row0 + rows[b]] = s;
+      if (ROPE) {
+        const int pp = s_pos[rows[b]];
+        const size_t to = (size_t)(col ? (pp & 0xffff) : (pp >> 16)) * m.n_freq + k0;
+        const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
+        const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
+        store8<T>(qr + off[b], from_f32x8<T>(rot4(x[b], cs, sn)));
+        store8<T>(kr + off[b], from_f32x8<T>(rot4(y[b], cs, sn)));
+      }
     }
   }
 }

@@ -10,6 +10,7 @@ namespace pvj {
 
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs; workgroups are dealt round-robin
 constexpr size_t kMetaAlign = 256;  // alignment of every metadata section
+constexpr int kMaxLatentSide = 32767;  // h_lat, w_lat limit (positions fit 16-bit fields)
 
 // Rows of one attention work item.  Forward: query rows per workgroup.
 // Backward: key rows per workgroup.

@@ -152,6 +152,9 @@ PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samp
     const pvj_sample_t& s = samples[i];
     if (s.h_lat < 0 || s.w_lat < 0 || s.l_text < 0)
       return fail(PVJ_ERR_INVALID_ARG, "sample %d has a negative size", i);
+    // kernels pack a RoPE position as two 16-bit fields
+    if (s.h_lat > kMaxLatentSide || s.w_lat > kMaxLatentSide)
+      return fail(PVJ_ERR_UNSUPPORTED, "sample %d: latent side above %d", i, kMaxLatentSide);
     int64_t hw = (int64_t)s.h_lat * (int64_t)s.w_lat;
     int64_t L = hw + s.l_text;
     // the kernels index rows with int32 and multiply a row by H*D in int64

@@ -146,8 +146,10 @@ def test_error_codes(lib):
     assert _create(lib, [(1, 1, 1)], pairing=1) == UNSUP
     assert _create(lib, [(1, 1, 1)], text_first=0) == UNSUP
     assert _create(lib, [(1, 1, 1)], theta=-1.0) == INVALID
-    assert _create(lib, [(50000, 50000, 0)]) == OVERFLOW           # one sample > int32
-    assert _create(lib, [(40000, 40000, 0)] * 2) == OVERFLOW       # T > int32
+    assert _create(lib, [(32767, 2, 0)]) == 0
+    assert _create(lib, [(32768, 2, 0)]) == UNSUP                  # latent side limit
+    assert _create(lib, [(2, 40000, 0)]) == UNSUP
+    assert _create(lib, [(30000, 30000, 0)] * 3) == OVERFLOW       # T > int32
     h = ctypes.c_void_p()
     assert lib.pvj_plan_create(None, 1, None, ctypes.byref(h)) == INVALID
     assert lib.pvj_status_string(5).decode() == "PVJ_ERR_WORKSPACE_TOO_SMALL"
