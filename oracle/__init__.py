@@ -30,12 +30,22 @@ The pages do not fix these conventions; the oracle takes the plainest reading:
   embedding of dimension D/2 with adjacent (interleaved) pairs
   (2k, 2k+1) and frequency theta**(-k / (D/4)), theta = 10000;
   Q and K are rotated, V is not; every head uses the same angles;
+* editing mode (review page, "Native-Resolution MMDiT": the edit model adds a
+  frame axis to the 2D RoPE, so every visual token has an (h, w, f) index): a
+  sample (h, w, t, F) holds t text tokens then F image grids of h x w, frame
+  after frame, each row-major; text sits at (0, 0, 0); image token p is at
+  (row, col, frame) = ((p mod hw) // w, p mod w, p // hw).  The head dim is
+  split into consecutive row | col | frame parts of (D-16)/2, (D-16)/2 and 16
+  dims, each a 1D rotary embedding of its own dimension d_a with frequency
+  theta**(-k / (d_a/2)) (the plain 2D mode is the special case of two D/2
+  parts);
 * attention is non-causal, softmax scale 1/sqrt(D), no bias, no dropout;
 * LSE is the natural-log log-sum-exp of the scaled logits, fp32 ``[H, T]``.
 
-Parity status: the exact pairing and frequency layout of the 2D RoPE are not
-fixed by the pages, so that layout is "parity unpinned" beyond its stated
-convention; every other function is pinned by the ``-m "not gpu"`` tests.
+Parity status: the exact pairing and frequency layout of the 2D RoPE, and the
+head-dim split and frame layout of the 3-axis RoPE, are not fixed by the
+pages, so those layouts are "parity unpinned" beyond their stated convention;
+every other function is pinned by the ``-m "not gpu"`` tests.
 """
 from __future__ import annotations
 
@@ -53,14 +63,20 @@ ROPE_THETA = 10000.0
 # packing: lengths, offsets, positions
 # ----------------------------------------------------------------------------
 
+def _frames(s) -> int:
+    return int(s[3]) if len(s) > 3 else 1
+
+
 def sample_lengths(samples: Sequence[Sample]) -> np.ndarray:
     """Tokens per sample: text tokens plus one image token per latent cell.
 
     Review page, "Native-Resolution MMDiT": each image becomes a variable-length
     latent token sequence and its text condition is kept at its own length (no
-    padding).  Review page, "Mage-VAE": one latent cell per 16x16 pixels.
+    padding).  Review page, "Mage-VAE": one latent cell per 16x16 pixels.  An
+    editing sample (h, w, t, F) carries F grids (source and target frames).
     """
-    return np.array([int(t) + int(h) * int(w) for (h, w, t) in samples], dtype=np.int64)
+    return np.array([int(s[2]) + int(s[0]) * int(s[1]) * _frames(s) for s in samples],
+                    dtype=np.int64)
 
 
 def cu_seqlens(samples: Sequence[Sample]) -> np.ndarray:
@@ -86,13 +102,42 @@ def token_positions(samples: Sequence[Sample]) -> np.ndarray:
     (p // w, p % w).
     """
     rows: List[Tuple[int, int]] = []
-    for (h, w, t) in samples:
+    for s in samples:
+        h, w, t = s[0], s[1], s[2]
         for _ in range(t):
             rows.append((0, 0))
-        for r in range(h):
-            for c in range(w):
-                rows.append((r, c))
+        for _f in range(_frames(s)):
+            for r in range(h):
+                for c in range(w):
+                    rows.append((r, c))
     return np.array(rows, dtype=np.int64).reshape(-1, 2)
+
+
+def token_positions3(samples: Sequence[Sample]) -> np.ndarray:
+    """(row, col, frame) RoPE position of every packed token, shape [T, 3].
+
+    Review page, "Native-Resolution MMDiT" (editing): a frame axis is added to
+    the 2D RoPE.  Text tokens are at (0, 0, 0); image grids follow frame after
+    frame, each row-major.
+    """
+    rows: List[Tuple[int, int, int]] = []
+    for s in samples:
+        h, w, t = s[0], s[1], s[2]
+        for _ in range(t):
+            rows.append((0, 0, 0))
+        for f in range(_frames(s)):
+            for r in range(h):
+                for c in range(w):
+                    rows.append((r, c, f))
+    return np.array(rows, dtype=np.int64).reshape(-1, 3)
+
+
+def rope_axis_dims(head_dim: int, axes: int):
+    """Head-dim parts of the rotary axes: (D/2, D/2) for (row, col); for
+    (row, col, frame): ((D-16)/2, (D-16)/2, 16)."""
+    if axes == 2:
+        return (head_dim // 2, head_dim // 2)
+    return ((head_dim - 16) // 2, (head_dim - 16) // 2, 16)
 
 
 # ----------------------------------------------------------------------------
@@ -103,6 +148,47 @@ def rope_frequencies(head_dim: int, theta: float = ROPE_THETA) -> np.ndarray:
     """omega_k = theta ** (-k / (D/4)), k = 0 .. D/4 - 1 (one 1D RoPE of dim D/2 per axis)."""
     npair = head_dim // 4
     return np.array([theta ** (-k / npair) for k in range(npair)], dtype=np.float64)
+
+
+def rope_nd_at(x: np.ndarray, pos: np.ndarray, dims, theta: float = ROPE_THETA,
+               inverse: bool = False) -> np.ndarray:
+    """Rotate ``x`` [N, H, D] by the positions ``pos`` [N, A] on A axes.
+
+    Axis a owns the consecutive head dims of part a (sizes ``dims``, summing to
+    D) and is a 1D rotary embedding of dimension d_a: pair k (dims
+    base + 2k, base + 2k + 1) turns by pos_a * theta**(-k / (d_a/2)).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, nh, d = x.shape
+    assert sum(dims) == d and pos.shape[1] == len(dims)
+    out = x.copy()
+    sign = -1.0 if inverse else 1.0
+    base = 0
+    for axis, da in enumerate(dims):
+        p = pos[:, axis].astype(np.float64)
+        for k in range(da // 2):
+            omega = theta ** (-k / (da // 2))
+            phi = sign * p * omega
+            c = np.cos(phi)[:, None]
+            s = np.sin(phi)[:, None]
+            a = x[:, :, base + 2 * k]
+            b = x[:, :, base + 2 * k + 1]
+            out[:, :, base + 2 * k] = a * c - b * s
+            out[:, :, base + 2 * k + 1] = a * s + b * c
+        base += da
+    return out
+
+
+def rope3d(x: np.ndarray, samples: Sequence[Sample], theta: float = ROPE_THETA,
+           inverse: bool = False) -> np.ndarray:
+    """Per-sample 3-axis (row, col, frame) RoPE of a packed tensor [T, H, D]."""
+    d = x.shape[2]
+    return rope_nd_at(x, token_positions3(samples), rope_axis_dims(d, 3), theta, inverse)
+
+
+def rope_apply(x, samples, theta: float = ROPE_THETA, inverse: bool = False, axes: int = 2):
+    """The RoPE of the given mode: 2 axes (row, col) or 3 axes (row, col, frame)."""
+    return rope3d(x, samples, theta, inverse) if axes == 3 else rope2d(x, samples, theta, inverse)
 
 
 def rope2d_at(x: np.ndarray, pos: np.ndarray, theta: float = ROPE_THETA,
@@ -162,13 +248,14 @@ def _attn_one(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
 
 
 def attn_fwd(q, k, v, samples: Sequence[Sample], scale: float = None, rope: bool = False,
-             theta: float = ROPE_THETA):
+             theta: float = ROPE_THETA, axes: int = 2):
     """Packed varlen joint attention forward.
 
     Review page, "Native-Resolution MMDiT": joint self-attention over each
     sample's concatenated text and image tokens, confined to the sample by its
     cumulative offsets.  With ``rope`` the per-sample 2D RoPE is applied to Q
-    and K first.  Returns O [T, H, D] and LSE [H, T] (fp64).
+    and K first (``axes`` = 3: the row, col, frame RoPE of editing samples).
+    Returns O [T, H, D] and LSE [H, T] (fp64).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -177,8 +264,8 @@ def attn_fwd(q, k, v, samples: Sequence[Sample], scale: float = None, rope: bool
     if scale is None:
         scale = default_scale(D)
     if rope:
-        q = rope2d(q, samples, theta)
-        k = rope2d(k, samples, theta)
+        q = rope_apply(q, samples, theta, axes=axes)
+        k = rope_apply(k, samples, theta, axes=axes)
     cu = cu_seqlens(samples)
     o = np.zeros((T, H, D))
     lse = np.zeros((H, T))
@@ -194,7 +281,8 @@ def attn_fwd(q, k, v, samples: Sequence[Sample], scale: float = None, rope: bool
 
 
 def attn_fwd_rows(q, k, v, samples: Sequence[Sample], sample: int, head: int, rows,
-                  scale: float = None, rope: bool = False, theta: float = ROPE_THETA):
+                  scale: float = None, rope: bool = False, theta: float = ROPE_THETA,
+                  axes: int = 2):
     """Selected output rows of ``attn_fwd`` for one (sample, head).
 
     ``rows`` are local query indices inside the sample.  Each output row of the
@@ -211,16 +299,15 @@ def attn_fwd_rows(q, k, v, samples: Sequence[Sample], sample: int, head: int, ro
     ki = np.asarray(k[a:b, head:head + 1], np.float64)
     vi = np.asarray(v[a:b, head], np.float64)
     if rope:
-        pos = token_positions([samples[sample]])
-        qi = rope2d_at(qi, pos, theta)
-        ki = rope2d_at(ki, pos, theta)
+        qi = rope_apply(qi, [samples[sample]], theta, axes=axes)
+        ki = rope_apply(ki, [samples[sample]], theta, axes=axes)
     rows = np.asarray(rows, dtype=np.int64)
     o, lse, _ = _attn_one(qi[rows, 0], ki[:, 0], vi, scale)
     return o, lse
 
 
 def attn_bwd(q, k, v, do, samples: Sequence[Sample], scale: float = None, rope: bool = False,
-             theta: float = ROPE_THETA):
+             theta: float = ROPE_THETA, axes: int = 2):
     """Gradients of L = sum(O * dO) with respect to Q, K, V.
 
     Per sample and head, with P the softmax probabilities:
@@ -237,8 +324,8 @@ def attn_bwd(q, k, v, do, samples: Sequence[Sample], scale: float = None, rope: 
     if scale is None:
         scale = default_scale(D)
     if rope:
-        q = rope2d(q, samples, theta)
-        k = rope2d(k, samples, theta)
+        q = rope_apply(q, samples, theta, axes=axes)
+        k = rope_apply(k, samples, theta, axes=axes)
     cu = cu_seqlens(samples)
     dq = np.zeros((T, H, D))
     dk = np.zeros((T, H, D))
@@ -257,8 +344,8 @@ def attn_bwd(q, k, v, do, samples: Sequence[Sample], scale: float = None, rope: 
             dq[a:b, h] = scale * (ds @ ki)
             dk[a:b, h] = scale * (ds.T @ qi)
     if rope:
-        dq = rope2d(dq, samples, theta, inverse=True)
-        dk = rope2d(dk, samples, theta, inverse=True)
+        dq = rope_apply(dq, samples, theta, inverse=True, axes=axes)
+        dk = rope_apply(dk, samples, theta, inverse=True, axes=axes)
     return dq, dk, dv
 
 
@@ -283,8 +370,7 @@ def dense_masked_attn_fwd(q, k, v, samples: Sequence[Sample], scale: float = Non
         scale = default_scale(D)
     owner = np.empty(T, dtype=np.int64)
     j = 0
-    for i, (h, w, t) in enumerate(samples):
-        n = t + h * w
+    for i, n in enumerate(sample_lengths(samples)):
         owner[j:j + n] = i
         j += n
     mask = owner[:, None] == owner[None, :]
@@ -315,11 +401,12 @@ def pack_joint(text: np.ndarray, image: np.ndarray, samples: Sequence[Sample]) -
     """
     parts = []
     ta = ia = 0
-    for (h, w, t) in samples:
+    for smp in samples:
+        t, n = smp[2], smp[0] * smp[1] * _frames(smp)
         parts.append(text[ta:ta + t])
-        parts.append(image[ia:ia + h * w])
+        parts.append(image[ia:ia + n])
         ta += t
-        ia += h * w
+        ia += n
     assert ta == text.shape[0] and ia == image.shape[0]
     return np.concatenate(parts, axis=0) if parts else text[:0].copy()
 
@@ -328,10 +415,11 @@ def unpack_joint(joint: np.ndarray, samples: Sequence[Sample]):
     """Inverse of ``pack_joint``: split joint rows back into the two streams."""
     texts, images = [], []
     j = 0
-    for (h, w, t) in samples:
+    for smp in samples:
+        t, n = smp[2], smp[0] * smp[1] * _frames(smp)
         texts.append(joint[j:j + t])
-        images.append(joint[j + t:j + t + h * w])
-        j += t + h * w
+        images.append(joint[j + t:j + t + n])
+        j += t + n
     assert j == joint.shape[0]
     if not samples:
         return joint[:0].copy(), joint[:0].copy()

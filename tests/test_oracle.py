@@ -161,7 +161,8 @@ def _masked_sdpa(q, k, v, samples, scale):
     """torch fp64 scaled_dot_product_attention over the whole pack with a boolean
     block-diagonal mask (a library routine, independent of the oracle)."""
     T = q.shape[0]
-    owner = np.concatenate([[i] * (t + h * w) for i, (h, w, t) in enumerate(samples)] + [[]])
+    lens = [s[2] + s[0] * s[1] * (s[3] if len(s) > 3 else 1) for s in samples]
+    owner = np.concatenate([[i] * n for i, n in enumerate(lens)] + [[]])
     owner = owner.astype(np.int64)
     mask = torch.from_numpy(owner[:, None] == owner[None, :])
     qt = torch.from_numpy(q).permute(1, 0, 2)[None]
@@ -385,3 +386,126 @@ def test_cfg_tensors_share_image_rows():
                       shared_image=wl.shared_image)
     assert np.array_equal(q[256:4352], q[4352 + 16:])
     assert not np.array_equal(q[:16], q[4352:4352 + 16])
+
+
+# ----------------------------------------------------------------------------
+# editing mode: 3-axis (row, col, frame) RoPE
+# ----------------------------------------------------------------------------
+
+def test_positions3_hand_example():
+    pos = oracle.token_positions3([(2, 2, 1, 2), (1, 2, 0)])
+    want = [(0, 0, 0),
+            (0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 0),
+            (0, 0, 1), (0, 1, 1), (1, 0, 1), (1, 1, 1),
+            (0, 0, 0), (0, 1, 0)]
+    assert [tuple(p) for p in pos.tolist()] == want
+    assert oracle.sample_lengths([(2, 2, 1, 2), (1, 2, 0)]).tolist() == [9, 2]
+    assert oracle.rope_axis_dims(128, 3) == (56, 56, 16)
+    assert oracle.rope_axis_dims(64, 3) == (24, 24, 16)
+
+
+def test_rope3_worked_values():
+    # D = 32 -> parts (8, 8, 16): row dims 0..7, col dims 8..15, frame dims 16..31
+    def unit(i):
+        e = np.zeros((1, 1, 32)); e[0, 0, i] = 1.0
+        return e
+    dims = oracle.rope_axis_dims(32, 3)
+    y = oracle.rope_nd_at(unit(16), np.array([[5, 3, 1]]), dims)      # frame pair 0 by f = 1
+    assert np.allclose(y[0, 0, 16:18], [math.cos(1), math.sin(1)], atol=1e-15)
+    assert np.allclose(np.delete(y.ravel(), [16, 17]), 0, atol=1e-15)
+    y = oracle.rope_nd_at(unit(8), np.array([[5, 3, 1]]), dims)       # col pair 0 by c = 3
+    assert np.allclose(y[0, 0, 8:10], [math.cos(3), math.sin(3)], atol=1e-15)
+    y = oracle.rope_nd_at(unit(2), np.array([[5, 3, 1]]), dims)       # row pair 1, omega = 1e4**-0.25
+    w = 1e4 ** -0.25
+    assert np.allclose(y[0, 0, 2:4], [math.cos(5 * w), math.sin(5 * w)], atol=1e-15)
+    y = oracle.rope_nd_at(unit(18), np.array([[5, 3, 2]]), dims)      # frame pair 1, omega = 1e4**-1/8
+    w = 1e4 ** (-1 / 8)
+    assert np.allclose(y[0, 0, 18:20], [math.cos(2 * w), math.sin(2 * w)], atol=1e-15)
+
+
+def test_rope_nd_two_axes_equals_2d():
+    rng = np.random.default_rng(30)
+    x = _rand(rng, 12, 2, 64)
+    pos = rng.integers(0, 50, size=(12, 2))
+    assert np.allclose(oracle.rope_nd_at(x, pos, (32, 32)), oracle.rope2d_at(x, pos), atol=1e-14)
+
+
+def test_rope3_norm_inverse_and_shift_invariance():
+    rng = np.random.default_rng(31)
+    samples = [(3, 4, 2, 2)]
+    T, D = 26, 64
+    q, k = _rand(rng, T, 2, D), _rand(rng, T, 2, D)
+    qr = oracle.rope3d(q, samples)
+    assert np.allclose(np.linalg.norm(qr, axis=2), np.linalg.norm(q, axis=2), rtol=1e-14)
+    assert np.allclose(oracle.rope3d(qr, samples, inverse=True), q, atol=1e-13)
+    pos = oracle.token_positions3(samples)[2:]          # image tokens only
+    dims = oracle.rope_axis_dims(D, 3)
+    s0 = np.einsum("ihd,jhd->hij", oracle.rope_nd_at(q[2:], pos, dims),
+                   oracle.rope_nd_at(k[2:], pos, dims))
+    sh = pos + np.array([[4, 9, 3]])
+    s1 = np.einsum("ihd,jhd->hij", oracle.rope_nd_at(q[2:], sh, dims),
+                   oracle.rope_nd_at(k[2:], sh, dims))
+    assert np.allclose(s0, s1, atol=1e-11)
+
+
+def test_frame_axis_separates_source_and_target():
+    # identical source and target grids: the 2-axis RoPE cannot tell them apart
+    # (equal outputs), the frame axis can (the pages' reason for adding it)
+    rng = np.random.default_rng(32)
+    h, w, t = 2, 3, 2
+    n = h * w
+    q, k, v = (_rand(rng, t + 2 * n, 1, 32) for _ in range(3))
+    for x in (q, k, v):
+        x[t + n:] = x[t:t + n]
+    o2, _ = oracle.attn_fwd(q, k, v, [(h, w, t, 2)], rope=True, axes=2)
+    o3, _ = oracle.attn_fwd(q, k, v, [(h, w, t, 2)], rope=True, axes=3)
+    assert np.allclose(o2[t:t + n], o2[t + n:], atol=1e-13)
+    assert np.abs(o3[t:t + n] - o3[t + n:]).max() > 1e-3
+
+
+def test_fwd3_matches_bruteforce_and_sdpa():
+    rng = np.random.default_rng(33)
+    samples = [(2, 3, 2, 2), (3, 1, 1, 1), (0, 0, 3, 1), (2, 2, 0, 3)]
+    T = int(oracle.sample_lengths(samples).sum())
+    q, k, v = (_rand(rng, T, 2, 32) for _ in range(3))
+    o, lse = oracle.attn_fwd(q, k, v, samples, rope=True, axes=3)
+    pos = oracle.token_positions3(samples)
+    dims = oracle.rope_axis_dims(32, 3)
+    qr, kr = oracle.rope_nd_at(q, pos, dims), oracle.rope_nd_at(k, pos, dims)
+    ob, lb = oracle.dense_masked_attn_fwd(qr, kr, v, samples)
+    assert np.abs(o - ob).max() <= 1e-12 and np.abs(lse - lb).max() <= 1e-12
+    os_, ls_ = _masked_sdpa(qr, kr, v, samples, 1 / math.sqrt(32))
+    assert np.abs(o - os_).max() <= 1e-12 and np.abs(lse - ls_).max() <= 1e-12
+
+
+def test_bwd3_finite_differences():
+    rng = np.random.default_rng(34)
+    samples = [(2, 2, 1, 2), (1, 2, 1, 1)]
+    T, H, D = 12, 1, 32
+    q, k, v, do = (_rand(rng, T, H, D) for _ in range(4))
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, samples, rope=True, axes=3)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_fwd(qq, kk, vv, samples, rope=True, axes=3)
+        return float((o * do).sum())
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(8):
+            i, d = rng.integers(0, T), rng.integers(0, D)
+            xp = x.copy(); xp[i, 0, d] += eps
+            xm = x.copy(); xm[i, 0, d] -= eps
+            args = {"q": q, "k": k, "v": v}
+            ap = dict(args); ap[name] = xp
+            am = dict(args); am[name] = xm
+            fd = (loss(ap["q"], ap["k"], ap["v"]) - loss(am["q"], am["k"], am["v"])) / (2 * eps)
+            assert abs(fd - g[i, 0, d]) <= 1e-6 * max(1.0, abs(fd)), (name, i, d)
+
+
+def test_pack3_hand_example():
+    samples = [(1, 2, 1, 2), (0, 0, 1, 1)]
+    text = np.array([100.0, 101.0]).reshape(2, 1, 1)
+    image = np.arange(4).reshape(4, 1, 1) + 200.0
+    joint = oracle.pack_joint(text, image, samples)
+    assert joint.ravel().tolist() == [100, 200, 201, 202, 203, 101]
+    t2, i2 = oracle.unpack_joint(joint, samples)
+    assert np.array_equal(t2, text) and np.array_equal(i2, image)
