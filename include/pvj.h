@@ -77,6 +77,15 @@ typedef struct pvj_sample {
   int32_t l_text; /* text tokens, >= 0 */
 } pvj_sample_t;
 
+/* An editing sample: n_frames latent grids of h_lat x w_lat (source, target,
+ * ...) after its l_text text tokens, frame after frame, each row-major. */
+typedef struct pvj_sample_frames {
+  int32_t h_lat;    /* 0 .. 32767 */
+  int32_t w_lat;    /* 0 .. 32767 */
+  int32_t l_text;   /* >= 0 */
+  int32_t n_frames; /* 0 .. 32767 */
+} pvj_sample_frames_t;
+
 typedef struct pvj_plan_desc {
   int32_t n_heads;      /* H >= 1 */
   int32_t head_dim;     /* D in {64, 128} */
@@ -101,6 +110,19 @@ typedef struct pvj_plan pvj_plan_t;
  */
 PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samples,
                                      const pvj_plan_desc_t* desc, pvj_plan_t** out);
+
+/* Editing packs (review page, "Native-Resolution MMDiT": the edit model adds a
+ * frame axis to the 2D RoPE, so each visual token carries an (h, w, f) index
+ * that tells source from target tokens).  Like pvj_plan_create, but sample i
+ * has l_text + n_frames*h_lat*w_lat tokens, and every RoPE of the plan (the
+ * standalone apply, the fused attention loads, the backward's inverse) is
+ * 3-axis: text at (0,0,0); image token p at (row, col, frame) =
+ * ((p mod hw) / w, p mod w, p / hw); the head dim is split into consecutive
+ * row | col | frame parts of (D-16)/2, (D-16)/2 and 16 dims, each a 1D rotary
+ * embedding of its own dimension d_a (pair k turns by pos * theta^(-k/(d_a/2))).
+ * The pack streams hold the text rows and all frames' image rows. */
+PVJ_API pvj_status_t pvj_plan_create_frames(const pvj_sample_frames_t* samples, int32_t n_samples,
+                                            const pvj_plan_desc_t* desc, pvj_plan_t** out);
 
 /* Sizes of a plan.  Any output pointer may be NULL.  *cu_seqlens_host points
  * into the plan (B+1 int32, valid until destroy); *meta_bytes is the size of
@@ -187,10 +209,15 @@ PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* plan, int32_t which,
                                          const int32_t** items, int32_t* n_items,
                                          int32_t* tile_rows);
 
-/* RoPE tables: cos/sin[p * n_freq + k] = cos/sin(p * theta^(-k/n_freq)), for
- * p in [0, n_pos), k in [0, n_freq = D/4), fp32.  Valid until destroy. */
+/* RoPE tables: cos/sin[p * n_pairs + k] for position p in [0, n_pos) and head-dim
+ * pair k (dims 2k, 2k+1) in [0, n_pairs = D/2): cos/sin(p * theta^(-j/(d_a/2)))
+ * where pair k is pair j of its axis part a (of d_a dims), fp64 rounded to
+ * fp32.  Valid until destroy. */
 PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* plan, const float** cos_tab,
-                                         const float** sin_tab, int32_t* n_pos, int32_t* n_freq);
+                                         const float** sin_tab, int32_t* n_pos, int32_t* n_pairs);
+/* RoPE axes of the plan: n_axes = 2 (row, col) or 3 (row, col, frame) and the
+ * head-dim size of each part (dims[2] = 0 for two axes). */
+PVJ_API pvj_status_t pvj_plan_rope_axes(const pvj_plan_t* plan, int32_t* n_axes, int32_t dims[3]);
 
 /* ---- per-kernel timing (tracing) ---------------------------------------------
  * When enabled, every kernel the library launches is bracketed by two HIP

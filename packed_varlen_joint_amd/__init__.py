@@ -48,6 +48,11 @@ class _Sample(ctypes.Structure):
     _fields_ = [("h_lat", ctypes.c_int32), ("w_lat", ctypes.c_int32), ("l_text", ctypes.c_int32)]
 
 
+class _SampleFrames(ctypes.Structure):
+    _fields_ = [("h_lat", ctypes.c_int32), ("w_lat", ctypes.c_int32), ("l_text", ctypes.c_int32),
+                ("n_frames", ctypes.c_int32)]
+
+
 class _Desc(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_float),
@@ -75,6 +80,9 @@ def load_library():
     sigs = {
         "pvj_plan_create": (I32, [ctypes.POINTER(_Sample), I32, ctypes.POINTER(_Desc),
                                   ctypes.POINTER(P)]),
+        "pvj_plan_create_frames": (I32, [ctypes.POINTER(_SampleFrames), I32,
+                                         ctypes.POINTER(_Desc), ctypes.POINTER(P)]),
+        "pvj_plan_rope_axes": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "pvj_plan_info": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I32),
                                 ctypes.POINTER(ctypes.POINTER(I32)), ctypes.POINTER(SZ)]),
         "pvj_plan_upload": (I32, [P, P, SZ, P]),
@@ -127,17 +135,37 @@ def _dtype_code(dtype) -> int:
 
 class Plan:
     """Per-pack plan: offsets, RoPE tables and work lists (built on the host by
-    ``pvj_plan_create``), plus the device copy of that metadata."""
+    ``pvj_plan_create``), plus the device copy of that metadata.
 
-    def __init__(self, samples: Sequence[Tuple[int, int, int]], n_heads: int, head_dim: int,
-                 dtype="bf16", rope_theta: float = 10000.0):
+    ``samples`` holds (h_lat, w_lat, l_text) triples, or, for an editing pack
+    with a frame axis, (h_lat, w_lat, l_text, n_frames) quadruples, which make
+    the plan's RoPE 3-axis (``pvj_plan_create_frames``).  ``frames=True``
+    forces the 3-axis plan for triples too (one frame each)."""
+
+    def __init__(self, samples: Sequence[Tuple[int, ...]], n_heads: int, head_dim: int,
+                 dtype="bf16", rope_theta: float = 10000.0, frames: bool = None):
         lib = load_library()
-        self.samples = [tuple(int(x) for x in s) for s in samples]
-        arr = (_Sample * max(1, len(self.samples)))(*[_Sample(*s) for s in self.samples])
+        raw = [tuple(int(x) for x in s) for s in samples]
+        if any(len(s) not in (3, 4) for s in raw):
+            raise ValueError("each sample is (h_lat, w_lat, l_text[, n_frames])")
+        if frames is None:
+            frames = any(len(s) == 4 for s in raw)
+        if not frames and any(len(s) == 4 for s in raw):
+            raise ValueError("samples with n_frames need a frames plan")
+        self.frames = bool(frames)
+        self.samples = [s if len(s) == 4 or not frames else s + (1,) for s in raw]
         desc = _Desc(int(n_heads), int(head_dim), _dtype_code(dtype), float(rope_theta),
                      PVJ_ROPE_INTERLEAVED, 1)
         h = ctypes.c_void_p()
-        _check(lib.pvj_plan_create(arr, len(self.samples), ctypes.byref(desc), ctypes.byref(h)))
+        if frames:
+            arr = (_SampleFrames * max(1, len(self.samples)))(
+                *[_SampleFrames(*s) for s in self.samples])
+            _check(lib.pvj_plan_create_frames(arr, len(self.samples), ctypes.byref(desc),
+                                              ctypes.byref(h)))
+        else:
+            arr = (_Sample * max(1, len(self.samples)))(*[_Sample(*s) for s in self.samples])
+            _check(lib.pvj_plan_create(arr, len(self.samples), ctypes.byref(desc),
+                                       ctypes.byref(h)))
         self._h = h
         self.n_heads = int(n_heads)
         self.head_dim = int(head_dim)
@@ -153,7 +181,7 @@ class Plan:
         self.cu_seqlens = [cu[i] for i in range(len(self.samples) + 1)]
         self.meta_bytes = mb.value
         self.n_text = sum(s[2] for s in self.samples)
-        self.n_image = sum(s[0] * s[1] for s in self.samples)
+        self.n_image = sum(s[0] * s[1] * (s[3] if len(s) == 4 else 1) for s in self.samples)
         self._meta = None
 
     @property
@@ -189,15 +217,23 @@ class Plan:
         return [tuple(p[4 * i + j] for j in range(4)) for i in range(n.value)], tr.value
 
     def rope_table(self):
+        """(cos, sin, n_pos, n_pairs): flat [n_pos][n_pairs] fp32 tables."""
         lib = load_library()
         c = ctypes.POINTER(ctypes.c_float)()
         s = ctypes.POINTER(ctypes.c_float)()
         npos = ctypes.c_int32()
-        nf = ctypes.c_int32()
+        npairs = ctypes.c_int32()
         _check(lib.pvj_plan_rope_table(self._h, ctypes.byref(c), ctypes.byref(s),
-                                       ctypes.byref(npos), ctypes.byref(nf)))
-        n = npos.value * nf.value
-        return [c[i] for i in range(n)], [s[i] for i in range(n)], npos.value, nf.value
+                                       ctypes.byref(npos), ctypes.byref(npairs)))
+        n = npos.value * npairs.value
+        return [c[i] for i in range(n)], [s[i] for i in range(n)], npos.value, npairs.value
+
+    def rope_axes(self):
+        """(n_axes, dims): 2 or 3 RoPE axes and the head-dim size of each."""
+        n = ctypes.c_int32()
+        dims = (ctypes.c_int32 * 3)()
+        _check(load_library().pvj_plan_rope_axes(self._h, ctypes.byref(n), dims))
+        return n.value, tuple(dims[i] for i in range(n.value))
 
     def bwd_workspace_bytes(self) -> int:
         b = ctypes.c_size_t()

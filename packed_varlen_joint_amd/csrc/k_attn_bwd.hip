@@ -250,11 +250,8 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
       const int kk = kv0 + row;
       if (kk < L) {
         f32x8 x = *reinterpret_cast<const f32x8*>(stage + row * D + unit * 8);
-        if (rope && pass == 0) {
-          int r, c;
-          token_pos(kk, si.l_text, si.w_lat, r, c);
-          x = rope_chunk(x, unit, D, r, c, m.cos_tab, m.sin_tab, m.n_freq, true);
-        }
+        if (rope && pass == 0)
+          x = rope_unit(x, unit, axis_pos(token_pos3(kk, si), unit_axis(unit, m)), m, true);
         store8<T>(out + base + (size_t)kk * RS + unit * 8, from_f32x8<T>(x));
       }
     }
@@ -393,8 +390,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
 
   // ---- epilogue: dQ = R^T (s dQ'); lane holds query qi, d = 32db + 8g + 4hi + e ----
   if (qi < L) {
-    int pr = 0, pc = 0;
-    if (rope) token_pos(qi, si.l_text, si.w_lat, pr, pc);
+    const RopePos qp = rope ? token_pos3(qi, si) : RopePos{0, 0, 0};
     T* row = dQ + base + (size_t)qi * RS;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -405,9 +401,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * scale;
         if (rope) {
-          const bool col = d0 >= D / 2;
-          const int k0 = (d0 - (col ? D / 2 : 0)) / 2;  // pairs (d0, d0+1), (d0+2, d0+3)
-          const size_t to = (size_t)(col ? pc : pr) * m.n_freq + k0;
+          // pairs (d0, d0+1), (d0+2, d0+3) of unit d0 / 8
+          const size_t to =
+              (size_t)axis_pos(qp, unit_axis(d0 >> 3, m)) * m.n_pairs + (d0 >> 1);
           const f32x2 cs = *reinterpret_cast<const f32x2*>(m.cos_tab + to);
           const f32x2 sn = *reinterpret_cast<const f32x2*>(m.sin_tab + to);
 #pragma unroll

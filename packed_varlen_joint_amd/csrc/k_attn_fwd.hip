@@ -85,8 +85,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load if ROPE ----
   V8 qf[KS];
   {
-    int qr = 0, qc = 0;
-    if (ROPE && qi < L) token_pos(qi, si.l_text, si.w_lat, qr, qc);
+    const RopePos qp = ROPE && qi < L ? token_pos3(qi, si) : RopePos{0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int unit = 2 * ks + hi;
@@ -94,8 +93,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       if (qi < L) {
         v = load8<T>(Qh + (size_t)qi * RS + unit * 8);
         if (ROPE)
-          v = from_f32x8<T>(rope_chunk(to_f32x8(v), unit, D, qr, qc, m.cos_tab, m.sin_tab,
-                                       m.n_freq, false));
+          v = from_f32x8<T>(
+              rope_unit(to_f32x8(v), unit, axis_pos(qp, unit_axis(unit, m)), m, false));
       }
       qf[ks] = v;
     }
@@ -110,10 +109,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int NVR = DMA ? 1 : NK;
   V8 kreg[NKR], vreg[NVR];
   // RoPE: this thread always handles the same unit of the head dim, so its
-  // axis and frequency offset are fixed; only the key position varies
-  const int half_units = D / 16;
-  const bool k_col = k_unit >= half_units;
-  const int k_f0 = (k_unit - (k_col ? half_units : 0)) * 4;
+  // axis is fixed; only the key position varies
+  const int k_axis = unit_axis(k_unit, m);
 
   auto load_tile = [&](int kv0, int b) {
     if constexpr (K_DMA) {
@@ -146,19 +143,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
         V8 v = kreg[i];
         if (ROPE) {
           const int kk = kv0 + k_row0 + i * K_ROW_STEP;
-          int r = 0, c = 0;
-          if (kk < L) token_pos(kk, si.l_text, si.w_lat, r, c);
-          const size_t toffs = (size_t)(k_col ? c : r) * m.n_freq + k_f0;
-          const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + toffs);
-          const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + toffs);
-          f32x8 x = to_f32x8(v), y;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float a = x[2 * q], bb = x[2 * q + 1];
-            y[2 * q] = a * cs[q] - bb * sn[q];
-            y[2 * q + 1] = a * sn[q] + bb * cs[q];
-          }
-          v = from_f32x8<T>(y);
+          const RopePos kp = kk < L ? token_pos3(kk, si) : RopePos{0, 0, 0};
+          v = from_f32x8<T>(rope_unit(to_f32x8(v), k_unit, axis_pos(kp, k_axis), m, false));
         }
         store8<T>(kb + toff<D>(bsigma(k_row0 + i * K_ROW_STEP), k_unit * 8), v);
       }

@@ -28,10 +28,10 @@ static int rows_per_block(const Meta& m, size_t elt) {
   return (int)(r < 1 ? 1 : (r > (size_t)kMaxRowsPerBlock ? kMaxRowsPerBlock : r));
 }
 
-// RoPE position (row, col) of packed row `tok`
-__device__ __forceinline__ void packed_pos(const Meta& m, int tok, int& r, int& c) {
+// RoPE position of packed row `tok`
+__device__ __forceinline__ RopePos packed_pos(const Meta& m, int tok) {
   const SampleInfo si = m.sinfo[find_sample(m.cu, m.n_samples, tok)];
-  token_pos(tok - si.start, si.l_text, si.w_lat, r, c);
+  return token_pos3(tok - si.start, si);
 }
 
 // ---------------------------------------------------------------------------
@@ -113,38 +113,26 @@ hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const
   return hipGetLastError();
 }
 
-// rotate 4 pairs of x by (cs, sn)
-__device__ __forceinline__ f32x8 rot4(f32x8 x, f32x4 cs, f32x4 sn) {
-  f32x8 y;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float a = x[2 * q], b = x[2 * q + 1];
-    y[2 * q] = a * cs[q] - b * sn[q];
-    y[2 * q + 1] = a * sn[q] + b * cs[q];
-  }
-  return y;
-}
-
 // ---------------------------------------------------------------------------
-// standalone 2D RoPE (HF paper page "Highlights": per-sample 2D RoPE; review
-// page, "Kernel fusion": RoPE application is a memory-bound op).
+// standalone per-sample RoPE (HF paper page "Highlights": per-sample 2D RoPE;
+// review page, "Kernel fusion": RoPE application is a memory-bound op; the
+// editing plans' third, frame axis comes from the same tables).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const T* x, T* y, int rpb,
                                                         int inverse) {
-  __shared__ int s_pos[kMaxRowsPerBlock];  // (row << 16) | col of each row's position
-  const int cpr = m.head_dim / 8;           // units per head row
-  const int upr = m.n_heads * cpr;          // units per packed row
-  const int chunk = threadIdx.x % cpr;      // fixed for this thread (cpr | kThreads)
-  const int half_chunks = m.head_dim / 16;
-  const bool col = chunk >= half_chunks;
-  const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
+  __shared__ int s_pos[3][kMaxRowsPerBlock];  // row, col, frame of each row's token
+  const int cpr = m.head_dim / 8;              // units per head row
+  const int upr = m.n_heads * cpr;             // units per packed row
+  const int chunk = threadIdx.x % cpr;         // fixed for this thread (cpr | kThreads)
+  const int axis = unit_axis(chunk, m);
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
   if ((int)threadIdx.x < nrows) {
-    int r, c;
-    packed_pos(m, row0 + threadIdx.x, r, c);
-    s_pos[threadIdx.x] = (r << 16) | c;
+    const RopePos rp = packed_pos(m, row0 + threadIdx.x);
+    s_pos[0][threadIdx.x] = rp.r;
+    s_pos[1][threadIdx.x] = rp.c;
+    s_pos[2][threadIdx.x] = rp.f;
   }
   __syncthreads();
   const int total = nrows * upr;
@@ -157,19 +145,13 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const T* x, T* y
       const int e = e0 + b * kThreads;
       const int row = e / upr, u = e - row * upr;
       off[b] = ((size_t)(row0 + row) * upr + u) * 8;
-      const int pp = e < total ? s_pos[row] : 0;
-      pos[b] = col ? (pp & 0xffff) : (pp >> 16);
+      pos[b] = e < total ? s_pos[axis][row] : 0;
       if (e < total) v[b] = to_f32x8(load8<T>(x + off[b]));
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      if (e0 + b * kThreads < total) {
-        const size_t to = (size_t)pos[b] * m.n_freq + k0;
-        const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
-        f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
-        if (inverse) sn = -sn;
-        store8<T>(y + off[b], from_f32x8<T>(rot4(v[b], cs, sn)));
-      }
+      if (e0 + b * kThreads < total)
+        store8<T>(y + off[b], from_f32x8<T>(rope_unit(v[b], chunk, pos[b], m, inverse != 0)));
     }
   }
 }
@@ -204,19 +186,18 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __re
                                                            float* __restrict__ delta,
                                                            T* __restrict__ qr,
                                                            T* __restrict__ kr, int rpb) {
-  __shared__ int s_pos[kMaxRowsPerBlock];
+  __shared__ int s_pos[3][kMaxRowsPerBlock];
   const int cpr = m.head_dim / 8;
   const int upr = m.n_heads * cpr;
   const int chunk = threadIdx.x % cpr;
-  const int half_chunks = m.head_dim / 16;
-  const bool col = chunk >= half_chunks;
-  const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
+  const int axis = unit_axis(chunk, m);
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
   if (ROPE && (int)threadIdx.x < nrows) {
-    int r, c;
-    packed_pos(m, row0 + threadIdx.x, r, c);
-    s_pos[threadIdx.x] = (r << 16) | c;
+    const RopePos rp = packed_pos(m, row0 + threadIdx.x);
+    s_pos[0][threadIdx.x] = rp.r;
+    s_pos[1][threadIdx.x] = rp.c;
+    s_pos[2][threadIdx.x] = rp.f;
   }
   if (ROPE) __syncthreads();
   const int total = nrows * upr;
@@ -249,12 +230,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __re
       if ((us[b] % cpr) == 0)
         delta[(size_t)(us[b] / cpr) * m.n_tokens + row0 + rows[b]] = s;
       if (ROPE) {
-        const int pp = s_pos[rows[b]];
-        const size_t to = (size_t)(col ? (pp & 0xffff) : (pp >> 16)) * m.n_freq + k0;
-        const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
-        const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
-        store8<T>(qr + off[b], from_f32x8<T>(rot4(x[b], cs, sn)));
-        store8<T>(kr + off[b], from_f32x8<T>(rot4(y[b], cs, sn)));
+        const int pos = s_pos[axis][rows[b]];
+        store8<T>(qr + off[b], from_f32x8<T>(rope_unit(x[b], chunk, pos, m, false)));
+        store8<T>(kr + off[b], from_f32x8<T>(rope_unit(y[b], chunk, pos, m, false)));
       }
     }
   }

@@ -85,39 +85,49 @@ __device__ __forceinline__ int find_sample(const int32_t* cu, int n_samples, int
   return lo - 1;
 }
 
-// RoPE position (row, col) of local token j: text tokens first at (0, 0), then
-// the image grid row-major.
-__device__ __forceinline__ void token_pos(int j, int l_text, int w_lat, int& r, int& c) {
-  if (j < l_text) {
-    r = 0;
-    c = 0;
-  } else {
-    int p = j - l_text;
-    r = p / w_lat;
-    c = p - r * w_lat;
+// RoPE position (row, col, frame) of local token j of a sample: text tokens
+// first at (0, 0, 0), then the image grids frame after frame, each row-major
+// (a plain sample has one frame, so frame = 0).
+struct RopePos {
+  int r, c, f;
+};
+__device__ __forceinline__ RopePos token_pos3(int j, const SampleInfo& si) {
+  RopePos p = {0, 0, 0};
+  if (j >= si.l_text) {  // then the sample has image tokens, so hw > 0
+    int q = j - si.l_text;
+    const int f = q / si.hw;
+    q -= f * si.hw;
+    const int r = q / si.w_lat;
+    p.r = r;
+    p.c = q - r * si.w_lat;
+    p.f = f;
   }
+  return p;
 }
 
-// Rotate the 8-element chunk `chunk` (dims 8*chunk .. 8*chunk+7) of one head
-// row at position (r, c): dims [0, D/2) use the row, [D/2, D) the column;
-// pairs (2k, 2k+1) turn by pos * omega_k, with cos/sin read from the plan's
-// tables.  inverse turns by -angle.
-__device__ __forceinline__ f32x8 rope_chunk(f32x8 x, int chunk, int head_dim, int r, int c,
-                                            const float* cos_tab, const float* sin_tab,
-                                            int n_freq, bool inverse) {
-  const int half_chunks = head_dim / 16;
-  const bool col = chunk >= half_chunks;
-  const int pos = col ? c : r;
-  const int k0 = (chunk - (col ? half_chunks : 0)) * 4;
-  const f32x4 cs = *reinterpret_cast<const f32x4*>(cos_tab + (size_t)pos * n_freq + k0);
-  f32x4 sn = *reinterpret_cast<const f32x4*>(sin_tab + (size_t)pos * n_freq + k0);
+// Position along the RoPE axis of head-dim unit u (dims 8u .. 8u+7): every
+// axis part is a whole number of units (row, then column, then frame).
+__device__ __forceinline__ int unit_axis(int u, const Meta& m) {
+  return u < m.rope_u0 ? 0 : (u < m.rope_u1 ? 1 : 2);
+}
+__device__ __forceinline__ int axis_pos(const RopePos& p, int axis) {
+  return axis == 0 ? p.r : (axis == 1 ? p.c : p.f);
+}
+
+// Rotate the 8 dims of unit u (pairs 4u .. 4u+3) at axis position pos with the
+// plan's cos/sin tables ([pos][D/2 pairs]); pairs (2k, 2k+1) turn as
+// (a, b) -> (a cos - b sin, a sin + b cos); inverse turns by -angle.
+__device__ __forceinline__ f32x8 rope_unit(f32x8 x, int u, int pos, const Meta& m, bool inverse) {
+  const size_t to = (size_t)pos * m.n_pairs + 4 * u;
+  const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
+  f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
   if (inverse) sn = -sn;
   f32x8 y;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float a = x[2 * m], b = x[2 * m + 1];
-    y[2 * m] = a * cs[m] - b * sn[m];
-    y[2 * m + 1] = a * sn[m] + b * cs[m];
+  for (int q = 0; q < 4; ++q) {
+    const float a = x[2 * q], b = x[2 * q + 1];
+    y[2 * q] = a * cs[q] - b * sn[q];
+    y[2 * q + 1] = a * sn[q] + b * cs[q];
   }
   return y;
 }

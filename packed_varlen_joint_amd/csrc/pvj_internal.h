@@ -10,7 +10,7 @@ namespace pvj {
 
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs; workgroups are dealt round-robin
 constexpr size_t kMetaAlign = 256;  // alignment of every metadata section
-constexpr int kMaxLatentSide = 32767;  // h_lat, w_lat limit (positions fit 16-bit fields)
+constexpr int kMaxLatentSide = 32767;  // h_lat, w_lat, n_frames limit (bounds the RoPE tables)
 
 // Rows of one attention work item.  Forward: query rows per workgroup.
 // Backward: key rows per workgroup.
@@ -31,7 +31,9 @@ struct SampleInfo {  // per-sample metadata read by the kernels
   int32_t start;   // first packed row (cu_seqlens[i])
   int32_t len;     // L_i
   int32_t l_text;  // text rows at the start of the sample
-  int32_t w_lat;   // latent grid width (image token p is at (p / w, p % w))
+  int32_t w_lat;   // latent grid width
+  int32_t hw;      // h_lat * w_lat: image token p is at ((p % hw) / w, p % w, p / hw)
+  int32_t pad[3];
 };
 
 // Device view of an uploaded plan (pointers into the caller's metadata buffer).
@@ -40,13 +42,16 @@ struct Meta {
   const int32_t* cu_text;   // [B+1]
   const int32_t* cu_img;    // [B+1]
   const SampleInfo* sinfo;  // [B]
-  const float* cos_tab;     // [n_pos][n_freq]
-  const float* sin_tab;     // [n_pos][n_freq]
+  const float* cos_tab;     // [n_pos][n_pairs]
+  const float* sin_tab;     // [n_pos][n_pairs]
   const Item* fwd_items;    // [n_fwd]
   const Item* bwd_items;    // [n_bwd]
   int32_t n_samples, n_tokens, n_heads, head_dim;
-  int32_t n_pos, n_freq, n_fwd, n_bwd;
+  int32_t n_pos, n_pairs, n_fwd, n_bwd;
   int32_t fwd_tile, bwd_tile, n_text, n_img;
+  // RoPE axis of head-dim unit u (dims 8u .. 8u+7): row if u < rope_u0, column
+  // if u < rope_u1, frame otherwise
+  int32_t rope_u0, rope_u1;
 };
 
 }  // namespace pvj
@@ -57,7 +62,8 @@ struct pvj_plan {
   int32_t n_samples;
   int64_t n_tokens;
   int32_t max_len;
-  int32_t n_pos, n_freq;
+  int32_t n_pos, n_pairs;
+  int32_t rope_axes, rope_dims[3];
   int32_t n_text, n_img;
   int32_t fwd_tile, bwd_tile;
   int32_t n_fwd, n_bwd;

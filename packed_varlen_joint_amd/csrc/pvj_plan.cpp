@@ -90,7 +90,9 @@ Meta device_meta(const pvj_plan* p) {
   m.n_heads = p->desc.n_heads;
   m.head_dim = p->desc.head_dim;
   m.n_pos = p->n_pos;
-  m.n_freq = p->n_freq;
+  m.n_pairs = p->n_pairs;
+  m.rope_u0 = p->rope_dims[0] / 8;
+  m.rope_u1 = (p->rope_dims[0] + p->rope_dims[1]) / 8;
   m.n_fwd = p->n_fwd;
   m.n_bwd = p->n_bwd;
   m.fwd_tile = p->fwd_tile;
@@ -123,13 +125,15 @@ PVJ_API const char* pvj_status_string(pvj_status_t s) {
   return "PVJ_ERR_UNKNOWN";
 }
 
-PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samples,
-                                     const pvj_plan_desc_t* desc, pvj_plan_t** out) {
+// shared by pvj_plan_create (frames = 1, 2 RoPE axes) and
+// pvj_plan_create_frames (3 RoPE axes)
+static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes,
+                                const pvj_plan_desc_t* desc, pvj_plan_t** out) {
   if (!out) return fail(PVJ_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!desc) return fail(PVJ_ERR_INVALID_ARG, "desc is NULL");
   if (n_samples < 0) return fail(PVJ_ERR_INVALID_ARG, "n_samples < 0");
-  if (n_samples > 0 && !samples) return fail(PVJ_ERR_INVALID_ARG, "samples is NULL");
+  if (n_samples > 0 && !hwtf) return fail(PVJ_ERR_INVALID_ARG, "samples is NULL");
   if (desc->n_heads < 1) return fail(PVJ_ERR_INVALID_ARG, "n_heads must be >= 1");
   if (desc->n_heads > 4096) return fail(PVJ_ERR_UNSUPPORTED, "n_heads > 4096");
   if (desc->head_dim != 64 && desc->head_dim != 128)
@@ -146,44 +150,60 @@ PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samp
   std::vector<int32_t> len(B), cu(B + 1), cu_text(B + 1), cu_img(B + 1);
   std::vector<SampleInfo> sinfo(B);
   int64_t T = 0, nt = 0, ni = 0;
-  int32_t max_len = 0, max_side = 0;
+  int32_t max_len = 0, max_side = 0, max_frames = 0;
   cu[0] = cu_text[0] = cu_img[0] = 0;
   for (int i = 0; i < B; ++i) {
-    const pvj_sample_t& s = samples[i];
-    if (s.h_lat < 0 || s.w_lat < 0 || s.l_text < 0)
+    const int32_t h = hwtf[4 * i], w = hwtf[4 * i + 1], t = hwtf[4 * i + 2];
+    const int32_t f = hwtf[4 * i + 3];
+    if (h < 0 || w < 0 || t < 0 || f < 0)
       return fail(PVJ_ERR_INVALID_ARG, "sample %d has a negative size", i);
-    // kernels pack a RoPE position as two 16-bit fields
-    if (s.h_lat > kMaxLatentSide || s.w_lat > kMaxLatentSide)
-      return fail(PVJ_ERR_UNSUPPORTED, "sample %d: latent side above %d", i, kMaxLatentSide);
-    int64_t hw = (int64_t)s.h_lat * (int64_t)s.w_lat;
-    int64_t L = hw + s.l_text;
+    // the RoPE tables have one row per position up to the largest side or frame count
+    if (h > kMaxLatentSide || w > kMaxLatentSide || f > kMaxLatentSide)
+      return fail(PVJ_ERR_UNSUPPORTED, "sample %d: latent side or frames above %d", i,
+                  kMaxLatentSide);
+    const int64_t hw = (int64_t)h * (int64_t)w;
+    const int64_t img = hw * (int64_t)f;
+    const int64_t L = img + t;
     // the kernels index rows with int32 and multiply a row by H*D in int64
-    if (L > INT32_MAX) return fail(PVJ_ERR_OVERFLOW, "sample %d length overflows int32", i);
+    if (hw > INT32_MAX || L > INT32_MAX)
+      return fail(PVJ_ERR_OVERFLOW, "sample %d length overflows int32", i);
     T += L;
-    nt += s.l_text;
-    ni += hw;
+    nt += t;
+    ni += img;
     if (T > INT32_MAX) return fail(PVJ_ERR_OVERFLOW, "packed length T overflows int32");
     len[i] = (int32_t)L;
     cu[i + 1] = (int32_t)T;
     cu_text[i + 1] = (int32_t)nt;
     cu_img[i + 1] = (int32_t)ni;
-    sinfo[i] = {cu[i], (int32_t)L, s.l_text, s.w_lat};
+    sinfo[i] = {cu[i], (int32_t)L, t, w, (int32_t)hw, {0, 0, 0}};
     max_len = std::max(max_len, (int32_t)L);
-    if (hw > 0) max_side = std::max(max_side, std::max(s.h_lat, s.w_lat));
+    if (img > 0) {
+      max_side = std::max(max_side, std::max(h, w));
+      max_frames = std::max(max_frames, f);
+    }
   }
 
   pvj_plan* p = new (std::nothrow) pvj_plan();
   if (!p) return fail(PVJ_ERR_INVALID_ARG, "out of host memory");
+  const int D = desc->head_dim;
   p->desc = *desc;
   p->n_samples = B;
   p->n_tokens = T;
   p->max_len = max_len;
   p->n_text = (int32_t)nt;
   p->n_img = (int32_t)ni;
-  p->n_pos = std::max(1, max_side);
-  p->n_freq = desc->head_dim / 4;
-  p->fwd_tile = fwd_tile_rows(desc->dtype, desc->head_dim);
-  p->bwd_tile = bwd_tile_rows(desc->dtype, desc->head_dim);
+  p->rope_axes = axes;
+  if (axes == 2) {
+    p->rope_dims[0] = p->rope_dims[1] = D / 2;
+    p->rope_dims[2] = 0;
+  } else {
+    p->rope_dims[0] = p->rope_dims[1] = (D - 16) / 2;
+    p->rope_dims[2] = 16;
+  }
+  p->n_pos = std::max(1, std::max(max_side, axes == 3 ? max_frames : 0));
+  p->n_pairs = D / 2;
+  p->fwd_tile = fwd_tile_rows(desc->dtype, D);
+  p->bwd_tile = bwd_tile_rows(desc->dtype, D);
   p->dev_meta = nullptr;
   p->dev_id = -1;
 
@@ -198,7 +218,7 @@ PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samp
     off = align_up(off + std::max<size_t>(bytes, 1), kMetaAlign);
     return o;
   };
-  const size_t tab = (size_t)p->n_pos * p->n_freq * sizeof(float);
+  const size_t tab = (size_t)p->n_pos * p->n_pairs * sizeof(float);
   p->off_cu = section((B + 1) * sizeof(int32_t));
   p->off_cu_text = section((B + 1) * sizeof(int32_t));
   p->off_cu_img = section((B + 1) * sizeof(int32_t));
@@ -217,21 +237,52 @@ PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samp
   std::memcpy(p->image + p->off_cu_text, cu_text.data(), (B + 1) * sizeof(int32_t));
   std::memcpy(p->image + p->off_cu_img, cu_img.data(), (B + 1) * sizeof(int32_t));
   if (B) std::memcpy(p->image + p->off_sinfo, sinfo.data(), B * sizeof(SampleInfo));
-  // RoPE tables: angle p * theta^(-k / (D/4)) in double, rounded to float once
+  // RoPE tables: pair k belongs to axis part a; as pair j of that part its angle
+  // is pos * theta^(-j / (d_a/2)), computed in double and rounded to float once
   float* ct = reinterpret_cast<float*>(p->image + p->off_cos);
   float* st = reinterpret_cast<float*>(p->image + p->off_sin);
-  for (int k = 0; k < p->n_freq; ++k) {
-    const double omega = std::pow((double)desc->rope_theta, -(double)k / (double)p->n_freq);
-    for (int pos = 0; pos < p->n_pos; ++pos) {
-      const double phi = (double)pos * omega;
-      ct[(size_t)pos * p->n_freq + k] = (float)std::cos(phi);
-      st[(size_t)pos * p->n_freq + k] = (float)std::sin(phi);
+  int k = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int half = p->rope_dims[a] / 2;
+    for (int j = 0; j < half; ++j, ++k) {
+      const double omega = std::pow((double)desc->rope_theta, -(double)j / (double)half);
+      for (int pos = 0; pos < p->n_pos; ++pos) {
+        const double phi = (double)pos * omega;
+        ct[(size_t)pos * p->n_pairs + k] = (float)std::cos(phi);
+        st[(size_t)pos * p->n_pairs + k] = (float)std::sin(phi);
+      }
     }
   }
   if (!fwd.empty()) std::memcpy(p->image + p->off_fwd, fwd.data(), fwd.size() * sizeof(Item));
   if (!bwd.empty()) std::memcpy(p->image + p->off_bwd, bwd.data(), bwd.size() * sizeof(Item));
   *out = p;
   return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_plan_create(const pvj_sample_t* samples, int32_t n_samples,
+                                     const pvj_plan_desc_t* desc, pvj_plan_t** out) {
+  if (n_samples > 0 && !samples) return fail(PVJ_ERR_INVALID_ARG, "samples is NULL");
+  std::vector<int32_t> v(4 * (size_t)std::max(n_samples, 0));
+  for (int i = 0; i < n_samples; ++i) {
+    v[4 * i] = samples[i].h_lat;
+    v[4 * i + 1] = samples[i].w_lat;
+    v[4 * i + 2] = samples[i].l_text;
+    v[4 * i + 3] = 1;
+  }
+  return create_plan(v.data(), n_samples, 2, desc, out);
+}
+
+PVJ_API pvj_status_t pvj_plan_create_frames(const pvj_sample_frames_t* samples, int32_t n_samples,
+                                            const pvj_plan_desc_t* desc, pvj_plan_t** out) {
+  if (n_samples > 0 && !samples) return fail(PVJ_ERR_INVALID_ARG, "samples is NULL");
+  std::vector<int32_t> v(4 * (size_t)std::max(n_samples, 0));
+  for (int i = 0; i < n_samples; ++i) {
+    v[4 * i] = samples[i].h_lat;
+    v[4 * i + 1] = samples[i].w_lat;
+    v[4 * i + 2] = samples[i].l_text;
+    v[4 * i + 3] = samples[i].n_frames;
+  }
+  return create_plan(v.data(), n_samples, 3, desc, out);
 }
 
 PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* p, int64_t* n_tokens, int32_t* max_len,
@@ -262,12 +313,20 @@ PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* p, int32_t which,
 }
 
 PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* p, const float** cos_tab,
-                                         const float** sin_tab, int32_t* n_pos, int32_t* n_freq) {
+                                         const float** sin_tab, int32_t* n_pos, int32_t* n_pairs) {
   if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
   if (cos_tab) *cos_tab = host_section<float>(p, p->off_cos);
   if (sin_tab) *sin_tab = host_section<float>(p, p->off_sin);
   if (n_pos) *n_pos = p->n_pos;
-  if (n_freq) *n_freq = p->n_freq;
+  if (n_pairs) *n_pairs = p->n_pairs;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_plan_rope_axes(const pvj_plan_t* p, int32_t* n_axes, int32_t dims[3]) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (n_axes) *n_axes = p->rope_axes;
+  if (dims)
+    for (int a = 0; a < 3; ++a) dims[a] = p->rope_dims[a];
   return PVJ_OK;
 }
 

@@ -27,9 +27,15 @@ available here):
                    exceed the budget; forward + backward.
 * ``extreme``      2048x2048, 2048x512, 512x2048 and four 512x512 samples, each
                    with text length drawn from [16, 512]; forward + backward.
+* ``edit_1024``    an editing pack (review page, section "Native-Resolution
+                   MMDiT": the edit model joins source and target latents under
+                   a frame axis): a 1024x1024 pair (two 64x64 frames) with 256
+                   text tokens and a 768x1024 pair (two 48x64 frames) with 128
+                   text tokens; 3-axis RoPE; forward + backward.
 
 A sample is the triple ``(h_lat, w_lat, l_text)`` (latent rows, latent columns,
-text tokens).  Tensors are packed ``[T, H, D]`` with samples in input order.
+text tokens), or for an editing pack the quadruple ``(h_lat, w_lat, l_text,
+n_frames)``.  Tensors are packed ``[T, H, D]`` with samples in input order.
 """
 from __future__ import annotations
 
@@ -38,7 +44,7 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-Sample = Tuple[int, int, int]  # (h_lat, w_lat, l_text)
+Sample = Tuple[int, ...]  # (h_lat, w_lat, l_text[, n_frames])
 
 PIXELS_PER_TOKEN_SIDE = 16  # Mage-VAE: 16x spatial downsampling, patchify absorbed
 TRAIN_TOKEN_BUDGET = 65536
@@ -59,7 +65,16 @@ class Workload:
     @property
     def n_tokens(self) -> int:
         # the total row count of the packed tensors (inputs are sized by it)
-        return int(sum(t + h * w for (h, w, t) in self.samples))
+        return int(sum(_rows(s) for s in self.samples))
+
+    @property
+    def frames(self) -> bool:
+        return any(len(s) == 4 for s in self.samples)
+
+
+def _rows(s: Sample) -> int:
+    """Rows a sample occupies in the packed tensors (for sizing inputs)."""
+    return s[2] + s[0] * s[1] * (s[3] if len(s) == 4 else 1)
 
 
 def draw_train_pack(seed: int, budget: int = TRAIN_TOKEN_BUDGET) -> List[Sample]:
@@ -104,10 +119,13 @@ def workload(name: str, seed: int = 0) -> Workload:
         return Workload(name, draw_train_pack(seed), 24, 128, "bf16", True, 1000 + seed)
     if name == "extreme":
         return Workload(name, draw_extreme_pack(seed), 24, 128, "bf16", True, seed)
+    if name == "edit_1024":
+        return Workload(name, [(64, 64, 256, 2), (48, 64, 128, 2)], 24, 128, "bf16", True,
+                        2000 + seed)
     raise KeyError(name)
 
 
-WORKLOADS = ["tiny_f32", "single_1024", "cfg_1024", "train_64k", "extreme"]
+WORKLOADS = ["tiny_f32", "single_1024", "cfg_1024", "train_64k", "extreme", "edit_1024"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -131,10 +149,10 @@ def draw_tensors(n_tokens: int, n_heads: int, head_dim: int, dtype: str, seed: i
     for _ in range(n):
         x = rng.standard_normal((n_tokens, n_heads, head_dim), dtype=np.float32)
         if shared_image:
-            starts = np.concatenate([[0], np.cumsum([t + h * w for (h, w, t) in samples])])
+            starts = np.concatenate([[0], np.cumsum([_rows(s) for s in samples])])
             for (src, dst) in shared_image:
-                hs, ws, ts = samples[src]
-                hd, wd, td = samples[dst]
+                hs, ws, ts = samples[src][:3]
+                hd, wd, td = samples[dst][:3]
                 assert (hs, ws) == (hd, wd)
                 a = int(starts[src]) + ts
                 b = int(starts[dst]) + td
@@ -151,15 +169,20 @@ def workload_tensors(wl: Workload, n: int = 4) -> List[np.ndarray]:
 
 
 def random_small_pack(rng: np.random.Generator, n_samples: int, max_side: int = 6,
-                      max_text: int = 7, allow_empty: bool = True) -> List[Sample]:
-    """Tiny random packs for brute-force checks (may include empty/text-only/image-only)."""
+                      max_text: int = 7, allow_empty: bool = True,
+                      max_frames: int = 0) -> List[Sample]:
+    """Tiny random packs for brute-force checks (may include empty/text-only/image-only).
+
+    With ``max_frames`` > 0 every sample is a quadruple with n_frames drawn from
+    [0 or 1, max_frames] (0 only when ``allow_empty``)."""
     out = []
     lo = 0 if allow_empty else 1
     for _ in range(n_samples):
         h = int(rng.integers(lo, max_side + 1))
         w = int(rng.integers(lo, max_side + 1)) if h > 0 else 0
         t = int(rng.integers(lo, max_text + 1))
-        if not allow_empty and h * w + t == 0:
+        f = int(rng.integers(lo, max_frames + 1)) if max_frames > 0 else 1
+        if not allow_empty and h * w * f + t == 0:
             t = 1
-        out.append((h, w, t))
+        out.append((h, w, t, f) if max_frames > 0 else (h, w, t))
     return out

@@ -103,17 +103,58 @@ def test_work_list_xcd_balance(lib):
     assert max(load) <= 1.10 * (sum(load) / 8)
 
 
+def _oracle_pair_angle(D, axes, pos, k):
+    """(cos, sin) the oracle gives pair k at position `pos` on pair k's axis:
+    rotate the unit vector e_{2k} and read dims 2k, 2k+1."""
+    dims = oracle.rope_axis_dims(D, axes)
+    x = np.zeros((1, 1, D))
+    x[0, 0, 2 * k] = 1.0
+    a = int(np.searchsorted(np.cumsum(dims), 2 * k, side="right"))  # axis of dim 2k
+    p = np.zeros((1, axes), dtype=np.int64)
+    p[0, a] = pos
+    y = oracle.rope_nd_at(x, p, dims)
+    return y[0, 0, 2 * k], y[0, 0, 2 * k + 1]
+
+
 @pytest.mark.parametrize("D", [64, 128])
-def test_rope_tables(lib, D):
-    samples = [(37, 5, 3), (2, 90, 1)]
+@pytest.mark.parametrize("axes", [2, 3])
+def test_rope_tables(lib, D, axes):
+    samples = [(37, 5, 3), (2, 90, 1)] if axes == 2 else [(37, 5, 3, 3), (2, 90, 1, 100)]
     p = _plan(samples, 1, D)
-    cos_t, sin_t, npos, nf = p.rope_table()
-    assert npos == 90 and nf == D // 4
-    omega = oracle.rope_frequencies(D)
+    cos_t, sin_t, npos, npairs = p.rope_table()
+    assert npos == (90 if axes == 2 else 100) and npairs == D // 2
+    assert p.rope_axes() == (axes, tuple(oracle.rope_axis_dims(D, axes)))
     for pos in (0, 1, 17, 89):
-        for k in range(nf):
-            assert abs(cos_t[pos * nf + k] - math.cos(pos * omega[k])) <= 6e-8
-            assert abs(sin_t[pos * nf + k] - math.sin(pos * omega[k])) <= 6e-8
+        for k in range(npairs):
+            c, s_ = _oracle_pair_angle(D, axes, pos, k)
+            assert abs(cos_t[pos * npairs + k] - c) <= 6e-8
+            assert abs(sin_t[pos * npairs + k] - s_) <= 6e-8
+
+
+def test_frames_plan_offsets_and_work_lists(lib):
+    rng = np.random.default_rng(5)
+    for _ in range(10):
+        samples = random_small_pack(rng, int(rng.integers(0, 9)), max_side=30, max_text=200,
+                                    max_frames=3)
+        p = _plan(samples, int(rng.integers(1, 4)), 128, "bf16")
+        assert p.frames and p.rope_axes()[0] == 3
+        assert p.cu_seqlens == oracle.cu_seqlens(samples).tolist()
+        assert p.n_image == sum(h * w * f for (h, w, t, f) in samples)
+        _check_work_list(p, samples, 0)
+        _check_work_list(p, samples, 1)
+    # a triple plan forced to frames mode is the one-frame editing plan
+    p = pvj.Plan([(4, 5, 6)], 2, 64, "f32", frames=True)
+    assert p.samples == [(4, 5, 6, 1)] and p.rope_axes()[0] == 3
+    with pytest.raises(ValueError):
+        pvj.Plan([(4, 5, 6, 2)], 2, 64, "f32", frames=False)
+
+
+@pytest.mark.parametrize("name", ["edit_1024"])
+def test_edit_workload_plan(lib, name):
+    wl = workload(name)
+    p = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
+    assert p.n_tokens == wl.n_tokens == int(oracle.sample_lengths(wl.samples).sum())
+    assert p.rope_axes() == (3, (56, 56, 16))
 
 
 def test_empty_and_degenerate_packs(lib):
@@ -130,6 +171,16 @@ def _create(lib, samples, H=2, D=64, dtype=0, theta=1e4, pairing=0, text_first=1
     desc = pvj._Desc(H, D, dtype, theta, pairing, text_first)
     h = ctypes.c_void_p()
     st = lib.pvj_plan_create(arr, len(samples), ctypes.byref(desc), ctypes.byref(h))
+    if st == 0:
+        lib.pvj_plan_destroy(h)
+    return st
+
+
+def _create_frames(lib, samples, H=2, D=64):
+    arr = (pvj._SampleFrames * max(1, len(samples)))(*[pvj._SampleFrames(*s) for s in samples])
+    desc = pvj._Desc(H, D, 0, 1e4, 0, 1)
+    h = ctypes.c_void_p()
+    st = lib.pvj_plan_create_frames(arr, len(samples), ctypes.byref(desc), ctypes.byref(h))
     if st == 0:
         lib.pvj_plan_destroy(h)
     return st
@@ -152,6 +203,12 @@ def test_error_codes(lib):
     assert _create(lib, [(30000, 30000, 0)] * 3) == OVERFLOW       # T > int32
     h = ctypes.c_void_p()
     assert lib.pvj_plan_create(None, 1, None, ctypes.byref(h)) == INVALID
+    assert _create_frames(lib, [(2, 3, 4, 2)]) == 0
+    assert _create_frames(lib, [(2, 3, 4, 0)]) == 0                # text only
+    assert _create_frames(lib, [(2, 3, 4, -1)]) == INVALID
+    assert _create_frames(lib, [(2, 3, 4, 32768)]) == UNSUP         # frame index limit
+    assert _create_frames(lib, [(30000, 30000, 0, 3)]) == OVERFLOW
+    assert _create_frames(lib, [(1, 1, 1, 1)], D=96) == UNSUP
     assert lib.pvj_status_string(5).decode() == "PVJ_ERR_WORKSPACE_TOO_SMALL"
     assert "int32" in lib.pvj_last_error().decode() or lib.pvj_last_error()
 
