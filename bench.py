@@ -3,10 +3,13 @@
 
 One step = the whole path over one synthetic pack, with every input already
 resident in HBM when the timed region starts:
-  plan (host planner + metadata upload) -> pack Q, K, V from the text/image
-  streams -> attention forward with 2D RoPE fused on load -> unpack O ->
-  pack dO -> attention backward (Delta preprocess, main kernel, dQ finalize
-  with the inverse rotation) -> unpack dQ, dK, dV.
+  plan (host planner + metadata upload) -> pack Q and K with the 2D RoPE in
+  the same pass, pack V -> attention forward -> unpack O -> pack dO ->
+  attention backward (Delta preprocess, dK/dV kernel, dQ kernel; both rotate
+  their gradient back with the inverse RoPE in the epilogue) -> unpack dQ,
+  dK, dV.
+`--rope load` instead packs Q and K plainly and rotates them on load inside
+the attention kernels (forward) and in the backward preprocess.
 
 Default workload: the native-resolution training pack (65,536-token budget,
 seed 0: 7 samples, 55,151 tokens, 24 heads, head_dim 128, bf16), the pack on
@@ -63,15 +66,16 @@ def _traffic(kernel):
 
 
 class PackStep:
-    def __init__(self, wl, seed):
+    def __init__(self, wl, seed, rope="pack"):
         import torch
         import packed_varlen_joint_amd as pvj
         self.pvj = pvj
         self.wl = wl
+        self.rope = rope
         H, D = wl.n_heads, wl.head_dim
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        nt = sum(t for (_, _, t) in wl.samples)
-        ni = sum(h * w for (h, w, _) in wl.samples)
+        probe = pvj.Plan(wl.samples, H, D, wl.dtype)
+        nt, ni = probe.n_text, probe.n_image
         T = wl.n_tokens
         g = torch.Generator(device="cuda").manual_seed(seed)
         mk = lambda n: torch.randn(n, H, D, device="cuda", generator=g).to(dt)
@@ -83,7 +87,6 @@ class PackStep:
                                 torch.empty(ni, H, D, device="cuda", dtype=dt))
                             for x in ("o", "dq", "dk", "dv")}
         self.lse = torch.empty(H, T, device="cuda", dtype=torch.float32)
-        probe = pvj.Plan(wl.samples, H, D, wl.dtype)
         self.ws = torch.empty(max(256, probe.bwd_workspace_bytes()), device="cuda",
                               dtype=torch.uint8)
         self.plan = None
@@ -91,16 +94,17 @@ class PackStep:
     def __call__(self):
         pvj, wl, j = self.pvj, self.wl, self.joint
         plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+        in_pack = self.rope == "pack"
         for x in ("q", "k", "v"):
-            pvj.pack(plan, *self.streams[x], joint=j[x])
-        pvj.varlen_attn_fwd(plan, j["q"], j["k"], j["v"], rope_fused=True, out=j["o"],
+            pvj.pack(plan, *self.streams[x], joint=j[x], rope=in_pack and x != "v")
+        pvj.varlen_attn_fwd(plan, j["q"], j["k"], j["v"], rope_fused=not in_pack, out=j["o"],
                             lse=self.lse)
         pvj.unpack(plan, j["o"], *self.out_streams["o"])
         if wl.backward:
             pvj.pack(plan, *self.streams["do"], joint=j["do"])
             pvj.varlen_attn_bwd(plan, j["q"], j["k"], j["v"], j["o"], self.lse, j["do"],
-                                rope_fused=True, dq=j["dq"], dk=j["dk"], dv=j["dv"],
-                                workspace=self.ws)
+                                rope_fused=not in_pack, rope_prerotated=in_pack,
+                                dq=j["dq"], dk=j["dk"], dv=j["dv"], workspace=self.ws)
             for x in ("dq", "dk", "dv"):
                 pvj.unpack(plan, j[x], *self.out_streams[x])
         self.plan = plan
@@ -118,20 +122,21 @@ def cpu_baseline(wl, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
-    order = sorted(range(len(wl.samples)), key=lambda i: wl.samples[i][2] + wl.samples[i][0] *
-                   wl.samples[i][1])
+    lens = oracle.sample_lengths(wl.samples)
+    axes = 3 if wl.frames else 2
+    order = sorted(range(len(wl.samples)), key=lambda i: lens[i])
     flops = 0.0
     done = []
     t0 = time.perf_counter()
     for i in order:
         s = wl.samples[i]
-        L = s[2] + s[0] * s[1]
+        L = int(lens[i])
         if L == 0:
             continue
         for h in range(wl.n_heads):
             q, k, v, do = draw_tensors(L, 1, wl.head_dim, wl.dtype, 7 + i * 100 + h, n=4)
-            oracle.attn_fwd(q, k, v, [s], rope=True)
-            oracle.attn_bwd(q, k, v, do, [s], rope=True)
+            oracle.attn_fwd(q, k, v, [s], rope=True, axes=axes)
+            oracle.attn_bwd(q, k, v, do, [s], rope=True, axes=axes)
             flops += 14.0 * wl.head_dim * L * L
             done.append((i, h, L))
             if time.perf_counter() - t0 >= seconds:
@@ -154,6 +159,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope", choices=("pack", "load"), default="pack",
+                    help="RoPE fused into the Q/K pack (default) or applied on load inside "
+                         "the attention kernels")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 512 MiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -179,13 +187,15 @@ def main():
         return
     wl = workload(args.workload, args.seed)
     H, D = wl.n_heads, wl.head_dim
-    lens = [t + h * w for (h, w, t) in wl.samples]
+    probe = pvj.Plan(wl.samples, H, D, wl.dtype)
+    cu = probe.cu_seqlens
+    lens = [cu[i + 1] - cu[i] for i in range(len(wl.samples))]
     S2 = float(sum(L * L for L in lens))
     f_fwd = 4.0 * H * D * S2
     f_bwd = 10.0 * H * D * S2
     f_step = f_fwd + (f_bwd if wl.backward else 0.0)
 
-    step = PackStep(wl, args.seed)
+    step = PackStep(wl, args.seed, args.rope)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -239,7 +249,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "seed": args.seed, "n_samples": len(wl.samples),
                    "n_tokens": wl.n_tokens, "heads": H, "head_dim": D,
-                   "sum_len_sq": int(S2), "backward": wl.backward, "rope": "fused on load",
+                   "sum_len_sq": int(S2), "backward": wl.backward,
+                   "rope": ("3-axis " if wl.frames else "2D ") + (
+                       "fused into the Q/K pack" if args.rope == "pack" else "fused on load"),
                    "step": "plan+pack+attn fwd+unpack" + ("+pack dO+attn bwd+unpack grads"
                                                            if wl.backward else "")},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

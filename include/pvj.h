@@ -69,7 +69,8 @@ typedef enum pvj_status {
 
 enum { PVJ_BF16 = 0, PVJ_F32 = 1 };          /* pvj_plan_desc_t.dtype */
 enum { PVJ_ROPE_INTERLEAVED = 0 };           /* pvj_plan_desc_t.rope_pairing */
-enum { PVJ_FLAG_ROPE_FUSED = 1u };           /* attention flags */
+enum { PVJ_FLAG_ROPE_FUSED = 1u,             /* attention flags */
+       PVJ_FLAG_ROPE_PREROTATED = 2u };      /* backward only */
 
 typedef struct pvj_sample {
   int32_t h_lat;  /* latent rows    (image pixels / 16), 0 .. 32767 */
@@ -153,6 +154,21 @@ PVJ_API pvj_status_t pvj_pack(const pvj_plan_t* plan, const void* text, const vo
 PVJ_API pvj_status_t pvj_unpack(const pvj_plan_t* plan, const void* joint, void* text,
                                 void* image, void* stream);
 
+/* Pack or unpack with the RoPE in the same pass (review page, "Kernel fusion":
+ * the memory-bound chains, RoPE application among them, are fused so each
+ * tensor is read and written once).  pvj_pack_rope writes R(pos) x (inverse
+ * != 0: R(pos)^T x) into the joint layout; pvj_unpack_rope rotates each joint
+ * row before scattering it to the streams.  The result is bitwise that of
+ * pvj_pack then pvj_rope2d_apply (or pvj_rope2d_apply then pvj_unpack): fp32
+ * rotation from the plan's tables, rounded once to the plan dtype.  Q and K
+ * packed this way feed pvj_varlen_attn_fwd without flags and
+ * pvj_varlen_attn_bwd with PVJ_FLAG_ROPE_PREROTATED.  Buffers must not
+ * overlap. */
+PVJ_API pvj_status_t pvj_pack_rope(const pvj_plan_t* plan, const void* text, const void* image,
+                                   void* joint, int32_t inverse, void* stream);
+PVJ_API pvj_status_t pvj_unpack_rope(const pvj_plan_t* plan, const void* joint, void* text,
+                                     void* image, int32_t inverse, void* stream);
+
 /* ---- standalone per-sample 2D RoPE ------------------------------------------
  * HF paper page "Highlights" / model card "Architecture": per-sample 2D rotary
  * embedding; review page, "Kernel fusion": RoPE application is one of the
@@ -183,13 +199,19 @@ PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* plan, const void* q, 
  * "Kernel fusion": 8-GPU training at ~50K packed tokens per GPU):
  *   Delta = rowsum(dO * O); P = exp(s Q'K'^T - LSE); dV = P^T dO;
  *   dS = P * (dO V^T - Delta); dQ' = s dS K'; dK' = s dS^T Q';
- * with PVJ_FLAG_ROPE_FUSED, dQ = R^T dQ' and dK = R^T dK' (gradients with
- * respect to the un-rotated Q, K); otherwise dQ = dQ', dK = dK'.
- * q, k, v, o, lse and the flags/scale must be those of the forward call.
+ * with PVJ_FLAG_ROPE_FUSED, Q' = R Q and K' = R K are formed here and
+ * dQ = R^T dQ', dK = R^T dK' (gradients with respect to the un-rotated Q, K);
+ * with PVJ_FLAG_ROPE_PREROTATED, q and k already hold Q' and K' (for example
+ * from pvj_pack_rope, with a forward called without flags) and dQ = R^T dQ',
+ * dK = R^T dK' likewise; with neither, dQ = dQ', dK = dK'.  The two flags
+ * exclude each other (INVALID_ARG).  Both RoPE modes give the same bits when
+ * the pre-rotated Q', K' were rounded as pvj_rope2d_apply rounds them.
+ * q, k, v, o, lse and the scale must be those of the forward call.
  * workspace: device memory of at least pvj_varlen_attn_bwd_workspace bytes,
  * 256-byte aligned, owned by the caller, contents need not be initialised;
  * it holds Delta (fp32 [H, T]) and, with PVJ_FLAG_ROPE_FUSED, the rotated
- * Q' and K' (two [T, H, D] tensors in the plan dtype).  No atomics: dQ, dK
+ * Q' and K' (two [T, H, D] tensors in the plan dtype; the size always counts
+ * them).  No atomics: dQ, dK
  * and dV are deterministic (the same inputs give the same bits).
  */
 PVJ_API pvj_status_t pvj_varlen_attn_bwd_workspace(const pvj_plan_t* plan, size_t* bytes);

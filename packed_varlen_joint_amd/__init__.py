@@ -32,6 +32,7 @@ PVJ_BF16 = 0
 PVJ_F32 = 1
 PVJ_ROPE_INTERLEAVED = 0
 PVJ_FLAG_ROPE_FUSED = 1
+PVJ_FLAG_ROPE_PREROTATED = 2
 
 KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
            "attn_bwd_dq": 6}
@@ -89,6 +90,8 @@ def load_library():
         "pvj_plan_destroy": (None, [P]),
         "pvj_pack": (I32, [P, P, P, P, P]),
         "pvj_unpack": (I32, [P, P, P, P, P]),
+        "pvj_pack_rope": (I32, [P, P, P, P, I32, P]),
+        "pvj_unpack_rope": (I32, [P, P, P, P, I32, P]),
         "pvj_rope2d_apply": (I32, [P, P, P, I32, P]),
         "pvj_varlen_attn_fwd": (I32, [P, P, P, P, P, P, F, U32, P]),
         "pvj_varlen_attn_bwd_workspace": (I32, [P, ctypes.POINTER(SZ)]),
@@ -296,25 +299,36 @@ def _empty_tokens(plan: Plan, like, rows=None):
                        device=like.device)
 
 
-def pack(plan: Plan, text, image, joint=None):
-    """Joint [T,H,D] from the text [sum t,H,D] and image [sum h*w,H,D] streams."""
+def pack(plan: Plan, text, image, joint=None, rope: bool = False, inverse: bool = False):
+    """Joint [T,H,D] from the text [sum t,H,D] and image [sum h*w,H,D] streams
+    (``rope``: rotated by the plan's RoPE in the same pass)."""
     _check_tokens(plan, "text", text, plan.n_text)
     _check_tokens(plan, "image", image, plan.n_image)
     joint = _empty_tokens(plan, text) if joint is None else joint
     _check_tokens(plan, "joint", joint)
-    _check(load_library().pvj_pack(plan.handle, _ptr(text), _ptr(image), _ptr(joint), _stream()))
+    lib = load_library()
+    if rope:
+        _check(lib.pvj_pack_rope(plan.handle, _ptr(text), _ptr(image), _ptr(joint),
+                                 int(bool(inverse)), _stream()))
+    else:
+        _check(lib.pvj_pack(plan.handle, _ptr(text), _ptr(image), _ptr(joint), _stream()))
     return joint
 
 
-def unpack(plan: Plan, joint, text=None, image=None):
-    """Inverse of ``pack``: (text, image) streams from the joint tensor."""
+def unpack(plan: Plan, joint, text=None, image=None, rope: bool = False, inverse: bool = False):
+    """Inverse of ``pack``: (text, image) streams from the joint tensor
+    (``rope``: each row rotated by the plan's RoPE in the same pass)."""
     _check_tokens(plan, "joint", joint)
     text = _empty_tokens(plan, joint, plan.n_text) if text is None else text
     image = _empty_tokens(plan, joint, plan.n_image) if image is None else image
     _check_tokens(plan, "text", text, plan.n_text)
     _check_tokens(plan, "image", image, plan.n_image)
-    _check(load_library().pvj_unpack(plan.handle, _ptr(joint), _ptr(text), _ptr(image),
-                                     _stream()))
+    lib = load_library()
+    if rope:
+        _check(lib.pvj_unpack_rope(plan.handle, _ptr(joint), _ptr(text), _ptr(image),
+                                   int(bool(inverse)), _stream()))
+    else:
+        _check(lib.pvj_unpack(plan.handle, _ptr(joint), _ptr(text), _ptr(image), _stream()))
     return text, image
 
 
@@ -345,8 +359,12 @@ def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused:
 
 
 def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.0,
-                    rope_fused: bool = False, dq=None, dk=None, dv=None, workspace=None):
-    """Packed varlen joint attention backward; returns (dQ, dK, dV)."""
+                    rope_fused: bool = False, dq=None, dk=None, dv=None, workspace=None,
+                    rope_prerotated: bool = False):
+    """Packed varlen joint attention backward; returns (dQ, dK, dV).
+
+    ``rope_prerotated``: q and k already hold R Q and R K (``pack(..., rope=True)``);
+    dQ and dK still come back with respect to the un-rotated Q and K."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tokens(plan, n, t)
@@ -356,7 +374,8 @@ def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.
     nbytes = plan.bwd_workspace_bytes()
     if workspace is None:
         workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=q.device)
-    flags = PVJ_FLAG_ROPE_FUSED if rope_fused else 0
+    flags = (PVJ_FLAG_ROPE_FUSED if rope_fused else 0) | (
+        PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0)
     _check(load_library().pvj_varlen_attn_bwd(
         plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), float(softmax_scale), flags,

@@ -38,17 +38,26 @@ __device__ __forceinline__ RopePos packed_pos(const Meta& m, int tok) {
 // pack / unpack: joint row j of sample i <-> text row cu_text[i] + j (j < t_i)
 // or image row cu_img[i] + j - t_i.  Review page, "Native-Resolution MMDiT":
 // text and image streams concatenated per sample for the joint attention.
+// With ROPE the same pass also rotates every unit by the plan's RoPE (review
+// page, "Kernel fusion": RoPE application is one of the memory-bound ops
+// fused so the data is read and written once): the joint tensor then holds
+// R x (pack) or the streams get R^T x (unpack with inverse), with the rounding
+// of pvj_rope2d_apply.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool ROPE>
 __global__ __launch_bounds__(kThreads) void pack_kernel(Meta m, const T* __restrict__ src_text,
                                                         const T* __restrict__ src_img,
                                                         T* __restrict__ joint_out,
                                                         const T* __restrict__ joint_in,
                                                         T* __restrict__ dst_text,
                                                         T* __restrict__ dst_img, int rpb,
-                                                        int unpack) {
+                                                        int unpack, int inverse) {
   __shared__ int s_row[kMaxRowsPerBlock];  // stream row; text rows are stored as -1 - row
-  const int upr = m.n_heads * m.head_dim / 8;  // units per row
+  __shared__ int s_pos[ROPE ? 3 : 1][kMaxRowsPerBlock];  // row, col, frame (ROPE only)
+  const int cpr = m.head_dim / 8;          // units per head row
+  const int upr = m.n_heads * cpr;         // units per packed row
+  const int chunk = threadIdx.x % cpr;     // fixed for this thread (cpr | kThreads)
+  const int axis = ROPE ? unit_axis(chunk, m) : 0;
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
   if ((int)threadIdx.x < nrows) {
@@ -57,6 +66,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(Meta m, const T* __restr
     const SampleInfo si = m.sinfo[i];
     const int j = tok - si.start;
     s_row[threadIdx.x] = j < si.l_text ? -1 - (m.cu_text[i] + j) : m.cu_img[i] + j - si.l_text;
+    if (ROPE) {
+      const RopePos rp = token_pos3(j, si);
+      s_pos[0][threadIdx.x] = rp.r;
+      s_pos[1][threadIdx.x] = rp.c;
+      s_pos[2][threadIdx.x] = rp.f;
+    }
   }
   __syncthreads();
   const int total = nrows * upr;
@@ -64,6 +79,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(Meta m, const T* __restr
     typename Vec8<T>::type v[kBatch];
     size_t jo[kBatch], so[kBatch];
     bool txt[kBatch];
+    int pos[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int e = e0 + b * kThreads;
@@ -72,12 +88,14 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(Meta m, const T* __restr
       txt[b] = sr < 0;
       jo[b] = ((size_t)(row0 + row) * upr + u) * 8;
       so[b] = ((size_t)(sr < 0 ? -1 - sr : sr) * upr + u) * 8;
+      if (ROPE) pos[b] = e < total ? s_pos[axis][row] : 0;
       if (e < total)
         v[b] = unpack ? load8<T>(joint_in + jo[b]) : load8<T>((txt[b] ? src_text : src_img) + so[b]);
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       if (e0 + b * kThreads < total) {
+        if (ROPE) v[b] = from_f32x8<T>(rope_unit(to_f32x8(v[b]), chunk, pos[b], m, inverse != 0));
         if (unpack)
           store8<T>((txt[b] ? dst_text : dst_img) + so[b], v[b]);
         else
@@ -88,28 +106,19 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(Meta m, const T* __restr
 }
 
 hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const void* image,
-                       void* joint, bool unpack, hipStream_t stream) {
+                       void* joint, bool unpack, bool rope, bool inverse, hipStream_t stream) {
   if (m.n_tokens == 0) return hipSuccess;
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int rpb = rows_per_block(m, bf ? 2 : 4);
   const dim3 grid((m.n_tokens + rpb - 1) / rpb);
+  const int inv = inverse ? 1 : 0;
+#define PVJ_PACK(TT, RR)                                                                         do {                                                                                             if (!unpack)                                                                                     pack_kernel<TT, RR><<<grid, kThreads, 0, stream>>>(m, (const TT*)text, (const TT*)image,                                                          (TT*)joint, nullptr, nullptr,                                                                  nullptr, rpb, 0, inv);                    else                                                                                             pack_kernel<TT, RR><<<grid, kThreads, 0, stream>>>(m, nullptr, nullptr, nullptr,                                                                  (const TT*)joint, (TT*)text,                                                                   (TT*)image, rpb, 1, inv);               } while (0)
   if (bf) {
-    typedef bf16 T;
-    if (!unpack)
-      pack_kernel<T><<<grid, kThreads, 0, stream>>>(m, (const T*)text, (const T*)image, (T*)joint,
-                                                     nullptr, nullptr, nullptr, rpb, 0);
-    else
-      pack_kernel<T><<<grid, kThreads, 0, stream>>>(m, nullptr, nullptr, nullptr, (const T*)joint,
-                                                     (T*)text, (T*)image, rpb, 1);
+    if (rope) PVJ_PACK(bf16, true); else PVJ_PACK(bf16, false);
   } else {
-    typedef float T;
-    if (!unpack)
-      pack_kernel<T><<<grid, kThreads, 0, stream>>>(m, (const T*)text, (const T*)image, (T*)joint,
-                                                     nullptr, nullptr, nullptr, rpb, 0);
-    else
-      pack_kernel<T><<<grid, kThreads, 0, stream>>>(m, nullptr, nullptr, nullptr, (const T*)joint,
-                                                     (T*)text, (T*)image, rpb, 1);
+    if (rope) PVJ_PACK(float, true); else PVJ_PACK(float, false);
   }
+#undef PVJ_PACK
   return hipGetLastError();
 }
 

@@ -126,9 +126,21 @@ PVJ_API pvj_status_t pvj_pack(const pvj_plan_t* p, const void* text, const void*
   PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
   PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
   KernelTimer t(PVJ_KERNEL_PACK, static_cast<hipStream_t>(stream));
-  return launched(t.done(launch_pack(p, device_meta(p), text, image, joint, false,
+  return launched(t.done(launch_pack(p, device_meta(p), text, image, joint, false, false, false,
                                      static_cast<hipStream_t>(stream))),
                   "pack");
+}
+
+PVJ_API pvj_status_t pvj_pack_rope(const pvj_plan_t* p, const void* text, const void* image,
+                                   void* joint, int32_t inverse, void* stream) {
+  PVJ_TRY(check_plan(p));
+  PVJ_TRY(check_ptr(text, "text", p->n_text > 0));
+  PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
+  PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
+  KernelTimer t(PVJ_KERNEL_PACK, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_pack(p, device_meta(p), text, image, joint, false, true,
+                                     inverse != 0, static_cast<hipStream_t>(stream))),
+                  "pack_rope");
 }
 
 PVJ_API pvj_status_t pvj_unpack(const pvj_plan_t* p, const void* joint, void* text, void* image,
@@ -139,8 +151,21 @@ PVJ_API pvj_status_t pvj_unpack(const pvj_plan_t* p, const void* joint, void* te
   PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
   KernelTimer t(PVJ_KERNEL_UNPACK, static_cast<hipStream_t>(stream));
   return launched(t.done(launch_pack(p, device_meta(p), text, image, const_cast<void*>(joint),
-                                     true, static_cast<hipStream_t>(stream))),
+                                     true, false, false, static_cast<hipStream_t>(stream))),
                   "unpack");
+}
+
+PVJ_API pvj_status_t pvj_unpack_rope(const pvj_plan_t* p, const void* joint, void* text,
+                                     void* image, int32_t inverse, void* stream) {
+  PVJ_TRY(check_plan(p));
+  PVJ_TRY(check_ptr(joint, "joint", p->n_tokens > 0));
+  PVJ_TRY(check_ptr(text, "text", p->n_text > 0));
+  PVJ_TRY(check_ptr(image, "image", p->n_img > 0));
+  KernelTimer t(PVJ_KERNEL_UNPACK, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_pack(p, device_meta(p), text, image, const_cast<void*>(joint),
+                                     true, true, inverse != 0,
+                                     static_cast<hipStream_t>(stream))),
+                  "unpack_rope");
 }
 
 PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* p, const void* x, void* y,
@@ -202,7 +227,10 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   PVJ_TRY(check_ptr(dq, "dq", need));
   PVJ_TRY(check_ptr(dk, "dk", need));
   PVJ_TRY(check_ptr(dv, "dv", need));
-  if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~(PVJ_FLAG_ROPE_FUSED | PVJ_FLAG_ROPE_PREROTATED))
+    return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & PVJ_FLAG_ROPE_FUSED) && (flags & PVJ_FLAG_ROPE_PREROTATED))
+    return fail(PVJ_ERR_INVALID_ARG, "ROPE_FUSED and ROPE_PREROTATED exclude each other");
   if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
   const size_t need_ws = ws_total(p);
   if (need) {
@@ -215,7 +243,10 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   if (!need) return PVJ_OK;
   const Meta m = device_meta(p);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // fused: rotate Q and K in the preprocess; pre-rotated: take them as given.
+  // Either way the epilogues rotate dQ' and dK' back (dX = R^T dX').
   const bool rope = (flags & PVJ_FLAG_ROPE_FUSED) != 0;
+  const bool unrotate = rope || (flags & PVJ_FLAG_ROPE_PREROTATED) != 0;
   const float scale = resolve_scale(p, softmax_scale);
   char* ws = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws);
@@ -231,12 +262,12 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   {
     KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
     PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, 0, qq, kk, v, dout, lse, delta, dq, dk, dv,
-                                            scale, rope, s)),
+                                            scale, unrotate, s)),
                      "varlen_attn_bwd dK/dV"));
   }
   KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
   return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
-                                         rope, s)),
+                                         unrotate, s)),
                   "varlen_attn_bwd dQ");
 }
 

@@ -122,12 +122,13 @@ __device__ __forceinline__ f32x8 rope_unit(f32x8 x, int u, int pos, const Meta& 
   const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
   f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
   if (inverse) sn = -sn;
+  // explicit fma order, so every kernel that rotates rounds the same way
   f32x8 y;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float a = x[2 * q], b = x[2 * q + 1];
-    y[2 * q] = a * cs[q] - b * sn[q];
-    y[2 * q + 1] = a * sn[q] + b * cs[q];
+    y[2 * q] = __builtin_fmaf(a, cs[q], -(b * sn[q]));
+    y[2 * q + 1] = __builtin_fmaf(a, sn[q], b * cs[q]);
   }
   return y;
 }

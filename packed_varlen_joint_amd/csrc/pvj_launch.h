@@ -9,7 +9,7 @@
 namespace pvj {
 
 hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const void* image,
-                       void* joint, bool unpack, hipStream_t stream);
+                       void* joint, bool unpack, bool rope, bool inverse, hipStream_t stream);
 hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* y, bool inverse,
                          hipStream_t stream);
 hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,

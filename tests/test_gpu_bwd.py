@@ -139,3 +139,47 @@ def test_bwd_large_workloads_sampled(name, seed):
         assert_close("dq", to_np(dq[a:b, h:h + 1]), rq, "bf16")
         assert_close("dk", to_np(dk[a:b, h:h + 1]), rk, "bf16")
         assert_close("dv", to_np(dv[a:b, h:h + 1]), rv, "bf16")
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64)])
+def test_bwd_prerotated_equals_fused(dt, D):
+    # Q', K' from the standalone RoPE + PREROTATED give the bits of ROPE_FUSED
+    # (the preprocess rotates and rounds exactly as the standalone RoPE does)
+    say("bwd PREROTATED == ROPE_FUSED dt=%s D=%d" % (dt, D))
+    H = 2
+    plan = _plan(RAGGED, H, D, dt)
+    q, k, v, do = (to_dev(x, dt) for x in draw_tensors(plan.n_tokens, H, D, dt, 88, n=4))
+    o, lse = pvj.varlen_attn_fwd(plan, q, k, v, rope_fused=True)
+    g1 = pvj.varlen_attn_bwd(plan, q, k, v, o, lse, do, rope_fused=True)
+    qr, kr = pvj.rope2d_apply(plan, q), pvj.rope2d_apply(plan, k)
+    g2 = pvj.varlen_attn_bwd(plan, qr, kr, v, o, lse, do, rope_prerotated=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    with pytest.raises(pvj.PvjError):
+        pvj.varlen_attn_bwd(plan, q, k, v, o, lse, do, rope_fused=True, rope_prerotated=True)
+
+
+def test_bwd_fused_chain_step_vs_oracle():
+    # the training step composition: pack_rope(Q), pack_rope(K), pack(V) ->
+    # forward without flags -> backward PREROTATED -> unpack; against the
+    # oracle's gradients with respect to the un-rotated Q, K
+    H, D, dt = 2, 128, "bf16"
+    plan = _plan(RAGGED, H, D, dt)
+    say("fused-chain step vs oracle")
+    q, k, v, do = draw_tensors(plan.n_tokens, H, D, dt, 91, n=4)
+    streams = [oracle.unpack_joint(x, RAGGED) for x in (q, k, v, do)]
+    dev = [(to_dev(t, dt), to_dev(i, dt)) for (t, i) in streams]
+    qr = pvj.pack(plan, *dev[0], rope=True)
+    kr = pvj.pack(plan, *dev[1], rope=True)
+    vj = pvj.pack(plan, *dev[2])
+    dj = pvj.pack(plan, *dev[3])
+    o, lse = pvj.varlen_attn_fwd(plan, qr, kr, vj)
+    dq, dk, dv = pvj.varlen_attn_bwd(plan, qr, kr, vj, o, lse, dj, rope_prerotated=True)
+    torch.cuda.synchronize()
+    ro, _ = oracle.attn_fwd(q, k, v, RAGGED, rope=True)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, RAGGED, rope=True)
+    assert_close("o", to_np(o), ro, dt)
+    assert_close("dq", to_np(dq), rq, dt)
+    assert_close("dk", to_np(dk), rk, dt)
+    assert_close("dv", to_np(dv), rv, dt)

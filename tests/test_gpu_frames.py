@@ -143,6 +143,31 @@ def test_fused_rope_equals_standalone_then_plain():
     assert (l1 - l2).abs().max().item() <= 1e-5
 
 
+def test_pack_rope_frames_chain():
+    # 3-axis: pack + RoPE in one pass == pack then RoPE (bitwise); the
+    # PREROTATED backward on it == the fused-RoPE backward (bitwise)
+    samples = EDIT_RAGGED
+    dt, H, D = "bf16", 2, 128
+    plan = _plan(samples, H, D, dt)
+    say("pack_rope + PREROTATED bwd on an editing pack")
+    tq, iq, tk, ik = (to_dev(draw_tensors(n, H, D, dt, 70 + s, n=1)[0], dt)
+                      for s, n in enumerate([plan.n_text, plan.n_image] * 2))
+    qr = pvj.pack(plan, tq, iq, rope=True)
+    q = pvj.pack(plan, tq, iq)
+    k = pvj.pack(plan, tk, ik)
+    kr = pvj.pack(plan, tk, ik, rope=True)
+    assert torch.equal(qr, pvj.rope2d_apply(plan, q))
+    v, do = (to_dev(x, dt) for x in draw_tensors(plan.n_tokens, H, D, dt, 75, n=2))
+    o1, l1 = pvj.varlen_attn_fwd(plan, q, k, v, rope_fused=True)
+    o2, l2 = pvj.varlen_attn_fwd(plan, qr, kr, v)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = pvj.varlen_attn_bwd(plan, q, k, v, o1, l1, do, rope_fused=True)
+    g2 = pvj.varlen_attn_bwd(plan, qr, kr, v, o2, l2, do, rope_prerotated=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_edit_workload_sampled():
     wl = workload("edit_1024")
     say("fwd+bwd edit_1024 T=%d" % wl.n_tokens)

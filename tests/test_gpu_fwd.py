@@ -85,6 +85,47 @@ def test_pack_unpack_bit_exact(dt):
     assert np.array_equal(to_np(t2), text) and np.array_equal(to_np(i2), image)
 
 
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64)])
+def test_pack_rope_fused_chain(dt, D):
+    # pack + RoPE in one pass == pack, then the standalone RoPE (bitwise), and
+    # matches the oracle's rotation of the packed tensor; unpack_rope likewise
+    say("pack_rope / unpack_rope dt=%s D=%d" % (dt, D))
+    H = 3
+    plan = _plan(RAGGED, H, D, dt)
+    text = to_dev(draw_tensors(plan.n_text, H, D, dt, 6, n=1)[0], dt)
+    image = to_dev(draw_tensors(plan.n_image, H, D, dt, 7, n=1)[0], dt)
+    for inverse in (False, True):
+        j = Guarded(plan.n_tokens, H, D, dt)
+        pvj.pack(plan, text, image, j.t, rope=True, inverse=inverse)
+        two = pvj.rope2d_apply(plan, pvj.pack(plan, text, image), inverse=inverse)
+        torch.cuda.synchronize()
+        j.check("pack_rope")
+        assert torch.equal(j.t, two)
+        ref = oracle.rope2d(oracle.pack_joint(to_np(text), to_np(image), RAGGED),
+                            RAGGED, inverse=inverse)
+        bound = (2.0 ** -8 * np.abs(ref) + 1e-5) if dt == "bf16" else 1e-5
+        assert np.all(np.abs(to_np(j.t) - ref) <= bound)
+        t2, i2 = pvj.unpack(plan, j.t, rope=True, inverse=not inverse)
+        t3, i3 = pvj.unpack(plan, pvj.rope2d_apply(plan, j.t, inverse=not inverse))
+        assert torch.equal(t2, t3) and torch.equal(i2, i3)
+
+
+def test_fwd_on_prerotated_pack_equals_fused():
+    # the forward on pack_rope's output (no flags) gives the bits of the
+    # forward with RoPE on load: both round R x to bf16 the same way
+    H, D, dt = 2, 128, "bf16"
+    plan = _plan(RAGGED, H, D, dt)
+    say("fwd on pack_rope output == fused RoPE fwd")
+    tq, iq, tk, ik, tv, iv = (to_dev(draw_tensors(n, H, D, dt, 60 + s, n=1)[0], dt)
+                              for s, n in enumerate([plan.n_text, plan.n_image] * 3))
+    q, k, v = pvj.pack(plan, tq, iq), pvj.pack(plan, tk, ik), pvj.pack(plan, tv, iv)
+    o1, l1 = pvj.varlen_attn_fwd(plan, q, k, v, rope_fused=True)
+    qr, kr = pvj.pack(plan, tq, iq, rope=True), pvj.pack(plan, tk, ik, rope=True)
+    o2, l2 = pvj.varlen_attn_fwd(plan, qr, kr, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_pack_large_bit_exact():
     wl = workload("train_64k", 1)
     say("pack/unpack train_64k seed 1, T=%d" % wl.n_tokens)
