@@ -98,18 +98,23 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   float lr = 0.f, dr = 0.f;
   const float* lse_h = LSE + (size_t)it.head * m.n_tokens + si.start;
   const float* del_h = DELTA + (size_t)it.head * m.n_tokens + si.start;
+  // direct copies: Q and dO tiles share one layout; rows past the sample end
+  // arrive as zeros (outside the buffer resources)
+  typedef DmaTile<D, BQ> DT;
+  const DT dma(RS);
+  const typename DT::Src rq = DT::src(Q + base, RS, L), rg = DT::src(dO + base, RS, L);
   auto load_q = [&](int q0, int b) {
     // LSE and Delta first: the wait for them (in-order counter) then leaves the
     // tile copies in flight
     if (tid < BQ) {
       const int qq = q0 + tid;
-      // queries past the end: LSE = +inf makes P = 0 (their rows are re-read data)
+      // queries past the end: LSE = +inf makes P = 0 (their rows read as zeros)
       lr = qq < L ? lse_h[qq] : INFINITY;
       dr = qq < L ? del_h[qq] : 0.f;
     }
     if constexpr (DMA) {
-      dma_tile<D, BQ>(b ? q_b1 : q_b0, Q + base, RS, q0, L);
-      dma_tile<D, BQ>(b ? g_b1 : g_b0, dO + base, RS, q0, L);
+      dma.copy(b ? q_b1 : q_b0, rq, RS, q0);
+      dma.copy(b ? g_b1 : g_b0, rg, RS, q0);
     } else {
 #pragma unroll
       for (int i = 0; i < KPQ; ++i) {
@@ -314,10 +319,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int K_ROW_STEP = kBwdThreads / UPR;
   constexpr bool DMA = sizeof(T) == 2;
   V8 kreg[DMA ? 1 : NK], vreg[DMA ? 1 : NK];
+  // direct copies (K and V tiles share one layout; rows past the end are zeros)
+  typedef DmaTile<D, kDqBN> DT;
+  const DT dma(RS);
+  const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
   auto load_kv = [&](int kv0, int b) {
     if constexpr (DMA) {
-      dma_tile<D, kDqBN>(ks_of(b), K + base, RS, kv0, L);
-      dma_tile<D, kDqBN>(vs_of(b), V + base, RS, kv0, L);
+      dma.copy(ks_of(b), rk, RS, kv0);
+      dma.copy(vs_of(b), rv, RS, kv0);
     } else {
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-        // the last tile's rows past the sample end hold re-read data: zero weight
+        // the last tile's rows past the sample end read as zeros: zero weight
         if (tail && kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7) >= L) p = 0.f;
         sfr[kb][r >> 3][r & 7] = (T)(p * (dp[r] - delta));
       }

@@ -32,6 +32,8 @@
 // rescaled) when a tile raises some row max by more than 8 (a factor 256).
 // Keys at or past the sample end are masked to -inf.
 
+#include <type_traits>
+
 #include "pvj_device.h"
 #include "pvj_launch.h"
 
@@ -111,10 +113,18 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   // RoPE: this thread always handles the same unit of the head dim, so its
   // axis is fixed; only the key position varies
   const int k_axis = unit_axis(k_unit, m);
+  // direct copies: per-thread offsets (K and V tiles share one layout) and
+  // one buffer resource per operand spanning this head's L rows
+  const DmaTile<D, kFwdBN> dma(RS);
+  typedef DmaTile<D, kFwdBN> DT;
+  const typename DT::Src rk = DT::src(Kh, RS, L), rv = DT::src(Vh, RS, L);
 
-  auto load_tile = [&](int kv0, int b) {
+  // the KV loop is unrolled by two so that every LDS address is a fixed
+  // per-lane offset plus a compile-time buffer offset
+  auto load_tile = [&](int kv0, auto bc) {
+    constexpr int B = decltype(bc)::value;
     if constexpr (K_DMA) {
-      dma_tile<D, kFwdBN>(b ? k_b1 : k_b0, Kh, RS, kv0, L);
+      dma.copy(B ? k_b1 : k_b0, rk, RS, kv0);
     } else {
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     if constexpr (DMA) {
-      dma_tile<D, kFwdBN>(b ? v_b1 : v_b0, Vh, RS, kv0, L);
+      dma.copy(B ? v_b1 : v_b0, rv, RS, kv0);
     } else {
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
@@ -135,9 +145,10 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  auto store_tile = [&](int b, int kv0) {
+  auto store_tile = [&](int kv0, auto bc) {
+    constexpr int B = decltype(bc)::value;
     if constexpr (!K_DMA) {
-      T* kb = b ? k_b1 : k_b0;
+      T* kb = B ? k_b1 : k_b0;
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
         V8 v = kreg[i];
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     if constexpr (!DMA) {
-      T* vb = b ? v_b1 : v_b0;
+      T* vb = B ? v_b1 : v_b0;
 #pragma unroll
       for (int i = 0; i < NK; ++i)
         store8<T>(vb + toff<D>(bsigma(k_row0 + i * K_ROW_STEP), k_unit * 8), vreg[i]);
@@ -160,8 +171,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   auto sig = [](int k) { return bsigma(k); };
 
   const int nkv = (L + kFwdBN - 1) / kFwdBN;
-  load_tile(0, 0);
-  store_tile(0, 0);
+  load_tile(0, std::integral_constant<int, 0>{});
+  store_tile(0, std::integral_constant<int, 0>{});
   __syncthreads();
 
   f32x16 oacc[DB];
@@ -169,12 +180,37 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int j = 0; j < nkv; ++j) {
-    const int b = j & 1;
+  // Per-lane LDS addresses of the operand reads, fixed for the whole loop
+  // (bf16): K row l32 at unit 2kk+hi, and the V fragment bases of output
+  // block db and half t.  The 32-key block kb, the 16-key half st and the
+  // buffer only add compile-time offsets (row bits 4-5 do not enter the
+  // swizzle, and sigma leaves them in place).  The empty asm pins each value
+  // in a register so it is not recomputed every tile.
+  uint32_t ka[KS], va[DB][2];
+  if constexpr (sizeof(T) == 2) {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      ka[kk] = (uint32_t)(toff<D>(l32, (2 * kk + hi) * 8) * sizeof(T));
+      asm volatile("" : "+v"(ka[kk]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        va[db][t] = (uint32_t)(toff<D>(bsigma(8 * (g >> 1) + 4 * t + (sl >> 2)),
+                                       db * 32 + 16 * (g & 1) + 4 * (sl & 3)) * sizeof(T));
+        asm volatile("" : "+v"(va[db][t]));
+      }
+  }
+
+  auto step = [&](int j, auto bc, auto mc) {
+    constexpr int B = decltype(bc)::value;
+    constexpr bool MASK = decltype(mc)::value;
     const int kv0 = j * kFwdBN;
-    if (j + 1 < nkv) load_tile(kv0 + kFwdBN, b ^ 1);
-    const T* ks = b ? k_b1 : k_b0;
-    const T* vs = b ? v_b1 : v_b0;
+    if (j + 1 < nkv) load_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
+    const T* ks = B ? k_b1 : k_b0;
+    const T* vs = B ? v_b1 : v_b0;
 
     // S^T = K Q^T for the two 32-key blocks
     f32x16 s[2];
@@ -183,11 +219,19 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       s[kb] = f32x16{};
       const int rho = kb * 32 + l32;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        mma16(s[kb], load8<T>(ks + toff<D>(rho, (2 * kk + hi) * 8)), qf[kk]);
+      for (int kk = 0; kk < KS; ++kk) {
+        V8 kf;
+        if constexpr (sizeof(T) == 2)
+          kf = *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(ks) + ka[kk] +
+                                            kb * 32 * D * sizeof(T));
+        else
+          kf = load8<T>(ks + toff<D>(rho, (2 * kk + hi) * 8));
+        mma16(s[kb], kf, qf[kk]);
+      }
     }
-    // mask keys past the sample end (last tile only; their rows hold re-read data)
-    if (kv0 + kFwdBN > L) {
+    // mask keys past the sample end (the last, partial tile only; their rows
+    // were read as zeros)
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -196,17 +240,25 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
           if (key >= L) s[kb][r] = -INFINITY;
         }
     }
-    // online softmax (base 2)
-    float mx = -INFINITY;
+    // online softmax (base 2); max and sum as short independent chains
+    float mx4[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int c = 0; c < 4; ++c)
+      mx4[c] = fmaxf(fmaxf(s[c >> 1][8 * (c & 1)], s[c >> 1][8 * (c & 1) + 1]),
+                     fmaxf(s[c >> 1][8 * (c & 1) + 2], s[c >> 1][8 * (c & 1) + 3]));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 4; r < 8; ++r) mx4[c] = fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
     mx = max_pair32(mx) * scale_log2;
     // Rescale only when some query's max grew by more than 2^8: otherwise keep
     // the stale reference max (p <= 256, far from overflow).  O / l is exact
-    // for any common reference, so this only skips work.
+    // for any common reference, so this only skips work.  (The empty asm keeps
+    // this a real branch: folded into selects it would cost the multiplies on
+    // every tile.)
     if (__any(mx > m_run + 8.f)) {
+      asm volatile("" ::: "memory");
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
@@ -214,17 +266,17 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
-    float ls = 0.f;
+    float ls4[4] = {0.f, 0.f, 0.f, 0.f};
     V8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
-        ls += p;
+        ls4[r & 3] += p;
         pf[kb][r >> 3][r & 7] = (T)p;
       }
-    l_run += ls;
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
 
     // O^T += V^T P^T (A = V^T by transposing reads of the row-major V tile)
 #pragma unroll
@@ -232,10 +284,46 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          mma16(oacc[db], frag_t<D>(vs, kb * 32 + 16 * st, db * 32, sig), pf[kb][st]);
-    if (j + 1 < nkv) store_tile(b ^ 1, kv0 + kFwdBN);
+        for (int st = 0; st < 2; ++st) {
+          V8 vf;
+          if constexpr (sizeof(T) == 2) {
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const uint32_t o = (uint32_t)((kb * 32 + 16 * st) * D * sizeof(T));
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(reinterpret_cast<const char*>(vs) + va[db][t] + o));
+              const bf16x4 h = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vf[4 * t + e] = h[e];
+            }
+          } else {
+            vf = frag_t<D>(vs, kb * 32 + 16 * st, db * 32, sig);
+          }
+          mma16(oacc[db], vf, pf[kb][st]);
+        }
+    if (j + 1 < nkv) store_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
     __syncthreads();
+  };
+  // full tiles in pairs (buffers 0, 1), then a leftover full tile, then the
+  // partial tile with the key mask
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<bool, false> NoMask;
+  typedef std::integral_constant<bool, true> Mask;
+  const int nfull = L / kFwdBN;
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    step(j, B0{}, NoMask{});
+    step(j + 1, B1{}, NoMask{});
+  }
+  if (j < nfull) {
+    step(j, B0{}, NoMask{});
+    ++j;
+  }
+  if (j < nkv) {
+    if (j & 1) step(j, B1{}, Mask{});
+    else step(j, B0{}, Mask{});
   }
 
   // ---- epilogue: O = O^T / l, LSE ----

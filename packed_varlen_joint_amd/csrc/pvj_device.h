@@ -148,16 +148,28 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // a following product over those rows.  (sigma is its own inverse.)
 __device__ __forceinline__ int bsigma(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-// XOR swizzle of the 8-element (16-byte) units of an LDS tile row.  It is a
-// permutation of row & 7, so 8 consecutive rows read at one unit hit 8
-// different units; and the 4 consecutive rows x 2 adjacent units that a
-// 16-lane group touches in one transposing read also land on 8 different
-// units (the low bit of the XOR comes from row bit 2, the rest from bits 0-1).
-__device__ __forceinline__ int tsw(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR swizzle of the 8-element (16-byte) units of an LDS tile row, chosen
+// from the measured bank behaviour of gfx950 LDS (64 banks of 4 bytes):
+//  * a ds_read_b128 operand read (lane l: row l%32, one unit) is served 16
+//    lanes at a time, so 16 consecutive rows must land on 16 different
+//    16-byte slots of a 256-byte bank window;
+//  * a transposing ds_read_b64_tr_b16 (16 lanes: 4 consecutive rows x one
+//    pair of adjacent units) needs those 4 rows on different unit pairs.
+// D = 128 (256-byte rows): unit ^= (row&3)<<2 | (row>>2)&3, a permutation of
+// 0..15 over any 16 aligned rows whose bits 1..2 differ within 4 rows.
+// D = 64 (128-byte rows, two rows per bank window): rows of one parity need
+// 8 different units, and rows 4i, 4i+2 different pairs:
+// unit ^= ((row>>1)&1)<<2 | (row>>2)&3.
+template <int D>
+__device__ __forceinline__ int tsw(int row) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 // element offset of (row, col) in a row-major LDS tile of D columns
 template <int D>
 __device__ __forceinline__ int toff(int row, int col) {
-  return row * D + (((col >> 3) ^ tsw(row)) << 3) + (col & 7);
+  return row * D + (((col >> 3) ^ tsw<D>(row)) << 3) + (col & 7);
 }
 
 // The 8-slot 32x32x16 operand fragment F[j] = M[kb8 + j][n] of a row-major
@@ -194,31 +206,70 @@ __device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, Ro
   return f;
 }
 
-// Direct global -> LDS copy (global_load_lds_dwordx4, no VGPR round trip) of a
-// [ROWS][D] bf16 tile: rows row0 .. row0+ROWS-1 of one (sample, head), stored
-// in LDS row sigma(r) with the tsw swizzle.  Each instruction writes one
-// wave's 64 consecutive 16-byte LDS slots in lane order, so every lane loads
-// the global unit that belongs in its slot.  Rows at or past the sample end
-// re-read row L-1 (finite data; the kernels give them zero weight).  The
-// copies complete asynchronously: wait_dma() before the barrier that
-// publishes the tile.
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds, no VGPR round trip)
+// of a [ROWS][D] bf16 tile: rows row0 .. row0+ROWS-1 of one (sample, head),
+// stored in LDS row sigma(r) with the tsw swizzle.  Each instruction writes
+// one wave's 64 consecutive 16-byte LDS slots in lane order, so every lane
+// loads the global unit that belongs in its slot.  The copies complete
+// asynchronously: wait_dma() before the barrier that publishes the tile.
+//
+// The source is addressed through a buffer resource that spans exactly the
+// head's L rows (num_records = ((L-1) RS + D) * 2 bytes): each thread's byte
+// offset inside a tile is fixed (computed once), the tile's first row is a
+// uniform SGPR offset, and rows at or past the sample end fall outside the
+// resource, so the hardware returns zeros for them (no clamp, no data from
+// another sample).  The planner keeps a sample's span below 2 GiB, so the
+// 32-bit offsets never wrap.
 template <int D, int ROWS>
-__device__ __forceinline__ void dma_tile(bf16* tile, const bf16* g, size_t RS, int row0, int L) {
-  constexpr int UPR = D / 8;
-  constexpr int PER = ROWS * UPR / kTileThreads;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+struct DmaTile {
+  static constexpr int UPR = D / 8;
+  static constexpr int PER = ROWS * UPR / kTileThreads;
+  uint32_t off[PER];
+  int wave;
+  __device__ __forceinline__ explicit DmaTile(size_t RS) {
+    wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int blk = i * (kTileThreads / 64) + wave;
-    const int slot = blk * 64 + lane;
-    const int rho = slot / UPR;
-    const int u = (slot % UPR) ^ tsw(rho);
-    int r = row0 + bsigma(rho);
-    r = r < L ? r : L - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)r * RS + u * 8),
-                                     (__attribute__((address_space(3))) void*)(tile + blk * 512),
-                                     16, 0, 0);
+    for (int i = 0; i < PER; ++i) {
+      const int slot = (i * (kTileThreads / 64) + wave) * 64 + lane;
+      const int rho = slot / UPR;
+      const int u = (slot % UPR) ^ tsw<D>(rho);
+      off[i] = (uint32_t)(((size_t)bsigma(rho) * RS + (size_t)u * 8) * sizeof(bf16));
+    }
   }
+  // source: the head whose row 0 is at g, rows 0 .. L-1 (the buffer resource
+  // is built where it is used: only device code handles the resource type)
+  struct Src {
+    const bf16* g;
+    int bytes;
+  };
+  __device__ __forceinline__ static Src src(const void* g, size_t RS, int L) {
+    return Src{static_cast<const bf16*>(g),
+               L > 0 ? (int)(((size_t)(L - 1) * RS + D) * sizeof(bf16)) : 0};
+  }
+  // copy rows row0 .. row0 + ROWS - 1 (dma_copy below)
+  __device__ __forceinline__ void copy(void* tile, Src sr, size_t RS, int row0) const;
+};
+
+// The resource-building copy is a free function template: kept out of the
+// kernels' own bodies, the host-side compile of the kernel templates does not
+// see the resource type.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_copy(const uint32_t* off, int wave, void* tile, const bf16* g,
+                                         int bytes, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g), (short)0, bytes, 0x00020000);
+  bf16* t = static_cast<bf16*>(tile);
+#pragma unroll
+  for (int i = 0; i < DmaTile<D, ROWS>::PER; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(t + (i * (kTileThreads / 64) + wave) * 512),
+        16, off[i], soff, 0, 0);
+}
+template <int D, int ROWS>
+__device__ __forceinline__ void DmaTile<D, ROWS>::copy(void* tile, Src sr, size_t RS,
+                                                      int row0) const {
+  dma_copy<D, ROWS>(off, wave, tile, sr.g, sr.bytes, (uint32_t)((size_t)row0 * RS * sizeof(bf16)));
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

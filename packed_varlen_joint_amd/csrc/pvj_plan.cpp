@@ -167,6 +167,10 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
     // the kernels index rows with int32 and multiply a row by H*D in int64
     if (hw > INT32_MAX || L > INT32_MAX)
       return fail(PVJ_ERR_OVERFLOW, "sample %d length overflows int32", i);
+    // the kernels address one (sample, head) with 32-bit byte offsets
+    const int64_t elt = desc->dtype == PVJ_BF16 ? 2 : 4;
+    if (L * desc->n_heads * desc->head_dim * elt >= (int64_t(1) << 31))
+      return fail(PVJ_ERR_UNSUPPORTED, "sample %d spans 2 GiB or more of a token tensor", i);
     T += L;
     nt += t;
     ni += img;

@@ -200,7 +200,10 @@ def test_error_codes(lib):
     assert _create(lib, [(32767, 2, 0)]) == 0
     assert _create(lib, [(32768, 2, 0)]) == UNSUP                  # latent side limit
     assert _create(lib, [(2, 40000, 0)]) == UNSUP
-    assert _create(lib, [(30000, 30000, 0)] * 3) == OVERFLOW       # T > int32
+    assert _create(lib, [(4000, 4000, 0)] * 135, H=1) == OVERFLOW  # T > int32
+    # one sample's span of a token tensor stays below 2 GiB (32-bit offsets)
+    assert _create(lib, [(31, 33, 0)], H=4096, D=128, dtype=1) == 0    # 1023 rows x 2 MiB
+    assert _create(lib, [(32, 32, 0)], H=4096, D=128, dtype=1) == UNSUP
     h = ctypes.c_void_p()
     assert lib.pvj_plan_create(None, 1, None, ctypes.byref(h)) == INVALID
     assert _create_frames(lib, [(2, 3, 4, 2)]) == 0
