@@ -26,6 +26,8 @@
 // With RoPE, the preprocess kernel writes Q' = R Q and K' = R K once into the
 // workspace, so both kernels read pre-rotated operands.
 
+#include <type_traits>
+
 #include "pvj_device.h"
 #include "pvj_launch.h"
 
@@ -150,14 +152,61 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
     dv_acc[db] = f32x16{};
   }
 
-  // S and dP of one 32-query block (A = Q', dO rows from LDS; B = K', V registers)
-  auto sdp = [&](const T* qs, const T* gs, int qb, f32x16& s, f32x16& dp) {
-    const int rho = qb * 32 + l32;
+  // Per-lane LDS addresses, fixed for the whole loop (bf16): row l32 at unit
+  // 2ks+hi of the Q' and dO tiles (same layout), and the transposed fragment
+  // bases of output block db and half t; the 32-query block, the 16-query
+  // half and the buffer add compile-time offsets.  The empty asm keeps them
+  // in registers.
+  uint32_t qa[KS], fa[DB][2];
+  if constexpr (DMA) {
+    const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int off = toff<D>(rho, (2 * ks + hi) * 8);
-      mma16(s, load8<T>(qs + off), kf[ks]);
-      mma16(dp, load8<T>(gs + off), vf[ks]);
+      qa[ks] = (uint32_t)(toff<D>(l32, (2 * ks + hi) * 8) * sizeof(T));
+      asm volatile("" : "+v"(qa[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        fa[db][t] = (uint32_t)(toff<D>(bsigma(8 * (g >> 1) + 4 * t + (sl >> 2)),
+                                       db * 32 + 16 * (g & 1) + 4 * (sl & 3)) * sizeof(T));
+        asm volatile("" : "+v"(fa[db][t]));
+      }
+  }
+  // A-operand row read (row qb*32 + l32, unit 2ks+hi) and transposed fragment
+  // (rows kbase.., columns db*32..) of a Q' or dO tile
+  auto rowfrag = [&](const T* t, int qb, int ks) -> V8 {
+    if constexpr (DMA)
+      return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(t) + qa[ks] +
+                                          qb * 32 * D * sizeof(T));
+    else
+      return load8<T>(t + toff<D>(qb * 32 + l32, (2 * ks + hi) * 8));
+  };
+  auto colfrag = [&](const T* t, int kbase, int db) -> V8 {
+    if constexpr (DMA) {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      V8 f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(reinterpret_cast<const char*>(t) + fa[db][tt] + kbase * D * sizeof(T)));
+        const bf16x4 h = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[4 * tt + e] = h[e];
+      }
+      return f;
+    } else {
+      return frag_t<D>(t, kbase, db * 32, sig);
+    }
+  };
+
+  // S and dP of one 32-query block (A = Q', dO rows from LDS; B = K', V registers)
+  auto sdp = [&](const T* qs, const T* gs, int qb, f32x16& s, f32x16& dp) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      mma16(s, rowfrag(qs, qb, ks), kf[ks]);
+      mma16(dp, rowfrag(gs, qb, ks), vf[ks]);
     }
     // keep six operand reads in flight ahead of the products
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
@@ -184,9 +233,9 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int kbase = qb * 32 + 16 * st;
-        mma16(dv_acc[db], pf[st], frag_t<D>(gs, kbase, db * 32, sig));
+        mma16(dv_acc[db], pf[st], colfrag(gs, kbase, db));
         fill(4 * db + 2 * st);
-        mma16(dk_acc[db], sf[st], frag_t<D>(qs, kbase, db * 32, sig));
+        mma16(dk_acc[db], sf[st], colfrag(qs, kbase, db));
         fill(4 * db + 2 * st + 1);
       }
   };
@@ -195,28 +244,25 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   load_q(0, 0);
   store_q(0);
   __syncthreads();
-  for (int qt = 0; qt < nq; ++qt) {
-    const int b = qt & 1;
-    if (qt + 1 < nq) load_q((qt + 1) * BQ, b ^ 1);
-    const T* qs = b ? q_b1 : q_b0;
-    const T* gs = b ? g_b1 : g_b0;
-    const float* lb = b ? l_b1 : l_b0;
+  // the query-tile loop is unrolled by two so the buffer is a compile-time choice
+  auto step = [&](int qt, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    if (qt + 1 < nq) load_q((qt + 1) * BQ, B ^ 1);
+    const T* qs = B ? q_b1 : q_b0;
+    const T* gs = B ? g_b1 : g_b0;
+    const float* lb = B ? l_b1 : l_b0;
     if constexpr (QB == 2) {
       // software pipeline over the two query blocks: the softmax VALU work of
       // one block sits between the matrix products of the other
       f32x16 s0 = {}, dp0 = {}, s1 = {}, dp1 = {};
       V8 pf0[2], sf0[2], pf1[2], sf1[2];
       sdp(qs, gs, 0, s0, dp0);
-      {
-        const int rho = 32 + l32;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = toff<D>(rho, (2 * ks + hi) * 8);
-          mma16(s1, load8<T>(qs + off), kf[ks]);
-          mma16(dp1, load8<T>(gs + off), vf[ks]);
+      for (int ks = 0; ks < KS; ++ks) {
+        mma16(s1, rowfrag(qs, 1, ks), kf[ks]);
+        mma16(dp1, rowfrag(gs, 1, ks), vf[ks]);
 #pragma unroll
-          for (int e = 0; e < 16 / KS; ++e) elem(lb, 0, (16 / KS) * ks + e, s0, dp0, pf0, sf0);
-        }
+        for (int e = 0; e < 16 / KS; ++e) elem(lb, 0, (16 / KS) * ks + e, s0, dp0, pf0, sf0);
       }
       dvdk(qs, gs, 0, pf0, sf0, [&](int slot) {
         constexpr int PER = 16 / (4 * DB);  // elements of block 1 per product slot
@@ -232,9 +278,15 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) elem(lb, 0, r, s0, dp0, pf0, sf0);
       dvdk(qs, gs, 0, pf0, sf0, [](int) {});
     }
-    if (qt + 1 < nq) store_q(b ^ 1);
+    if (qt + 1 < nq) store_q(B ^ 1);
     __syncthreads();
+  };
+  int qt = 0;
+  for (; qt + 1 < nq; qt += 2) {
+    step(qt, std::integral_constant<int, 0>{});
+    step(qt + 1, std::integral_constant<int, 1>{});
   }
+  if (qt < nq) step(qt, std::integral_constant<int, 0>{});
 
   // ---- epilogue: dK = R^T (s dK'), dV; staged through LDS for row-major stores ----
 #pragma unroll
@@ -355,17 +407,39 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
+  // Per-lane LDS addresses, fixed for the whole loop (bf16): row l32 at unit
+  // 2kk+hi of the K and V tiles (same layout), and the K^T fragment bases of
+  // output block db and half t; the 32-key block, the 16-key half and the
+  // buffer add compile-time offsets.  The empty asm keeps them in registers.
+  uint32_t ka[KS], va[DB][2];
+  if constexpr (DMA) {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      ka[kk] = (uint32_t)(toff<D>(l32, (2 * kk + hi) * 8) * sizeof(T));
+      asm volatile("" : "+v"(ka[kk]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        va[db][t] = (uint32_t)(toff<D>(bsigma(8 * (g >> 1) + 4 * t + (sl >> 2)),
+                                       db * 32 + 16 * (g & 1) + 4 * (sl & 3)) * sizeof(T));
+        asm volatile("" : "+v"(va[db][t]));
+      }
+  }
+
   const int nkv = (L + kDqBN - 1) / kDqBN;
   load_kv(0, 0);
   store_kv(0);
   __syncthreads();
-  for (int j = 0; j < nkv; ++j) {
-    const int b = j & 1;
+  auto step = [&](int j, auto bc, auto mc) {
+    constexpr int B = decltype(bc)::value;
+    constexpr bool MASK = decltype(mc)::value;
     const int kv0 = j * kDqBN;
-    if (j + 1 < nkv) load_kv(kv0 + kDqBN, b ^ 1);
-    const bool tail = kv0 + kDqBN > L;
-    const T* ks = ks_of(b);
-    const T* vs = vs_of(b);
+    if (j + 1 < nkv) load_kv(kv0 + kDqBN, B ^ 1);
+    const T* ks = B ? k_b1 : k_b0;
+    const T* vs = B ? v_b1 : v_b0;
     V8 sfr[2][2];  // dS^T fragments [32-key block][16-key step]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -373,15 +447,25 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
       const int rho = kb * 32 + l32;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const int off = toff<D>(rho, (2 * kk + hi) * 8);
-        mma16(s, load8<T>(ks + off), qf[kk]);
-        mma16(dp, load8<T>(vs + off), gf[kk]);
+        V8 kf, vf;
+        if constexpr (DMA) {
+          const uint32_t o = ka[kk] + kb * 32 * D * sizeof(T);
+          kf = *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(ks) + o);
+          vf = *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(vs) + o);
+        } else {
+          const int off = toff<D>(rho, (2 * kk + hi) * 8);
+          kf = load8<T>(ks + off);
+          vf = load8<T>(vs + off);
+        }
+        mma16(s, kf, qf[kk]);
+        mma16(dp, vf, gf[kk]);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
         // the last tile's rows past the sample end read as zeros: zero weight
-        if (tail && kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7) >= L) p = 0.f;
+        if constexpr (MASK)
+          if (kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7) >= L) p = 0.f;
         sfr[kb][r >> 3][r & 7] = (T)(p * (dp[r] - delta));
       }
     }
@@ -391,10 +475,46 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          mma16(acc[db], frag_t<D>(ks, kb * 32 + 16 * st, db * 32, sig), sfr[kb][st]);
-    if (j + 1 < nkv) store_kv(b ^ 1);
+        for (int st = 0; st < 2; ++st) {
+          V8 kt;
+          if constexpr (DMA) {
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const uint32_t o = (uint32_t)((kb * 32 + 16 * st) * D * sizeof(T));
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(reinterpret_cast<const char*>(ks) + va[db][t] + o));
+              const bf16x4 h = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) kt[4 * t + e] = h[e];
+            }
+          } else {
+            kt = frag_t<D>(ks, kb * 32 + 16 * st, db * 32, sig);
+          }
+          mma16(acc[db], kt, sfr[kb][st]);
+        }
+    if (j + 1 < nkv) store_kv(B ^ 1);
     __syncthreads();
+  };
+  // full tiles in pairs (buffers 0, 1), a leftover full tile, then the
+  // partial tile with the key mask
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<bool, false> NoMask;
+  typedef std::integral_constant<bool, true> Mask;
+  const int nfull = L / kDqBN;
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    step(j, B0{}, NoMask{});
+    step(j + 1, B1{}, NoMask{});
+  }
+  if (j < nfull) {
+    step(j, B0{}, NoMask{});
+    ++j;
+  }
+  if (j < nkv) {
+    if (j & 1) step(j, B1{}, Mask{});
+    else step(j, B0{}, Mask{});
   }
 
   // ---- epilogue: dQ = R^T (s dQ'); lane holds query qi, d = 32db + 8g + 4hi + e ----
