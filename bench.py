@@ -110,6 +110,68 @@ class PackStep:
         self.plan = plan
 
 
+def chain_bench(wl, reps):
+    """HBM-bound chains around the attention on both streams of the pack, at the
+    backbone width H*D: adaptive layer norm + modulation and gate + residual,
+    forward and backward.  Timed with events on torch's current stream (the
+    stream the library launches on); bytes are algorithmic (each tensor read
+    or written once)."""
+    import torch
+    import packed_varlen_joint_amd as pvj
+    plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+    C = wl.n_heads * wl.head_dim
+    dt = plan.torch_dtype
+    elt = 2 if wl.dtype == "bf16" else 4
+    B = len(wl.samples)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    out = {}
+    streams = [("text", plan.n_text), ("image", plan.n_image)]
+    data = {}
+    for which, n in streams:
+        mk = lambda r: torch.randn(r, C, device="cuda", generator=g).to(dt)
+        data[which] = dict(x=mk(n), y=mk(n), d=mk(n), sh=mk(B), sc=mk(B), gt=mk(B),
+                           o=torch.empty(n, C, device="cuda", dtype=dt),
+                           dx=torch.empty(n, C, device="cuda", dtype=dt),
+                           ws_a=torch.empty(max(256, pvj.chain_workspace_bytes(
+                               plan, pvj.CHAIN_ADALN, which, C)), dtype=torch.uint8,
+                               device="cuda"),
+                           ws_g=torch.empty(max(256, pvj.chain_workspace_bytes(
+                               plan, pvj.CHAIN_GATE, which, C)), dtype=torch.uint8,
+                               device="cuda"))
+    ops = {
+        "adaln_fwd": (2, lambda w, t: pvj.adaln_modulate(plan, w, t["x"], t["sh"], t["sc"],
+                                                         y=t["o"])),
+        "gate_residual_fwd": (3, lambda w, t: pvj.gate_residual(plan, w, t["x"], t["y"], t["gt"],
+                                                                out=t["o"])),
+        "adaln_bwd": (3, lambda w, t: pvj.adaln_modulate_bwd(plan, w, t["x"], t["sc"], t["d"],
+                                                             dx=t["dx"], workspace=t["ws_a"])),
+        "gate_residual_bwd": (3, lambda w, t: pvj.gate_residual_bwd(plan, w, t["y"], t["gt"],
+                                                                    t["d"], dy=t["dx"],
+                                                                    workspace=t["ws_g"])),
+    }
+    rows = plan.n_text + plan.n_image
+    for name, (ntens, fn) in ops.items():
+        for _ in range(2):
+            for w, _n in streams:
+                fn(w, data[w])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for w, _n in streams:
+                fn(w, data[w])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = ntens * rows * C * elt
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes,
+                     "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["_note"] = ("both streams per call, hidden %d, algorithmic bytes = tensors read + "
+                    "written once (%d rows)" % (C, rows))
+    return out
+
+
 def cpu_baseline(wl, seconds):
     """The oracle (fp64 NumPy, as it stands) on a bounded sample of the workload:
     forward + backward of (sample, head) slices, smallest samples first, until
@@ -159,6 +221,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chains", action="store_true",
+                    help="skip the memory-bound chain measurements (reported beside the step)")
     ap.add_argument("--rope", choices=("pack", "load"), default="pack",
                     help="RoPE fused into the Q/K pack (default) or applied on load inside "
                          "the attention kernels")
@@ -268,6 +332,8 @@ def main():
         out["bwd_tflops"] = round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)
         out["fwd_bwd_kernel_tflops"] = round(
             (f_fwd + f_bwd) / ((kern["attn_fwd"]["avg_ms"] + t_bwd) * 1e-3) / 1e12, 2)
+    if not args.no_chains:
+        out["chains"] = chain_bench(wl, 10)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:

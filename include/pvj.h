@@ -221,6 +221,55 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* plan, const void* q, 
                                          void* workspace, size_t ws_bytes, float softmax_scale,
                                          uint32_t flags, void* stream);
 
+/* ---- memory-bound chains around the attention ---------------------------------
+ * Review page, "Kernel fusion": the backbone's memory-bound chains
+ * (normalization, adaptive modulation, gating, residual addition) are fused so
+ * each tensor is read and written once; "Native-Resolution MMDiT": the text
+ * and image streams keep modality-specific parameters.  Reading taken (the
+ * pages name the operations, not the formulas): adaptive LayerNorm of the
+ * MMDiT block design, LayerNorm without affine parameters, population
+ * variance.
+ *
+ * Every call works on one stream of the plan (which = PVJ_STREAM_TEXT: the
+ * n_text rows in sample order; PVJ_STREAM_IMAGE: the n_image rows) with
+ * `hidden` columns (a multiple of 8 in [8, 8192]).  Row tensors are
+ * [rows, hidden] and per-sample vectors [n_samples, hidden], in the plan
+ * dtype, row-major, 16-byte aligned; a row's sample is the one whose slice of
+ * the stream holds it.  Parameter gradients are fp32 [n_samples, hidden]
+ * (zero for samples without rows in the stream).  Computation is fp32.
+ * Deterministic: the per-sample sums are reduced in a fixed order.
+ */
+enum { PVJ_STREAM_TEXT = 0, PVJ_STREAM_IMAGE = 1 };
+enum { PVJ_CHAIN_ADALN = 0, PVJ_CHAIN_GATE = 1 };
+
+/* y = LN(x) * (1 + scale_i) + shift_i, LN over hidden with `eps` (1e-6).
+ * y may equal x (in place). */
+PVJ_API pvj_status_t pvj_adaln_modulate(const pvj_plan_t* plan, int32_t which, int32_t hidden,
+                                        const void* x, const void* shift, const void* scale,
+                                        void* y, float eps, void* stream);
+/* out = x + gate_i * y.  out may equal x or y. */
+PVJ_API pvj_status_t pvj_gate_residual(const pvj_plan_t* plan, int32_t which, int32_t hidden,
+                                       const void* x, const void* y, const void* gate, void* out,
+                                       void* stream);
+/* Workspace of a chain backward (op = PVJ_CHAIN_ADALN or PVJ_CHAIN_GATE):
+ * per-sample partial sums, and for the layer norm the row statistics. */
+PVJ_API pvj_status_t pvj_chain_bwd_workspace(const pvj_plan_t* plan, int32_t op, int32_t which,
+                                             int32_t hidden, size_t* bytes);
+/* Gradients of sum(y * dy): dx (plan dtype, rows x hidden), dshift_i = sum of
+ * dy over the sample's rows, dscale_i = sum of dy * xhat; x, scale and eps
+ * are those of the forward.  dx must not overlap x or dy. */
+PVJ_API pvj_status_t pvj_adaln_modulate_bwd(const pvj_plan_t* plan, int32_t which, int32_t hidden,
+                                            const void* x, const void* scale, const void* dy,
+                                            void* dx, float* dshift, float* dscale, float eps,
+                                            void* workspace, size_t ws_bytes, void* stream);
+/* Gradients of sum(out * dout): dy = gate_i * dout, dgate_i = sum over the
+ * sample's rows of dout * y; the gradient of x is dout itself (no copy made).
+ * dy must not overlap y or dout. */
+PVJ_API pvj_status_t pvj_gate_residual_bwd(const pvj_plan_t* plan, int32_t which, int32_t hidden,
+                                           const void* y, const void* gate, const void* dout,
+                                           void* dy, float* dgate, void* workspace,
+                                           size_t ws_bytes, void* stream);
+
 /* ---- introspection (pure host; used by tests and tooling) -------------------- */
 
 /* Attention work list of the plan: which = 0 forward, 1 backward.  *items
@@ -256,7 +305,9 @@ enum {
   PVJ_KERNEL_BWD_PRE = 4,
   PVJ_KERNEL_ATTN_BWD = 5,         /* dK, dV */
   PVJ_KERNEL_ATTN_BWD_DQ = 6,
-  PVJ_KERNEL_COUNT = 7
+  PVJ_KERNEL_CHAIN_FWD = 7,        /* adaptive layer norm, gate + residual */
+  PVJ_KERNEL_CHAIN_BWD = 8,        /* their backward passes */
+  PVJ_KERNEL_COUNT = 9
 };
 PVJ_API pvj_status_t pvj_profile_enable(int32_t on);
 PVJ_API pvj_status_t pvj_profile_read(int32_t kernel, double* total_ms, int64_t* launches);

@@ -35,7 +35,9 @@ PVJ_FLAG_ROPE_FUSED = 1
 PVJ_FLAG_ROPE_PREROTATED = 2
 
 KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
-           "attn_bwd_dq": 6}
+           "attn_bwd_dq": 6, "chain_fwd": 7, "chain_bwd": 8}
+STREAMS = {"text": 0, "image": 1}
+CHAIN_ADALN, CHAIN_GATE = 0, 1
 
 
 class PvjError(RuntimeError):
@@ -101,6 +103,11 @@ def load_library():
         "pvj_plan_rope_table": (I32, [P, ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
                                       ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
                                       ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "pvj_adaln_modulate": (I32, [P, I32, I32, P, P, P, P, F, P]),
+        "pvj_gate_residual": (I32, [P, I32, I32, P, P, P, P, P]),
+        "pvj_chain_bwd_workspace": (I32, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "pvj_adaln_modulate_bwd": (I32, [P, I32, I32, P, P, P, P, P, P, F, P, SZ, P]),
+        "pvj_gate_residual_bwd": (I32, [P, I32, I32, P, P, P, P, P, P, SZ, P]),
         "pvj_profile_enable": (I32, [I32]),
         "pvj_profile_read": (I32, [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "pvj_status_string": (ctypes.c_char_p, [I32]),
@@ -381,3 +388,96 @@ def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.
         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), float(softmax_scale), flags,
         _stream()))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# memory-bound chains around the attention (one modality stream at a time)
+# ---------------------------------------------------------------------------
+
+def _stream_rows(plan: Plan, which: str) -> int:
+    if which not in STREAMS:
+        raise ValueError("stream must be 'text' or 'image'")
+    return plan.n_text if which == "text" else plan.n_image
+
+
+def _check_2d(name, t, rows, cols, dtype):
+    if t is None or t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError("%s must be [%d, %d]" % (name, rows, cols))
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+
+
+def chain_workspace_bytes(plan: Plan, op: int, which: str, hidden: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load_library().pvj_chain_bwd_workspace(plan.handle, op, STREAMS[which], int(hidden),
+                                                  ctypes.byref(b)))
+    return b.value
+
+
+def adaln_modulate(plan: Plan, which: str, x, shift, scale, y=None, eps: float = 1e-6):
+    """y = LN(x) (1 + scale_i) + shift_i on one stream ([rows, hidden])."""
+    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    _check_2d("x", x, rows, hidden, plan.torch_dtype)
+    _check_2d("shift", shift, len(plan.samples), hidden, plan.torch_dtype)
+    _check_2d("scale", scale, len(plan.samples), hidden, plan.torch_dtype)
+    y = _torch().empty_like(x) if y is None else y
+    _check_2d("y", y, rows, hidden, plan.torch_dtype)
+    _check(load_library().pvj_adaln_modulate(plan.handle, STREAMS[which], hidden, _ptr(x),
+                                             _ptr(shift), _ptr(scale), _ptr(y), float(eps),
+                                             _stream()))
+    return y
+
+
+def gate_residual(plan: Plan, which: str, x, y, gate, out=None):
+    """out = x + gate_i * y on one stream."""
+    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    for n, t in (("x", x), ("y", y)):
+        _check_2d(n, t, rows, hidden, plan.torch_dtype)
+    _check_2d("gate", gate, len(plan.samples), hidden, plan.torch_dtype)
+    out = _torch().empty_like(x) if out is None else out
+    _check_2d("out", out, rows, hidden, plan.torch_dtype)
+    _check(load_library().pvj_gate_residual(plan.handle, STREAMS[which], hidden, _ptr(x), _ptr(y),
+                                            _ptr(gate), _ptr(out), _stream()))
+    return out
+
+
+def _ws(plan, op, which, hidden, like, workspace):
+    n = chain_workspace_bytes(plan, op, which, hidden)
+    if workspace is None:
+        workspace = _torch().empty(max(256, n), dtype=_torch().uint8, device=like.device)
+    return workspace
+
+
+def adaln_modulate_bwd(plan: Plan, which: str, x, scale, dy, eps: float = 1e-6, dx=None,
+                       workspace=None):
+    """(dx, dshift fp32, dscale fp32) for ``adaln_modulate``."""
+    torch = _torch()
+    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    for n, t in (("x", x), ("dy", dy)):
+        _check_2d(n, t, rows, hidden, plan.torch_dtype)
+    _check_2d("scale", scale, len(plan.samples), hidden, plan.torch_dtype)
+    dx = torch.empty_like(x) if dx is None else dx
+    B = len(plan.samples)
+    dshift = torch.empty(B, hidden, dtype=torch.float32, device=x.device)
+    dscale = torch.empty(B, hidden, dtype=torch.float32, device=x.device)
+    workspace = _ws(plan, CHAIN_ADALN, which, hidden, x, workspace)
+    _check(load_library().pvj_adaln_modulate_bwd(
+        plan.handle, STREAMS[which], hidden, _ptr(x), _ptr(scale), _ptr(dy), _ptr(dx),
+        _ptr(dshift), _ptr(dscale), float(eps), _ptr(workspace), workspace.numel(), _stream()))
+    return dx, dshift, dscale
+
+
+def gate_residual_bwd(plan: Plan, which: str, y, gate, dout, dy=None, workspace=None):
+    """(dy, dgate fp32) for ``gate_residual``; the gradient of x is dout itself."""
+    torch = _torch()
+    rows, hidden = _stream_rows(plan, which), int(y.shape[-1])
+    for n, t in (("y", y), ("dout", dout)):
+        _check_2d(n, t, rows, hidden, plan.torch_dtype)
+    _check_2d("gate", gate, len(plan.samples), hidden, plan.torch_dtype)
+    dy = torch.empty_like(y) if dy is None else dy
+    dgate = torch.empty(len(plan.samples), hidden, dtype=torch.float32, device=y.device)
+    workspace = _ws(plan, CHAIN_GATE, which, hidden, y, workspace)
+    _check(load_library().pvj_gate_residual_bwd(
+        plan.handle, STREAMS[which], hidden, _ptr(y), _ptr(gate), _ptr(dout), _ptr(dy),
+        _ptr(dgate), _ptr(workspace), workspace.numel(), _stream()))
+    return dy, dgate

@@ -1,0 +1,384 @@
+// Memory-bound chains around the joint attention, fused so each tensor is
+// read and written once (Mage-Flow review page, section "Kernel fusion":
+// normalization, adaptive modulation, gating and residual addition around the
+// backbone's main operators; section "Native-Resolution MMDiT": text and image
+// streams keep modality-specific parameters).
+//
+//  * adaln_fwd: y = LN(x) (1 + scale_i) + shift_i per row of one stream
+//    (LayerNorm without affine, population variance); one wave per row, the
+//    row held in registers (two-pass mean / variance in fp32).
+//  * gate_fwd: out = x + gate_i * y, one wave per row.
+//  * adaln_bwd_rows: dx = r (g - mean(g) - xhat mean(g xhat)), g = dy (1 +
+//    scale_i), and the row's mean and 1/std for the reduction below.
+//  * seg_partial / seg_final: the per-sample parameter gradients (dshift =
+//    sum dy, dscale = sum dy xhat, dgate = sum dout y) as deterministic
+//    column sums: every sample's rows are cut into `splits` fixed ranges
+//    (about 32 rows each for the stream's longest sample, so the reduction
+//    fills the chip), one wave per (sample, range, 512-column chunk) writes a
+//    partial sum with four rows in flight, and the final pass adds the
+//    partials in order.  The gate backward's
+//    dy = gate_i * dout is written by the same pass.
+// A row's sample i is found by binary search in the stream's cumulative
+// offsets (cu_text or cu_img of the plan).
+
+#include "pvj_device.h"
+#include "pvj_launch.h"
+
+namespace pvj {
+
+constexpr int kChainThreads = 256;     // 4 waves, one row each
+constexpr int kColChunk = 512;         // columns per reduction wave (8 per lane)
+constexpr int kRowsPerSplit = 32;      // target rows per reduction wave
+constexpr int kMaxSplit = 256;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) v += __shfl_xor(v, w, 64);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ f32x8 ld8f(const T* p) { return to_f32x8(load8<T>(p)); }
+
+// ---------------------------------------------------------------------------
+// forward: adaptive layer norm
+// ---------------------------------------------------------------------------
+template <typename T, int NU>
+__global__ __launch_bounds__(kChainThreads) void adaln_fwd_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int rows, int C, const T* __restrict__ x,
+    const T* __restrict__ shift, const T* __restrict__ scale, T* y, float eps) {
+  const int row = blockIdx.x * (kChainThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int upr = C / 8;
+  const int s = find_sample(cu, n_samples, row);
+  const T* xr = x + (size_t)row * C;
+  f32x8 v[NU];
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    v[k] = u < upr ? ld8f(xr + u * 8) : f32x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += v[k][e];
+  }
+  const float mean = wave_sum(sum) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    if (u < upr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[k][e] - mean;
+        ss += d * d;
+      }
+    }
+  }
+  const float rstd = 1.0f / __builtin_sqrtf(wave_sum(ss) / C + eps);
+  const T* sh = shift + (size_t)s * C;
+  const T* sc = scale + (size_t)s * C;
+  T* yr = y + (size_t)row * C;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    if (u < upr) {
+      const f32x8 a = ld8f(sc + u * 8), b = ld8f(sh + u * 8);
+      f32x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[k][e] - mean) * rstd * (1.f + a[e]) + b[e];
+      store8<T>(yr + u * 8, from_f32x8<T>(o));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// forward: gate + residual
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kChainThreads) void gate_fwd_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int rows, int C, const T* x, const T* y,
+    const T* __restrict__ gate, T* out) {
+  const int row = blockIdx.x * (kChainThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int upr = C / 8;
+  const int s = find_sample(cu, n_samples, row);
+  const size_t ro = (size_t)row * C;
+  const T* g = gate + (size_t)s * C;
+  for (int u = lane; u < upr; u += 64) {
+    const f32x8 a = ld8f(x + ro + u * 8), b = ld8f(y + ro + u * 8), w = ld8f(g + u * 8);
+    f32x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = a[e] + w[e] * b[e];
+    store8<T>(out + ro + u * 8, from_f32x8<T>(o));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward: adaptive layer norm, per row (dx and the row statistics)
+// ---------------------------------------------------------------------------
+template <typename T, int NU>
+__global__ __launch_bounds__(kChainThreads) void adaln_bwd_rows_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int rows, int C, const T* __restrict__ x,
+    const T* __restrict__ scale, const T* __restrict__ dy, T* dx, float2* __restrict__ stats,
+    float eps) {
+  const int row = blockIdx.x * (kChainThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int upr = C / 8;
+  const int s = find_sample(cu, n_samples, row);
+  const size_t ro = (size_t)row * C;
+  f32x8 v[NU], g[NU];
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    v[k] = u < upr ? ld8f(x + ro + u * 8) : f32x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += v[k][e];
+  }
+  const float mean = wave_sum(sum) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    if (u < upr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[k][e] - mean;
+        ss += d * d;
+      }
+    }
+  }
+  const float rstd = 1.0f / __builtin_sqrtf(wave_sum(ss) / C + eps);
+  // g = dy (1 + scale_s); means of g and g * xhat
+  float sg = 0.f, sgx = 0.f;
+  const T* sc = scale + (size_t)s * C;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    if (u < upr) {
+      const f32x8 d = ld8f(dy + ro + u * 8), a = ld8f(sc + u * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[k][e] = (v[k][e] - mean) * rstd;  // xhat from here on
+        g[k][e] = d[e] * (1.f + a[e]);
+        sg += g[k][e];
+        sgx += g[k][e] * v[k][e];
+      }
+    } else {
+      g[k] = f32x8{};
+    }
+  }
+  const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    if (u < upr) {
+      f32x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rstd * (g[k][e] - mg - v[k][e] * mgx);
+      store8<T>(dx + ro + u * 8, from_f32x8<T>(o));
+    }
+  }
+  if (lane == 0) stats[row] = make_float2(mean, rstd);
+}
+
+// ---------------------------------------------------------------------------
+// per-sample column sums: partial pass and final pass
+//   MODE 0 (adaln): p0 = sum dy, p1 = sum dy * (x - mean) rstd
+//   MODE 1 (gate):  p0 = sum dout * y, and dy = gate_s * dout is written
+// partial layout: [kind][sample][split][C] fp32
+// ---------------------------------------------------------------------------
+template <typename T, int MODE>
+__global__ __launch_bounds__(64) void seg_partial_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int C, int splits, const T* __restrict__ a,
+    const T* __restrict__ b, const float2* __restrict__ stats, const T* __restrict__ gate,
+    T* __restrict__ dy_out, float* __restrict__ partial) {
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int split = (blockIdx.x / nchunk) % splits;
+  const int s = blockIdx.x / (nchunk * splits);
+  const int r0 = cu[s], len = cu[s + 1] - cu[s];
+  const int lo = r0 + (int)((long long)len * split / splits);
+  const int hi = r0 + (int)((long long)len * (split + 1) / splits);
+  const int col = chunk * kColChunk + threadIdx.x * 8;
+  if (col >= C) return;
+  f32x8 acc0[2] = {}, acc1[2] = {};
+  f32x8 w = {};
+  if (MODE == 1) w = ld8f(gate + (size_t)s * C + col);
+  auto row = [&](int r, int slot) {
+    const size_t o = (size_t)r * C + col;
+    const f32x8 va = ld8f(a + o), vb = ld8f(b + o);
+    if (MODE == 0) {
+      const float2 st = stats[r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc0[slot][e] += vb[e];                            // b = dy
+        acc1[slot][e] += vb[e] * ((va[e] - st.x) * st.y);  // a = x
+      }
+    } else {
+      f32x8 d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc0[slot][e] += va[e] * vb[e];  // a = dout, b = y
+        d[e] = w[e] * va[e];
+      }
+      store8<T>(dy_out + o, from_f32x8<T>(d));
+    }
+  };
+  int r = lo;
+  for (; r + 4 <= hi; r += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) row(r + k, k & 1);
+  }
+  for (; r < hi; ++r) row(r, 0);
+  const size_t po = ((size_t)s * splits + split) * C + col;
+  *reinterpret_cast<f32x8*>(partial + po) = acc0[0] + acc0[1];
+  if (MODE == 0)
+    *reinterpret_cast<f32x8*>(partial + (size_t)n_samples * splits * C + po) = acc1[0] + acc1[1];
+}
+
+__global__ __launch_bounds__(64) void seg_final_kernel(int n_samples, int C, int splits, int kinds,
+                                                       const float* __restrict__ partial,
+                                                       float* __restrict__ out0,
+                                                       float* __restrict__ out1) {
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int s = (blockIdx.x / nchunk) % n_samples;
+  const int kind = blockIdx.x / (nchunk * n_samples);
+  if (kind >= kinds) return;
+  const int col = chunk * kColChunk + threadIdx.x * 8;
+  if (col >= C) return;
+  const float* p =
+      partial + (size_t)kind * n_samples * splits * C + (size_t)s * splits * C + col;
+  f32x8 acc = {};
+  for (int k = 0; k < splits; ++k) acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * C);
+  *reinterpret_cast<f32x8*>((kind ? out1 : out0) + (size_t)s * C + col) = acc;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+int chain_splits(int max_sample_rows) {
+  const int s = (max_sample_rows + kRowsPerSplit - 1) / kRowsPerSplit;
+  return s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
+}
+
+size_t chain_workspace_bytes(int n_samples, int C, int rows, int mode, int splits) {
+  const size_t part = (size_t)(mode == 0 ? 2 : 1) * n_samples * splits * C * sizeof(float);
+  const size_t st = mode == 0 ? (size_t)rows * sizeof(float2) : 0;
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  return al(part) + al(st);
+}
+
+template <typename T, int NU>
+static void adaln_fwd_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int rows, int C,
+                        const void* x, const void* shift, const void* scale, void* y, float eps) {
+  adaln_fwd_kernel<T, NU><<<g, kChainThreads, 0, st>>>(cu, B, rows, C, (const T*)x, (const T*)shift,
+                                                       (const T*)scale, (T*)y, eps);
+}
+template <typename T, int NU>
+static void adaln_bwd_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int rows, int C,
+                        const void* x, const void* scale, const void* dy, void* dx, float2* stats,
+                        float eps) {
+  adaln_bwd_rows_kernel<T, NU><<<g, kChainThreads, 0, st>>>(
+      cu, B, rows, C, (const T*)x, (const T*)scale, (const T*)dy, (T*)dx, stats, eps);
+}
+
+// units per lane for a row of C columns (C / 8 units over 64 lanes)
+static int units_per_lane(int C) { return (C / 8 + 63) / 64; }
+
+#define PVJ_NU_DISPATCH(FN, T, ...)                  \
+  do {                                               \
+    const int nu = units_per_lane(C);                \
+    if (nu <= 1) FN<T, 1>(__VA_ARGS__);              \
+    else if (nu <= 2) FN<T, 2>(__VA_ARGS__);         \
+    else if (nu <= 4) FN<T, 4>(__VA_ARGS__);         \
+    else if (nu <= 6) FN<T, 6>(__VA_ARGS__);         \
+    else if (nu <= 8) FN<T, 8>(__VA_ARGS__);         \
+    else if (nu <= 12) FN<T, 12>(__VA_ARGS__);       \
+    else FN<T, 16>(__VA_ARGS__);                     \
+  } while (0)
+
+hipError_t launch_adaln_fwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+                            const void* shift, const void* scale, void* y, float eps,
+                            hipStream_t st) {
+  const int rows = which == 0 ? m.n_text : m.n_img;
+  if (rows == 0) return hipSuccess;
+  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  const dim3 g((rows + 3) / 4);
+  if (p->desc.dtype == PVJ_BF16)
+    PVJ_NU_DISPATCH(adaln_fwd_t, bf16, g, st, cu, m.n_samples, rows, C, x, shift, scale, y, eps);
+  else
+    PVJ_NU_DISPATCH(adaln_fwd_t, float, g, st, cu, m.n_samples, rows, C, x, shift, scale, y, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_fwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+                           const void* y, const void* gate, void* out, hipStream_t st) {
+  const int rows = which == 0 ? m.n_text : m.n_img;
+  if (rows == 0) return hipSuccess;
+  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  const dim3 g((rows + 3) / 4);
+  if (p->desc.dtype == PVJ_BF16)
+    gate_fwd_kernel<bf16><<<g, kChainThreads, 0, st>>>(cu, m.n_samples, rows, C, (const bf16*)x,
+                                                       (const bf16*)y, (const bf16*)gate, (bf16*)out);
+  else
+    gate_fwd_kernel<float><<<g, kChainThreads, 0, st>>>(cu, m.n_samples, rows, C, (const float*)x,
+                                                        (const float*)y, (const float*)gate,
+                                                        (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+                            const void* scale, const void* dy, void* dx, float* dshift,
+                            float* dscale, float eps, int splits, void* ws, hipStream_t st) {
+  const int rows = which == 0 ? m.n_text : m.n_img;
+  const int B = m.n_samples;
+  if (B == 0) return hipSuccess;
+  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  const size_t part = (size_t)2 * B * splits * C * sizeof(float);
+  float* partial = static_cast<float*>(ws);
+  float2* stats = reinterpret_cast<float2*>(static_cast<char*>(ws) + (part + 255) / 256 * 256);
+  const bool bf = p->desc.dtype == PVJ_BF16;
+  if (rows > 0) {
+    const dim3 g((rows + 3) / 4);
+    if (bf)
+      PVJ_NU_DISPATCH(adaln_bwd_t, bf16, g, st, cu, B, rows, C, x, scale, dy, dx, stats, eps);
+    else
+      PVJ_NU_DISPATCH(adaln_bwd_t, float, g, st, cu, B, rows, C, x, scale, dy, dx, stats, eps);
+  }
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  if (bf)
+    seg_partial_kernel<bf16, 0><<<B * splits * nchunk, 64, 0, st>>>(
+        cu, B, C, splits, (const bf16*)x, (const bf16*)dy, stats, nullptr, nullptr, partial);
+  else
+    seg_partial_kernel<float, 0><<<B * splits * nchunk, 64, 0, st>>>(
+        cu, B, C, splits, (const float*)x, (const float*)dy, stats, nullptr, nullptr, partial);
+  seg_final_kernel<<<2 * B * nchunk, 64, 0, st>>>(B, C, splits, 2, partial, dshift, dscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, const void* y,
+                           const void* gate, const void* dout, void* dy, float* dgate, int splits,
+                           void* ws, hipStream_t st) {
+  const int B = m.n_samples;
+  if (B == 0) return hipSuccess;
+  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  float* partial = static_cast<float*>(ws);
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  if (p->desc.dtype == PVJ_BF16)
+    seg_partial_kernel<bf16, 1><<<B * splits * nchunk, 64, 0, st>>>(
+        cu, B, C, splits, (const bf16*)dout, (const bf16*)y, nullptr, (const bf16*)gate,
+        (bf16*)dy, partial);
+  else
+    seg_partial_kernel<float, 1><<<B * splits * nchunk, 64, 0, st>>>(
+        cu, B, C, splits, (const float*)dout, (const float*)y, nullptr, (const float*)gate,
+        (float*)dy, partial);
+  seg_final_kernel<<<B * nchunk, 64, 0, st>>>(B, C, splits, 1, partial, dgate, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace pvj

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -269,6 +270,130 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
   return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
                                          unrotate, s)),
                   "varlen_attn_bwd dQ");
+}
+
+// ---- memory-bound chains --------------------------------------------------
+
+static pvj_status_t check_chain(const pvj_plan* p, int32_t which, int32_t hidden, int* rows) {
+  PVJ_TRY(check_plan(p));
+  if (which != PVJ_STREAM_TEXT && which != PVJ_STREAM_IMAGE)
+    return fail(PVJ_ERR_INVALID_ARG, "stream must be PVJ_STREAM_TEXT or PVJ_STREAM_IMAGE");
+  if (hidden < 8 || hidden > 8192 || hidden % 8)
+    return fail(PVJ_ERR_UNSUPPORTED, "hidden %d: need a multiple of 8 in [8, 8192]", hidden);
+  const int64_t n = which == PVJ_STREAM_TEXT ? p->n_text : p->n_img;
+  if (n * hidden * (int64_t)elt_size(p) >= (int64_t(1) << 40))
+    return fail(PVJ_ERR_OVERFLOW, "stream tensor too large");
+  *rows = (int)n;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_adaln_modulate(const pvj_plan_t* p, int32_t which, int32_t hidden,
+                                        const void* x, const void* shift, const void* scale,
+                                        void* y, float eps, void* stream) {
+  int rows = 0;
+  PVJ_TRY(check_chain(p, which, hidden, &rows));
+  PVJ_TRY(check_ptr(x, "x", rows > 0));
+  PVJ_TRY(check_ptr(y, "y", rows > 0));
+  PVJ_TRY(check_ptr(shift, "shift", rows > 0));
+  PVJ_TRY(check_ptr(scale, "scale", rows > 0));
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(PVJ_ERR_INVALID_ARG, "eps must be > 0");
+  KernelTimer t(PVJ_KERNEL_CHAIN_FWD, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_adaln_fwd(p, device_meta(p), which, hidden, x, shift, scale, y,
+                                          eps, static_cast<hipStream_t>(stream))),
+                  "adaln_modulate");
+}
+
+PVJ_API pvj_status_t pvj_gate_residual(const pvj_plan_t* p, int32_t which, int32_t hidden,
+                                       const void* x, const void* y, const void* gate, void* out,
+                                       void* stream) {
+  int rows = 0;
+  PVJ_TRY(check_chain(p, which, hidden, &rows));
+  PVJ_TRY(check_ptr(x, "x", rows > 0));
+  PVJ_TRY(check_ptr(y, "y", rows > 0));
+  PVJ_TRY(check_ptr(gate, "gate", rows > 0));
+  PVJ_TRY(check_ptr(out, "out", rows > 0));
+  KernelTimer t(PVJ_KERNEL_CHAIN_FWD, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_gate_fwd(p, device_meta(p), which, hidden, x, y, gate, out,
+                                         static_cast<hipStream_t>(stream))),
+                  "gate_residual");
+}
+
+// row ranges per sample of the chain reductions (from the stream's longest sample)
+static int stream_splits(const pvj_plan* p, int32_t which) {
+  const int32_t* cu = host_section<int32_t>(p, which == PVJ_STREAM_TEXT ? p->off_cu_text
+                                                                        : p->off_cu_img);
+  int mx = 0;
+  for (int i = 0; i < p->n_samples; ++i) mx = std::max(mx, (int)(cu[i + 1] - cu[i]));
+  return chain_splits(mx);
+}
+
+PVJ_API pvj_status_t pvj_chain_bwd_workspace(const pvj_plan_t* p, int32_t op, int32_t which,
+                                             int32_t hidden, size_t* bytes) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (!bytes) return fail(PVJ_ERR_INVALID_ARG, "bytes is NULL");
+  if (op != PVJ_CHAIN_ADALN && op != PVJ_CHAIN_GATE)
+    return fail(PVJ_ERR_INVALID_ARG, "op must be PVJ_CHAIN_ADALN or PVJ_CHAIN_GATE");
+  if (which != PVJ_STREAM_TEXT && which != PVJ_STREAM_IMAGE)
+    return fail(PVJ_ERR_INVALID_ARG, "stream must be PVJ_STREAM_TEXT or PVJ_STREAM_IMAGE");
+  if (hidden < 8 || hidden > 8192 || hidden % 8)
+    return fail(PVJ_ERR_UNSUPPORTED, "hidden %d: need a multiple of 8 in [8, 8192]", hidden);
+  const int rows = which == PVJ_STREAM_TEXT ? p->n_text : p->n_img;
+  *bytes = chain_workspace_bytes(p->n_samples, hidden, rows, op == PVJ_CHAIN_ADALN ? 0 : 1,
+                                 stream_splits(p, which));
+  return PVJ_OK;
+}
+
+static pvj_status_t check_ws(const pvj_plan* p, int32_t op, int32_t which, int32_t hidden,
+                             const void* ws, size_t ws_bytes) {
+  size_t need = 0;
+  PVJ_TRY(pvj_chain_bwd_workspace(p, op, which, hidden, &need));
+  if (p->n_samples == 0) return PVJ_OK;
+  if (!ws) return fail(PVJ_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(PVJ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(PVJ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_adaln_modulate_bwd(const pvj_plan_t* p, int32_t which, int32_t hidden,
+                                            const void* x, const void* scale, const void* dy,
+                                            void* dx, float* dshift, float* dscale, float eps,
+                                            void* workspace, size_t ws_bytes, void* stream) {
+  int rows = 0;
+  PVJ_TRY(check_chain(p, which, hidden, &rows));
+  PVJ_TRY(check_ptr(x, "x", rows > 0));
+  PVJ_TRY(check_ptr(dy, "dy", rows > 0));
+  PVJ_TRY(check_ptr(dx, "dx", rows > 0));
+  PVJ_TRY(check_ptr(scale, "scale", rows > 0));
+  PVJ_TRY(check_ptr(dshift, "dshift", p->n_samples > 0));
+  PVJ_TRY(check_ptr(dscale, "dscale", p->n_samples > 0));
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(PVJ_ERR_INVALID_ARG, "eps must be > 0");
+  PVJ_TRY(check_ws(p, PVJ_CHAIN_ADALN, which, hidden, workspace, ws_bytes));
+  KernelTimer t(PVJ_KERNEL_CHAIN_BWD, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_adaln_bwd(p, device_meta(p), which, hidden, x, scale, dy, dx,
+                                          dshift, dscale, eps, stream_splits(p, which), workspace,
+                                          static_cast<hipStream_t>(stream))),
+                  "adaln_modulate_bwd");
+}
+
+PVJ_API pvj_status_t pvj_gate_residual_bwd(const pvj_plan_t* p, int32_t which, int32_t hidden,
+                                           const void* y, const void* gate, const void* dout,
+                                           void* dy, float* dgate, void* workspace,
+                                           size_t ws_bytes, void* stream) {
+  int rows = 0;
+  PVJ_TRY(check_chain(p, which, hidden, &rows));
+  PVJ_TRY(check_ptr(y, "y", rows > 0));
+  PVJ_TRY(check_ptr(dout, "dout", rows > 0));
+  PVJ_TRY(check_ptr(dy, "dy", rows > 0));
+  PVJ_TRY(check_ptr(gate, "gate", rows > 0));
+  PVJ_TRY(check_ptr(dgate, "dgate", p->n_samples > 0));
+  PVJ_TRY(check_ws(p, PVJ_CHAIN_GATE, which, hidden, workspace, ws_bytes));
+  KernelTimer t(PVJ_KERNEL_CHAIN_BWD, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_gate_bwd(p, device_meta(p), which, hidden, y, gate, dout, dy,
+                                         dgate, stream_splits(p, which), workspace,
+                                         static_cast<hipStream_t>(stream))),
+                  "gate_residual_bwd");
 }
 
 PVJ_API pvj_status_t pvj_profile_enable(int32_t on) {
