@@ -110,6 +110,30 @@ class PackStep:
         self.plan = plan
 
 
+def inference_bench(steps, warmup=2):
+    """The multi-prompt classifier-free-guidance inference pack (6 prompts x
+    cond/uncond, forward only: plan, pack with RoPE, attention forward, unpack
+    O), timed like the main step."""
+    import torch
+    from pvj_inputs import workload
+    wl = workload("infer_multi")
+    step = PackStep(wl, 0)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    cu = step.plan.cu_seqlens
+    S2 = float(sum((cu[i + 1] - cu[i]) ** 2 for i in range(len(wl.samples))))
+    f = 4.0 * wl.n_heads * wl.head_dim * S2
+    return {"workload": wl.name, "n_samples": len(wl.samples), "n_tokens": wl.n_tokens,
+            "ms_per_step": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(wl.n_tokens / (ms * 1e-3), 1)}
+
+
 def chain_bench(wl, reps):
     """HBM-bound chains around the attention on both streams of the pack, at the
     backbone width H*D: adaptive layer norm + modulation and gate + residual,
@@ -334,6 +358,7 @@ def main():
             (f_fwd + f_bwd) / ((kern["attn_fwd"]["avg_ms"] + t_bwd) * 1e-3) / 1e12, 2)
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
+        out["inference"] = inference_bench(5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:

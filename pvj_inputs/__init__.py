@@ -27,6 +27,15 @@ available here):
                    exceed the budget; forward + backward.
 * ``extreme``      2048x2048, 2048x512, 512x2048 and four 512x512 samples, each
                    with text length drawn from [16, 512]; forward + backward.
+* ``infer_multi``  a multi-prompt inference pack (review page, section
+                   "Native-Resolution MMDiT": the classifier-free-guidance
+                   branches of a sample share one pack; HF model card, "Python
+                   API": a list of per-sample heights and widths in one call):
+                   6 prompts, pixel sides drawn from {512, 576, ..., 2048},
+                   text length from [32, 512]; each prompt contributes a
+                   conditional sample and an unconditional sample with 16
+                   text tokens whose image rows are copies of the conditional
+                   ones; forward only.
 * ``edit_1024``    an editing pack (review page, section "Native-Resolution
                    MMDiT": the edit model joins source and target latents under
                    a frame axis): a 1024x1024 pair (two 64x64 frames) with 256
@@ -107,6 +116,22 @@ def draw_extreme_pack(seed: int) -> List[Sample]:
     return [(h, w, int(rng.integers(16, 513))) for (h, w) in grids]
 
 
+def draw_multi_prompt_pack(seed: int, n_prompts: int = 6):
+    """(samples, shared_image) of a multi-prompt CFG pack: per prompt a
+    conditional sample (h, w, t) then its unconditional twin (h, w, 16)."""
+    rng = np.random.default_rng(seed)
+    samples: List[Sample] = []
+    shared = []
+    for _ in range(n_prompts):
+        hp = 512 + 64 * int(rng.integers(0, 25))
+        wp = 512 + 64 * int(rng.integers(0, 25))
+        t = int(rng.integers(32, 513))
+        h, w = hp // PIXELS_PER_TOKEN_SIDE, wp // PIXELS_PER_TOKEN_SIDE
+        shared.append((len(samples), len(samples) + 1))
+        samples += [(h, w, t), (h, w, 16)]
+    return samples, shared
+
+
 def workload(name: str, seed: int = 0) -> Workload:
     if name == "tiny_f32":
         return Workload(name, [(16, 16, 32), (8, 32, 16)], 2, 64, "f32", False, seed)
@@ -119,13 +144,17 @@ def workload(name: str, seed: int = 0) -> Workload:
         return Workload(name, draw_train_pack(seed), 24, 128, "bf16", True, 1000 + seed)
     if name == "extreme":
         return Workload(name, draw_extreme_pack(seed), 24, 128, "bf16", True, seed)
+    if name == "infer_multi":
+        smp, shared = draw_multi_prompt_pack(seed)
+        return Workload(name, smp, 24, 128, "bf16", False, 3000 + seed, shared_image=shared)
     if name == "edit_1024":
         return Workload(name, [(64, 64, 256, 2), (48, 64, 128, 2)], 24, 128, "bf16", True,
                         2000 + seed)
     raise KeyError(name)
 
 
-WORKLOADS = ["tiny_f32", "single_1024", "cfg_1024", "train_64k", "extreme", "edit_1024"]
+WORKLOADS = ["tiny_f32", "single_1024", "cfg_1024", "train_64k", "extreme", "edit_1024",
+             "infer_multi"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

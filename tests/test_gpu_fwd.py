@@ -320,3 +320,25 @@ def test_fwd_large_workloads_sampled(name, seed):
     q, k, v = workload_tensors(wl, 3)
     o, lse = _fwd(plan, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), True, "bf16")
     _sampled_rows(wl, q, k, v, o, lse, np.random.default_rng(1), 6, 64)
+
+
+def test_fwd_multi_prompt_cfg_pack():
+    # several prompts, each a cond/uncond pair sharing its image rows, in one
+    # inference pack: every pair's rows equal a call on that pair alone
+    # (bitwise), the uncond image rows see the same queries as the cond ones,
+    # and sampled rows match the oracle
+    wl = workload("infer_multi")
+    say("fwd infer_multi T=%d prompts=%d" % (wl.n_tokens, len(wl.shared_image)))
+    plan = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
+    q, k, v = workload_tensors(wl, 3)
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    o, lse = _fwd(plan, qd, kd, vd, True, "bf16")
+    cu = plan.cu_seqlens
+    for (c, u) in wl.shared_image[:3]:
+        a, b = cu[c], cu[u + 1]
+        p2 = _plan(wl.samples[c:u + 1], wl.n_heads, wl.head_dim, "bf16")
+        o2, l2 = pvj.varlen_attn_fwd(p2, qd[a:b].contiguous(), kd[a:b].contiguous(),
+                                     vd[a:b].contiguous(), rope_fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o[a:b]) and torch.equal(l2, lse[:, a:b])
+    _sampled_rows(wl, q, k, v, o, lse, np.random.default_rng(5), 6, 48)
