@@ -16,7 +16,7 @@
 //    (about 32 rows each for the stream's longest sample, so the reduction
 //    fills the chip), one wave per (sample, range, 512-column chunk) writes a
 //    partial sum with four rows in flight, and the final pass adds the
-//    partials in order.  The gate backward's
+//    partials in a fixed order.  The gate backward's
 //    dy = gate_i * dout is written by the same pass.
 // A row's sample i is found by binary search in the stream's cumulative
 // offsets (cu_text or cu_img of the plan).
@@ -240,22 +240,41 @@ __global__ __launch_bounds__(64) void seg_partial_kernel(
     *reinterpret_cast<f32x8*>(partial + (size_t)n_samples * splits * C + po) = acc1[0] + acc1[1];
 }
 
-__global__ __launch_bounds__(64) void seg_final_kernel(int n_samples, int C, int splits, int kinds,
-                                                       const float* __restrict__ partial,
-                                                       float* __restrict__ out0,
-                                                       float* __restrict__ out1) {
+// final pass: 4 waves per (kind, sample, column chunk); wave w adds the
+// partials w, w+4, ... with two loads in flight, then wave 0 adds the four
+// wave sums in order (a fixed order: deterministic)
+__global__ __launch_bounds__(256) void seg_final_kernel(int n_samples, int C, int splits, int kinds,
+                                                        const float* __restrict__ partial,
+                                                        float* __restrict__ out0,
+                                                        float* __restrict__ out1) {
+  __shared__ f32x8 red[3][64];
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   const int chunk = blockIdx.x % nchunk;
   const int s = (blockIdx.x / nchunk) % n_samples;
   const int kind = blockIdx.x / (nchunk * n_samples);
-  if (kind >= kinds) return;
-  const int col = chunk * kColChunk + threadIdx.x * 8;
-  if (col >= C) return;
-  const float* p =
-      partial + (size_t)kind * n_samples * splits * C + (size_t)s * splits * C + col;
-  f32x8 acc = {};
-  for (int k = 0; k < splits; ++k) acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * C);
-  *reinterpret_cast<f32x8*>((kind ? out1 : out0) + (size_t)s * C + col) = acc;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = chunk * kColChunk + lane * 8;
+  const bool active = kind < kinds && col < C;
+  f32x8 acc0 = {}, acc1 = {};
+  if (active) {
+    const float* p =
+        partial + (size_t)kind * n_samples * splits * C + (size_t)s * splits * C + col;
+    int k = wave;
+    for (; k + 4 < splits; k += 8) {
+      acc0 += *reinterpret_cast<const f32x8*>(p + (size_t)k * C);
+      acc1 += *reinterpret_cast<const f32x8*>(p + (size_t)(k + 4) * C);
+    }
+    if (k < splits) acc0 += *reinterpret_cast<const f32x8*>(p + (size_t)k * C);
+    acc0 += acc1;
+  }
+  if (wave > 0) red[wave - 1][lane] = acc0;
+  __syncthreads();
+  if (wave == 0 && active) {
+    acc0 += red[0][lane];
+    acc0 += red[1][lane];
+    acc0 += red[2][lane];
+    *reinterpret_cast<f32x8*>((kind ? out1 : out0) + (size_t)s * C + col) = acc0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -357,7 +376,7 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
   else
     seg_partial_kernel<float, 0><<<B * splits * nchunk, 64, 0, st>>>(
         cu, B, C, splits, (const float*)x, (const float*)dy, stats, nullptr, nullptr, partial);
-  seg_final_kernel<<<2 * B * nchunk, 64, 0, st>>>(B, C, splits, 2, partial, dshift, dscale);
+  seg_final_kernel<<<2 * B * nchunk, 256, 0, st>>>(B, C, splits, 2, partial, dshift, dscale);
   return hipGetLastError();
 }
 
@@ -377,7 +396,7 @@ hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, c
     seg_partial_kernel<float, 1><<<B * splits * nchunk, 64, 0, st>>>(
         cu, B, C, splits, (const float*)dout, (const float*)y, nullptr, (const float*)gate,
         (float*)dy, partial);
-  seg_final_kernel<<<B * nchunk, 64, 0, st>>>(B, C, splits, 1, partial, dgate, nullptr);
+  seg_final_kernel<<<B * nchunk, 256, 0, st>>>(B, C, splits, 1, partial, dgate, nullptr);
   return hipGetLastError();
 }
 
