@@ -443,6 +443,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
     V8 sfr[2][2];  // dS^T fragments [32-key block][16-key step]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // the products run at raised wave priority: the SIMD's other wave (another
+      // workgroup) then fills the gaps with its softmax work instead of
+      // delaying these matrix-core issues
+      __builtin_amdgcn_s_setprio(1);
       f32x16 s = {}, dp = {};
       const int rho = kb * 32 + l32;
 #pragma unroll
@@ -460,6 +464,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
         mma16(s, kf, qf[kk]);
         mma16(dp, vf, gf[kk]);
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
@@ -470,6 +475,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     // dQ'^T += K'^T dS^T
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -493,6 +499,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
           }
           mma16(acc[db], kt, sfr[kb][st]);
         }
+    __builtin_amdgcn_s_setprio(0);
     if (j + 1 < nkv) store_kv(B ^ 1);
     __syncthreads();
   };
