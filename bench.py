@@ -356,6 +356,11 @@ def main():
         out["bwd_tflops"] = round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)
         out["fwd_bwd_kernel_tflops"] = round(
             (f_fwd + f_bwd) / ((kern["attn_fwd"]["avg_ms"] + t_bwd) * 1e-3) / 1e12, 2)
+    if roof is not None:
+        # the chip's sustained matrix-core rate, measured live beside the published peak
+        ceil = pvj.diag_mfma_peak()
+        roof["measured_ceiling"] = round(ceil, 1)
+        roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
         out["inference"] = inference_bench(5)

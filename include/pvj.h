@@ -290,6 +290,17 @@ PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* plan, const float** c
  * head-dim size of each part (dims[2] = 0 for two axes). */
 PVJ_API pvj_status_t pvj_plan_rope_axes(const pvj_plan_t* plan, int32_t* n_axes, int32_t dims[3]);
 
+/* ---- diagnostic: measured matrix-core ceiling -----------------------------------
+ * Enqueues a kernel that keeps every SIMD issuing only independent
+ * v_mfma_f32_32x32x16_bf16 (2 workgroups of 4 waves per CU, `rounds` times
+ * over the 256 CUs, `iters` x 4 products per wave) and returns its bf16 FLOP
+ * count in *flop; timing it (events on `stream`) gives the sustained
+ * matrix-core rate the attention kernels are compared with beside the
+ * published dense peak.  sink: device fp32, >= 131072 * rounds floats
+ * (receives the accumulators so the work is kept). */
+PVJ_API pvj_status_t pvj_diag_mfma_peak(int32_t rounds, int32_t iters, float* sink,
+                                        size_t sink_floats, double* flop, void* stream);
+
 /* ---- per-kernel timing (tracing) ---------------------------------------------
  * When enabled, every kernel the library launches is bracketed by two HIP
  * events recorded on the stream it is launched on; pvj_profile_read waits for

@@ -108,6 +108,7 @@ def load_library():
         "pvj_chain_bwd_workspace": (I32, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
         "pvj_adaln_modulate_bwd": (I32, [P, I32, I32, P, P, P, P, P, P, F, P, SZ, P]),
         "pvj_gate_residual_bwd": (I32, [P, I32, I32, P, P, P, P, P, P, SZ, P]),
+        "pvj_diag_mfma_peak": (I32, [I32, I32, P, SZ, ctypes.POINTER(ctypes.c_double), P]),
         "pvj_profile_enable": (I32, [I32]),
         "pvj_profile_read": (I32, [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "pvj_status_string": (ctypes.c_char_p, [I32]),
@@ -481,3 +482,23 @@ def gate_residual_bwd(plan: Plan, which: str, y, gate, dout, dy=None, workspace=
         plan.handle, STREAMS[which], hidden, _ptr(y), _ptr(gate), _ptr(dout), _ptr(dy),
         _ptr(dgate), _ptr(workspace), workspace.numel(), _stream()))
     return dy, dgate
+
+
+def diag_mfma_peak(rounds: int = 4, iters: int = 20000, reps: int = 3) -> float:
+    """Sustained bf16 matrix-core TFLOP/s of the chip (best of `reps` timed runs
+    of the library's matrix-core-only kernel, after one warm-up run)."""
+    torch = _torch()
+    sink = torch.empty(131072 * rounds, dtype=torch.float32, device="cuda")
+    flop = ctypes.c_double()
+    lib = load_library()
+    best = 0.0
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check(lib.pvj_diag_mfma_peak(rounds, iters, _ptr(sink), sink.numel(), ctypes.byref(flop),
+                                      _stream()))
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            best = max(best, flop.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best

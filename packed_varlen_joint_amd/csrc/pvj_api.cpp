@@ -396,6 +396,19 @@ PVJ_API pvj_status_t pvj_gate_residual_bwd(const pvj_plan_t* p, int32_t which, i
                   "gate_residual_bwd");
 }
 
+PVJ_API pvj_status_t pvj_diag_mfma_peak(int32_t rounds, int32_t iters, float* sink,
+                                        size_t sink_floats, double* flop, void* stream) {
+  if (rounds < 1 || rounds > 64 || iters < 1 || iters > (1 << 20))
+    return fail(PVJ_ERR_INVALID_ARG, "rounds in [1, 64], iters in [1, 2^20]");
+  if (!flop) return fail(PVJ_ERR_INVALID_ARG, "flop is NULL");
+  const size_t need = (size_t)256 * 2 * rounds * 256;
+  PVJ_TRY(check_ptr(sink, "sink", true));
+  if (sink_floats < need)
+    return fail(PVJ_ERR_WORKSPACE_TOO_SMALL, "sink %zu < %zu floats", sink_floats, need);
+  return launched(launch_mfma_peak(rounds, iters, sink, flop, static_cast<hipStream_t>(stream)),
+                  "diag_mfma_peak");
+}
+
 PVJ_API pvj_status_t pvj_profile_enable(int32_t on) {
   for (auto& e : g_prof_pending) {
     (void)hipEventSynchronize(e.stop);

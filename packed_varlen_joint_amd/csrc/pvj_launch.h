@@ -44,4 +44,7 @@ hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, c
                            const void* gate, const void* dout, void* dy, float* dgate, int splits,
                            void* ws, hipStream_t stream);
 
+// diagnostic: matrix-core-only kernel on every CU; *flop = its bf16 FLOP count
+hipError_t launch_mfma_peak(int rounds, int iters, float* sink, double* flop, hipStream_t stream);
+
 }  // namespace pvj

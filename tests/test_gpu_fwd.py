@@ -342,3 +342,15 @@ def test_fwd_multi_prompt_cfg_pack():
         torch.cuda.synchronize()
         assert torch.equal(o2, o[a:b]) and torch.equal(l2, lse[:, a:b])
     _sampled_rows(wl, q, k, v, o, lse, np.random.default_rng(5), 6, 48)
+
+
+def test_diag_mfma_peak_runs():
+    # the matrix-core ceiling probe runs and reports a plausible rate
+    # (well above what the attention kernels reach, at most the chip's peak)
+    tf = pvj.diag_mfma_peak(rounds=1, iters=2000, reps=1)
+    say("measured matrix-core ceiling (small run): %.0f TFLOP/s" % tf)
+    assert 500.0 < tf < 2600.0
+    lib = pvj.load_library()
+    import ctypes
+    f = ctypes.c_double()
+    assert lib.pvj_diag_mfma_peak(0, 10, 16, 1 << 20, ctypes.byref(f), None) == 1
