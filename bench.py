@@ -196,6 +196,50 @@ def chain_bench(wl, reps):
     return out
 
 
+def proj_bench(wl, reps):
+    """The per-stream projections with the pack / unpack fused in, at the
+    backbone width (hidden = H*D): QKV projection writing joint Q, K, V with
+    RoPE, and the output projection reading the joint O; both streams per call,
+    algorithmic FLOP 2 * rows * hidden * out_features."""
+    import torch
+    import packed_varlen_joint_amd as pvj
+    plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+    HD = wl.n_heads * wl.head_dim
+    C = HD
+    g = torch.Generator(device="cuda").manual_seed(11)
+    mk = lambda *sh: (torch.randn(*sh, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    xs = {"text": mk(plan.n_text, C), "image": mk(plan.n_image, C)}
+    wq = {w: mk(3 * HD, C) for w in xs}
+    wo = {w: mk(C, HD) for w in xs}
+    q, k, v = (torch.empty(plan.n_tokens, wl.n_heads, wl.head_dim, device="cuda",
+                           dtype=torch.bfloat16) for _ in range(3))
+    ys = {w: torch.empty(xs[w].shape[0], C, device="cuda", dtype=torch.bfloat16) for w in xs}
+    rows = plan.n_text + plan.n_image
+    ops = {
+        "qkv_proj_pack": (2.0 * rows * C * 3 * HD, lambda: [pvj.qkv_proj_pack(
+            plan, w, xs[w], wq[w], q=q, k=k, v=v, rope=True) for w in xs]),
+        "out_proj_unpack": (2.0 * rows * HD * C, lambda: [pvj.out_proj_unpack(
+            plan, w, q, wo[w], y=ys[w]) for w in xs]),
+    }
+    out = {}
+    for name, (flop, fn) in ops.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    out["_note"] = "both streams per call, hidden %d, %d rows" % (C, rows)
+    return out
+
+
 def cpu_baseline(wl, seconds):
     """The oracle (fp64 NumPy, as it stands) on a bounded sample of the workload:
     forward + backward of (sample, head) slices, smallest samples first, until
@@ -364,6 +408,8 @@ def main():
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
         out["inference"] = inference_bench(5)
+        if wl.dtype == "bf16":
+            out["projections"] = proj_bench(wl, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:

@@ -290,6 +290,32 @@ PVJ_API pvj_status_t pvj_plan_rope_table(const pvj_plan_t* plan, const float** c
  * head-dim size of each part (dims[2] = 0 for two axes). */
 PVJ_API pvj_status_t pvj_plan_rope_axes(const pvj_plan_t* plan, int32_t* n_axes, int32_t dims[3]);
 
+/* ---- projections with the modality pack / unpack fused in -----------------------
+ * Review page, "Native-Resolution MMDiT": each modality stream has its own
+ * projection layers; the tokens are concatenated only for the joint attention.
+ * Reading taken (the pages do not write the layer out): a linear layer with
+ * bias per stream, y = x W^T + b, W row-major [out_features, in_features] (the
+ * usual layout of a linear layer's weight), the QKV output ordered [Q | K | V]
+ * along the features and each part [H, D].  bf16 plans only; fp32
+ * accumulation, one rounding of each output.  hidden is a multiple of 64 in
+ * [64, 65536]; bias may be NULL.
+ *
+ * pvj_qkv_proj_pack: for the rows of one stream (x [rows, hidden], w
+ * [3 H D, hidden], bias [3 H D]) writes each token's Q, K and V straight into
+ * its joint row of q, k, v ([T, H, D]); with PVJ_FLAG_ROPE_FUSED the plan's
+ * RoPE is applied to Q and K before the rounding (the values pvj_pack_rope
+ * would produce from the projected streams, up to that rounding).  Calling it
+ * for both streams fills every joint row.
+ * pvj_out_proj_unpack: y [rows, hidden] = o_s W^T + b, where o_s are the
+ * stream's rows of the joint o [T, H, D] (w [hidden, H D], bias [hidden]).
+ */
+PVJ_API pvj_status_t pvj_qkv_proj_pack(const pvj_plan_t* plan, int32_t which, int32_t hidden,
+                                       const void* x, const void* w, const void* bias, void* q,
+                                       void* k, void* v, uint32_t flags, void* stream);
+PVJ_API pvj_status_t pvj_out_proj_unpack(const pvj_plan_t* plan, int32_t which, int32_t hidden,
+                                         const void* o, const void* w, const void* bias, void* y,
+                                         void* stream);
+
 /* ---- diagnostic: measured matrix-core ceiling -----------------------------------
  * Enqueues a kernel that keeps every SIMD issuing only independent
  * v_mfma_f32_32x32x16_bf16 (2 workgroups of 4 waves per CU, `rounds` times
@@ -318,7 +344,8 @@ enum {
   PVJ_KERNEL_ATTN_BWD_DQ = 6,
   PVJ_KERNEL_CHAIN_FWD = 7,        /* adaptive layer norm, gate + residual */
   PVJ_KERNEL_CHAIN_BWD = 8,        /* their backward passes */
-  PVJ_KERNEL_COUNT = 9
+  PVJ_KERNEL_PROJ = 9,             /* projections with the pack / unpack fused */
+  PVJ_KERNEL_COUNT = 10
 };
 PVJ_API pvj_status_t pvj_profile_enable(int32_t on);
 PVJ_API pvj_status_t pvj_profile_read(int32_t kernel, double* total_ms, int64_t* launches);

@@ -35,7 +35,7 @@ PVJ_FLAG_ROPE_FUSED = 1
 PVJ_FLAG_ROPE_PREROTATED = 2
 
 KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
-           "attn_bwd_dq": 6, "chain_fwd": 7, "chain_bwd": 8}
+           "attn_bwd_dq": 6, "chain_fwd": 7, "chain_bwd": 8, "proj": 9}
 STREAMS = {"text": 0, "image": 1}
 CHAIN_ADALN, CHAIN_GATE = 0, 1
 
@@ -108,6 +108,8 @@ def load_library():
         "pvj_chain_bwd_workspace": (I32, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
         "pvj_adaln_modulate_bwd": (I32, [P, I32, I32, P, P, P, P, P, P, F, P, SZ, P]),
         "pvj_gate_residual_bwd": (I32, [P, I32, I32, P, P, P, P, P, P, SZ, P]),
+        "pvj_qkv_proj_pack": (I32, [P, I32, I32, P, P, P, P, P, P, U32, P]),
+        "pvj_out_proj_unpack": (I32, [P, I32, I32, P, P, P, P, P]),
         "pvj_diag_mfma_peak": (I32, [I32, I32, P, SZ, ctypes.POINTER(ctypes.c_double), P]),
         "pvj_profile_enable": (I32, [I32]),
         "pvj_profile_read": (I32, [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
@@ -502,3 +504,43 @@ def diag_mfma_peak(rounds: int = 4, iters: int = 20000, reps: int = 3) -> float:
         if r > 0:
             best = max(best, flop.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     return best
+
+
+# ---------------------------------------------------------------------------
+# projections with the pack / unpack fused in (bf16 plans)
+# ---------------------------------------------------------------------------
+
+def qkv_proj_pack(plan: Plan, which: str, x, w, bias=None, q=None, k=None, v=None,
+                  rope: bool = True):
+    """Joint Q, K, V rows of one stream from x [rows, hidden] @ w[3HD, hidden]^T + bias
+    (RoPE on Q and K when ``rope``); pass the same q, k, v for both streams."""
+    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    hd = plan.n_heads * plan.head_dim
+    _check_2d("x", x, rows, hidden, plan.torch_dtype)
+    _check_2d("w", w, 3 * hd, hidden, plan.torch_dtype)
+    if bias is not None and (bias.dim() != 1 or bias.numel() != 3 * hd):
+        raise ValueError("bias must be [3 H D]")
+    q = _empty_tokens(plan, x) if q is None else q
+    k = _empty_tokens(plan, x) if k is None else k
+    v = _empty_tokens(plan, x) if v is None else v
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_tokens(plan, n, t)
+    _check(load_library().pvj_qkv_proj_pack(
+        plan.handle, STREAMS[which], hidden, _ptr(x), _ptr(w), _ptr(bias), _ptr(q), _ptr(k),
+        _ptr(v), PVJ_FLAG_ROPE_FUSED if rope else 0, _stream()))
+    return q, k, v
+
+
+def out_proj_unpack(plan: Plan, which: str, o, w, bias=None, y=None):
+    """y [rows, hidden] = (the stream's rows of the joint o) @ w[hidden, HD]^T + bias."""
+    rows, hidden = _stream_rows(plan, which), int(w.shape[0])
+    hd = plan.n_heads * plan.head_dim
+    _check_tokens(plan, "o", o)
+    _check_2d("w", w, hidden, hd, plan.torch_dtype)
+    if bias is not None and (bias.dim() != 1 or bias.numel() != hidden):
+        raise ValueError("bias must be [hidden]")
+    y = _torch().empty(rows, hidden, dtype=plan.torch_dtype, device=o.device) if y is None else y
+    _check_2d("y", y, rows, hidden, plan.torch_dtype)
+    _check(load_library().pvj_out_proj_unpack(plan.handle, STREAMS[which], hidden, _ptr(o),
+                                              _ptr(w), _ptr(bias), _ptr(y), _stream()))
+    return y

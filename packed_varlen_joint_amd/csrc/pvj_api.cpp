@@ -396,6 +396,61 @@ PVJ_API pvj_status_t pvj_gate_residual_bwd(const pvj_plan_t* p, int32_t which, i
                   "gate_residual_bwd");
 }
 
+// ---- projections with the pack / unpack fused ----------------------------------
+
+static pvj_status_t check_proj(const pvj_plan* p, int32_t which, int32_t hidden, int* rows) {
+  PVJ_TRY(check_plan(p));
+  if (p->desc.dtype != PVJ_BF16)
+    return fail(PVJ_ERR_UNSUPPORTED, "the fused projections take bf16 plans only");
+  if (which != PVJ_STREAM_TEXT && which != PVJ_STREAM_IMAGE)
+    return fail(PVJ_ERR_INVALID_ARG, "stream must be PVJ_STREAM_TEXT or PVJ_STREAM_IMAGE");
+  if (hidden < 64 || hidden % 64 || hidden > 65536)
+    return fail(PVJ_ERR_UNSUPPORTED, "hidden %d: need a multiple of 64 in [64, 65536]", hidden);
+  const int64_t hd = (int64_t)p->desc.n_heads * p->desc.head_dim;
+  const int64_t n = which == PVJ_STREAM_TEXT ? p->n_text : p->n_img;
+  const int64_t lim = int64_t(1) << 31;
+  // 32-bit byte offsets inside every operand
+  if ((n + 128) * hidden * 2 >= lim || (p->n_tokens + 128) * hd * 2 >= lim ||
+      3 * hd * hidden * 2 >= lim || (n + 128) * 3 * hd * 2 >= lim)
+    return fail(PVJ_ERR_UNSUPPORTED, "projection operands must stay below 2 GiB");
+  *rows = (int)n;
+  return PVJ_OK;
+}
+
+PVJ_API pvj_status_t pvj_qkv_proj_pack(const pvj_plan_t* p, int32_t which, int32_t hidden,
+                                       const void* x, const void* w, const void* bias, void* q,
+                                       void* k, void* v, uint32_t flags, void* stream) {
+  int rows = 0;
+  PVJ_TRY(check_proj(p, which, hidden, &rows));
+  PVJ_TRY(check_ptr(x, "x", rows > 0));
+  PVJ_TRY(check_ptr(w, "w", rows > 0));
+  if (bias) PVJ_TRY(check_ptr(bias, "bias", true));
+  PVJ_TRY(check_ptr(q, "q", rows > 0));
+  PVJ_TRY(check_ptr(k, "k", rows > 0));
+  PVJ_TRY(check_ptr(v, "v", rows > 0));
+  if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  KernelTimer t(PVJ_KERNEL_PROJ, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_qkv_proj(p, device_meta(p), which, hidden, x, w, bias, q, k, v,
+                                         (flags & PVJ_FLAG_ROPE_FUSED) != 0,
+                                         static_cast<hipStream_t>(stream))),
+                  "qkv_proj_pack");
+}
+
+PVJ_API pvj_status_t pvj_out_proj_unpack(const pvj_plan_t* p, int32_t which, int32_t hidden,
+                                         const void* o, const void* w, const void* bias, void* y,
+                                         void* stream) {
+  int rows = 0;
+  PVJ_TRY(check_proj(p, which, hidden, &rows));
+  PVJ_TRY(check_ptr(o, "o", rows > 0));
+  PVJ_TRY(check_ptr(w, "w", rows > 0));
+  if (bias) PVJ_TRY(check_ptr(bias, "bias", true));
+  PVJ_TRY(check_ptr(y, "y", rows > 0));
+  KernelTimer t(PVJ_KERNEL_PROJ, static_cast<hipStream_t>(stream));
+  return launched(t.done(launch_out_proj(p, device_meta(p), which, hidden, o, w, bias, y,
+                                         static_cast<hipStream_t>(stream))),
+                  "out_proj_unpack");
+}
+
 PVJ_API pvj_status_t pvj_diag_mfma_peak(int32_t rounds, int32_t iters, float* sink,
                                         size_t sink_floats, double* flop, void* stream) {
   if (rounds < 1 || rounds > 64 || iters < 1 || iters > (1 << 20))

@@ -44,6 +44,13 @@ hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, c
                            const void* gate, const void* dout, void* dy, float* dgate, int splits,
                            void* ws, hipStream_t stream);
 
+// projections with the pack / unpack fused (bf16): qkv writes joint Q, K, V rows
+// (RoPE on Q, K when rope), out reads the stream's rows from the joint O
+hipError_t launch_qkv_proj(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+                           const void* w, const void* bias, void* q, void* k, void* v, bool rope,
+                           hipStream_t stream);
+hipError_t launch_out_proj(const pvj_plan* p, const Meta& m, int which, int C, const void* o,
+                           const void* w, const void* bias, void* y, hipStream_t stream);
 // diagnostic: matrix-core-only kernel on every CU; *flop = its bf16 FLOP count
 hipError_t launch_mfma_peak(int rounds, int iters, float* sink, double* flop, hipStream_t stream);
 
