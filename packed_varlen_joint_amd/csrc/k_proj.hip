@@ -27,28 +27,41 @@
 
 namespace pvj {
 
-constexpr int kPjThreads = 256;
-constexpr int kPjBM = 128;   // tokens per workgroup
-constexpr int kPjBN = 128;   // output features per workgroup
 constexpr int kPjBK = 64;    // K per LDS stage
 constexpr int kPjG = 4;      // token blocks per XCD sharing a weight slice
-constexpr int kPjUnits = kPjBM * kPjBK / 8 / kPjThreads;  // 16-byte units per thread per tile
 
-// LDS slot of copy i of this lane: the tile is [128 rows][64] with the tsw<64>
+// Tile configuration: WAVES_N x WAVES_M waves, each owning NB x MB blocks of
+// 32 features x 32 tokens; the workgroup tile is (32 NB WAVES_N) features x
+// (32 MB WAVES_M) tokens.
+template <int WAVES_N, int WAVES_M, int NB, int MB>
+struct PjCfg {
+  static constexpr int WAVES = WAVES_N * WAVES_M;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BN = 32 * NB * WAVES_N;  // output features per workgroup
+  static constexpr int BM = 32 * MB * WAVES_M;  // tokens per workgroup
+  static constexpr int UW = BN * kPjBK / 8 / THREADS;  // 16-byte units per thread, W tile
+  static constexpr int UX = BM * kPjBK / 8 / THREADS;  // 16-byte units per thread, X tile
+  static constexpr int NB_ = NB, MB_ = MB, WAVES_M_ = WAVES_M;
+};
+typedef PjCfg<2, 4, 4, 2> PjBig;    // 256 x 256, 8 waves of 128 x 64
+
+// LDS slot of copy i of this lane: tiles are [rows][64] with the tsw<64>
 // swizzle, each copy instruction filling one wave's 64 consecutive slots
+template <int WAVES>
 __device__ __forceinline__ void pj_slot(int i, int wave, int lane, int& row, int& unit) {
-  const int slot = (i * (kPjThreads / 64) + wave) * 64 + lane;
+  const int slot = (i * WAVES + wave) * 64 + lane;
   row = slot / 8;
   unit = (slot % 8) ^ tsw<64>(row);
 }
 
+template <int WAVES, int UNITS>
 __device__ __forceinline__ void pj_copy(__amdgpu_buffer_rsrc_t r, const uint32_t* off, int wave,
                                         bf16* tile, uint32_t soff) {
 #pragma unroll
-  for (int i = 0; i < kPjUnits; ++i)
+  for (int i = 0; i < UNITS; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(tile + (i * (kPjThreads / 64) + wave) * 512),
-        16, off[i], soff, 0, 0);
+        r, (__attribute__((address_space(3))) void*)(tile + (i * WAVES + wave) * 512), 16, off[i],
+        soff, 0, 0);
 }
 
 // stream row m -> joint row (the stream's rows in sample order)
@@ -60,11 +73,13 @@ __device__ __forceinline__ int joint_row(const Meta& m, int which, int r, int& s
   return si.start + (which == 0 ? 0 : si.l_text) + (r - cu[s]);
 }
 
-template <int MODE, bool ROPE>
-__global__ __launch_bounds__(kPjThreads, 2) void proj_kernel(
+template <typename CF, int MODE, bool ROPE>
+__global__ __launch_bounds__(CF::THREADS) void proj_kernel(
     Meta m, int which, int M, int N, int K, const bf16* __restrict__ A,
     const bf16* __restrict__ W, const bf16* __restrict__ bias, bf16* __restrict__ out0,
     bf16* __restrict__ out1, bf16* __restrict__ out2, int a_rows_total) {
+  constexpr int kPjBN = CF::BN, kPjBM = CF::BM, NB = CF::NB_, MB = CF::MB_;
+  constexpr int WAVES = CF::WAVES, WM_N = CF::WAVES_M_;
   __shared__ __align__(16) bf16 w_b0[kPjBN * kPjBK], w_b1[kPjBN * kPjBK];
   __shared__ __align__(16) bf16 x_b0[kPjBM * kPjBK], x_b1[kPjBM * kPjBK];
 
@@ -80,15 +95,20 @@ __global__ __launch_bounds__(kPjThreads, 2) void proj_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int wn = wave >> 1, wm = wave & 1;  // this wave's 64 x 64 sub-tile
+  const int wn = wave / WM_N, wm = wave % WM_N;  // this wave's sub-tile
 
   // per-lane copy offsets (bytes), fixed for the whole K loop
-  uint32_t offw[kPjUnits], offx[kPjUnits];
+  uint32_t offw[CF::UW], offx[CF::UX];
 #pragma unroll
-  for (int i = 0; i < kPjUnits; ++i) {
+  for (int i = 0; i < CF::UW; ++i) {
     int row, unit;
-    pj_slot(i, wave, lane, row, unit);
+    pj_slot<WAVES>(i, wave, lane, row, unit);
     offw[i] = (uint32_t)(((size_t)(n0 + row) * K + unit * 8) * sizeof(bf16));
+  }
+#pragma unroll
+  for (int i = 0; i < CF::UX; ++i) {
+    int row, unit;
+    pj_slot<WAVES>(i, wave, lane, row, unit);
     const int r = m0 + row;
     if (MODE == 0) {
       offx[i] = (uint32_t)(((size_t)r * K + unit * 8) * sizeof(bf16));
@@ -104,52 +124,52 @@ __global__ __launch_bounds__(kPjThreads, 2) void proj_kernel(
       const_cast<bf16*>(A), (short)0,
       (int)((size_t)(MODE == 0 ? M : a_rows_total) * K * sizeof(bf16)), 0x00020000);
 
-  // operand read offsets (bytes) inside a tile: row (block*32 + l32), unit 2kk+hi
-  uint32_t ra[2][4], rb[2][4];
+  // operand read offsets (bytes) inside a tile: row (block*32 + l32), unit
+  // 2kk+hi; the blocks of a wave add whole 32-row steps (no swizzle change)
+  uint32_t ra[4], rb[4];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      ra[b][kk] = (uint32_t)(toff<64>(wn * 64 + b * 32 + l32, (2 * kk + hi) * 8) * sizeof(bf16));
-      rb[b][kk] = (uint32_t)(toff<64>(wm * 64 + b * 32 + l32, (2 * kk + hi) * 8) * sizeof(bf16));
-    }
+  for (int kk = 0; kk < 4; ++kk) {
+    ra[kk] = (uint32_t)(toff<64>(wn * 32 * NB + l32, (2 * kk + hi) * 8) * sizeof(bf16));
+    rb[kk] = (uint32_t)(toff<64>(wm * 32 * MB + l32, (2 * kk + hi) * 8) * sizeof(bf16));
+  }
 
-  f32x16 acc[2][2];
+  f32x16 acc[NB][MB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < MB; ++b) acc[a][b] = f32x16{};
 
   const int nk = K / kPjBK;
-  pj_copy(rw, offw, wave, w_b0, 0);
-  pj_copy(rx, offx, wave, x_b0, 0);
+  pj_copy<WAVES, CF::UW>(rw, offw, wave, w_b0, 0);
+  pj_copy<WAVES, CF::UX>(rx, offx, wave, x_b0, 0);
   wait_dma();
   __syncthreads();
   auto stage = [&](int ks, auto bc) {
     constexpr int B = decltype(bc)::value;
     if (ks + 1 < nk) {
       const uint32_t so = (uint32_t)((ks + 1) * kPjBK * sizeof(bf16));
-      pj_copy(rw, offw, wave, B ? w_b0 : w_b1, so);
-      pj_copy(rx, offx, wave, B ? x_b0 : x_b1, so);
+      pj_copy<WAVES, CF::UW>(rw, offw, wave, B ? w_b0 : w_b1, so);
+      pj_copy<WAVES, CF::UX>(rx, offx, wave, B ? x_b0 : x_b1, so);
     }
+    // keep the next stage's copies ahead of this stage's products (left to
+    // itself the scheduler sinks them to the stage end, exposing their latency)
+    __builtin_amdgcn_sched_barrier(0);
     const char* wt = reinterpret_cast<const char*>(B ? w_b1 : w_b0);
     const char* xt = reinterpret_cast<const char*>(B ? x_b1 : x_b0);
-    // all 16 operand reads of the stage first (in-order LDS returns let each
-    // product wait only for its own operands), then the 16 products
-    bf16x8 fa[4][2], fb[4][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 fa[NB], fb[MB];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        fa[kk][b] = *reinterpret_cast<const bf16x8*>(wt + ra[b][kk]);
-        fb[kk][b] = *reinterpret_cast<const bf16x8*>(xt + rb[b][kk]);
-      }
+      for (int a = 0; a < NB; ++a)
+        fa[a] = *reinterpret_cast<const bf16x8*>(wt + ra[kk] + a * 32 * 64 * sizeof(bf16));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+      for (int b = 0; b < MB; ++b)
+        fb[b] = *reinterpret_cast<const bf16x8*>(xt + rb[kk] + b * 32 * 64 * sizeof(bf16));
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < NB; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) mma16(acc[a][b], fa[kk][a], fb[kk][b]);
+        for (int b = 0; b < MB; ++b) mma16(acc[a][b], fa[a], fb[b]);
+    }
     wait_dma();
     __syncthreads();
   };
@@ -163,8 +183,8 @@ __global__ __launch_bounds__(kPjThreads, 2) void proj_kernel(
   // ---- epilogue: lane = token, 4-feature runs per register group ----
   const int HD = m.n_heads * m.head_dim;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int r = m0 + wm * 64 + b * 32 + l32;
+  for (int b = 0; b < MB; ++b) {
+    const int r = m0 + wm * 32 * MB + b * 32 + l32;
     if (r >= M) continue;
     int sample = 0;
     size_t orow;
@@ -177,10 +197,10 @@ __global__ __launch_bounds__(kPjThreads, 2) void proj_kernel(
       orow = (size_t)r * N;
     }
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NB; ++a)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + a * 32 + 8 * g + 4 * hi;
+        const int n = n0 + wn * 32 * NB + a * 32 + 8 * g + 4 * hi;
         if (n >= N) continue;
         float x[4];
 #pragma unroll
@@ -218,8 +238,9 @@ __global__ __launch_bounds__(kPjThreads, 2) void proj_kernel(
   }
 }
 
+template <typename CF>
 static int proj_grid(int M, int N) {
-  const int nM = (M + kPjBM - 1) / kPjBM, nN = (N + kPjBN - 1) / kPjBN;
+  const int nM = (M + CF::BM - 1) / CF::BM, nN = (N + CF::BN - 1) / CF::BN;
   const int per_band = kNumXcd * kPjG;
   const int bands = (nM + per_band - 1) / per_band;
   return bands * per_band * nN;
@@ -232,15 +253,16 @@ hipError_t launch_qkv_proj(const pvj_plan* p, const Meta& m, int which, int C, c
   const int N = 3 * m.n_heads * m.head_dim;
   if (M == 0) return hipSuccess;
   (void)p;
-  const dim3 g(proj_grid(M, N));
+  typedef PjBig CF;
+  const dim3 g(proj_grid<CF>(M, N));
   if (rope)
-    proj_kernel<0, true><<<g, kPjThreads, 0, st>>>(m, which, M, N, C, (const bf16*)x,
-                                                   (const bf16*)w, (const bf16*)bias, (bf16*)q,
-                                                   (bf16*)k, (bf16*)v, 0);
+    proj_kernel<CF, 0, true><<<g, CF::THREADS, 0, st>>>(m, which, M, N, C, (const bf16*)x,
+                                                        (const bf16*)w, (const bf16*)bias,
+                                                        (bf16*)q, (bf16*)k, (bf16*)v, 0);
   else
-    proj_kernel<0, false><<<g, kPjThreads, 0, st>>>(m, which, M, N, C, (const bf16*)x,
-                                                    (const bf16*)w, (const bf16*)bias, (bf16*)q,
-                                                    (bf16*)k, (bf16*)v, 0);
+    proj_kernel<CF, 0, false><<<g, CF::THREADS, 0, st>>>(m, which, M, N, C, (const bf16*)x,
+                                                         (const bf16*)w, (const bf16*)bias,
+                                                         (bf16*)q, (bf16*)k, (bf16*)v, 0);
   return hipGetLastError();
 }
 
@@ -250,10 +272,11 @@ hipError_t launch_out_proj(const pvj_plan* p, const Meta& m, int which, int C, c
   const int K = m.n_heads * m.head_dim;
   if (M == 0) return hipSuccess;
   (void)p;
-  const dim3 g(proj_grid(M, C));
-  proj_kernel<1, false><<<g, kPjThreads, 0, st>>>(m, which, M, C, K, (const bf16*)o,
-                                                  (const bf16*)w, (const bf16*)bias, (bf16*)y,
-                                                  nullptr, nullptr, m.n_tokens);
+  typedef PjBig CF;
+  const dim3 g(proj_grid<CF>(M, C));
+  proj_kernel<CF, 1, false><<<g, CF::THREADS, 0, st>>>(m, which, M, C, K, (const bf16*)o,
+                                                       (const bf16*)w, (const bf16*)bias,
+                                                       (bf16*)y, nullptr, nullptr, m.n_tokens);
   return hipGetLastError();
 }
 
