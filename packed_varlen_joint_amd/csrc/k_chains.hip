@@ -8,16 +8,22 @@
 //    (LayerNorm without affine, population variance); one wave per row, the
 //    row held in registers (two-pass mean / variance in fp32).
 //  * gate_fwd: out = x + gate_i * y, one wave per row.
-//  * adaln_bwd_rows: dx = r (g - mean(g) - xhat mean(g xhat)), g = dy (1 +
-//    scale_i), and the row's mean and 1/std for the reduction below.
-//  * seg_partial / seg_final: the per-sample parameter gradients (dshift =
-//    sum dy, dscale = sum dy xhat, dgate = sum dout y) as deterministic
-//    column sums: every sample's rows are cut into `splits` fixed ranges
-//    (about 32 rows each for the stream's longest sample, so the reduction
-//    fills the chip), one wave per (sample, range, 512-column chunk) writes a
-//    partial sum with four rows in flight, and the final pass adds the
-//    partials in a fixed order.  The gate backward's
-//    dy = gate_i * dout is written by the same pass.
+//  * adaln_bwd (rows up to 3072 columns): one pass per row range.  Each wave
+//    owns R consecutive rows of one sample (R sized so the stream's waves
+//    fill the chip) and, per row, computes dx = r (g - mean(g) - xhat
+//    mean(g xhat)) with g = dy (1 + scale_i), while it keeps the per-sample
+//    parameter gradients' column sums (dshift = sum dy, dscale = sum dy xhat)
+//    for its rows in registers; it writes them as one partial per wave, so x
+//    and dy are read once.  Sample i owns partial slots cu_i / R + i ..
+//    + ceil(L_i / R) - 1 (disjoint, increasing), and seg_final_slots adds a
+//    sample's partials in a fixed order.
+//  * wider rows, and the gate backward: adaln_bwd_rows writes dx and the
+//    row's mean and 1/std; the column sums (dshift, dscale; dgate = sum dout
+//    y, with dy = gate_i * dout written by the same pass) come from
+//    seg_partial, where every sample's rows are cut into `splits`
+//    fixed ranges (about 32 rows each for the stream's longest sample), one
+//    wave per (sample, range, 512-column chunk) writes a partial sum with four
+//    rows in flight, and seg_final adds the partials in a fixed order.
 // A row's sample i is found by binary search in the stream's cumulative
 // offsets (cu_text or cu_img of the plan).
 
@@ -31,10 +37,21 @@ constexpr int kColChunk = 512;         // columns per reduction wave (8 per lane
 constexpr int kRowsPerSplit = 32;      // target rows per reduction wave
 constexpr int kMaxSplit = 256;
 
+// sum over the wave, in every lane, without LDS round trips: DPP within
+// quads, 8- and 16-lane rows, then the 16- and 32-lane swaps of gfx950
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int w = 1; w < 64; w <<= 1) v += __shfl_xor(v, w, 64);
-  return v;
+  v += dpp<0xB1>(v);   // quad_perm 1,0,3,2
+  v += dpp<0x4E>(v);   // quad_perm 2,3,0,1
+  v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8 lanes
+  v += dpp<0x140>(v);  // row_mirror: the other 8 lanes of each 16
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  return sum_pair32(v);
 }
 
 template <typename T>
@@ -51,14 +68,21 @@ __global__ __launch_bounds__(kChainThreads) void adaln_fwd_kernel(
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   const int upr = C / 8;
-  const int s = find_sample(cu, n_samples, row);
+  // the row's loads go out before the sample lookup (a chain of dependent loads)
   const T* xr = x + (size_t)row * C;
+  typename Vec8<T>::type xv[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    typename Vec8<T>::type z = {};
+    xv[k] = u < upr ? load8<T>(xr + u * 8) : z;
+  }
+  const int s = find_sample(cu, n_samples, row);
   f32x8 v[NU];
   float sum = 0.f;
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
-    const int u = lane + 64 * k;
-    v[k] = u < upr ? ld8f(xr + u * 8) : f32x8{};
+    v[k] = to_f32x8(xv[k]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum += v[k][e];
   }
@@ -103,11 +127,19 @@ __global__ __launch_bounds__(kChainThreads) void gate_fwd_kernel(
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   const int upr = C / 8;
-  const int s = find_sample(cu, n_samples, row);
   const size_t ro = (size_t)row * C;
+  // first unit of x and y before the sample lookup (a chain of dependent loads)
+  typename Vec8<T>::type x0 = {}, y0 = {};
+  if (lane < upr) {
+    x0 = load8<T>(x + ro + lane * 8);
+    y0 = load8<T>(y + ro + lane * 8);
+  }
+  const int s = find_sample(cu, n_samples, row);
   const T* g = gate + (size_t)s * C;
   for (int u = lane; u < upr; u += 64) {
-    const f32x8 a = ld8f(x + ro + u * 8), b = ld8f(y + ro + u * 8), w = ld8f(g + u * 8);
+    const f32x8 a = u == lane ? to_f32x8(x0) : ld8f(x + ro + u * 8);
+    const f32x8 b = u == lane ? to_f32x8(y0) : ld8f(y + ro + u * 8);
+    const f32x8 w = ld8f(g + u * 8);
     f32x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = a[e] + w[e] * b[e];
@@ -183,6 +215,161 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_rows_kernel(
     }
   }
   if (lane == 0) stats[row] = make_float2(mean, rstd);
+}
+
+// ---------------------------------------------------------------------------
+// backward: adaptive layer norm, one pass (dx and the partial column sums)
+// ---------------------------------------------------------------------------
+// first partial slot of sample i (rows per wave R)
+__device__ __forceinline__ int slot_base(const int32_t* cu, int i, int R) { return cu[i] / R + i; }
+
+// the rows [r0, r1) of partial slot `slot` and their sample i (empty when the
+// slot lies past its sample's rows; such slots are never read)
+__device__ __forceinline__ void slot_rows(const int32_t* cu, int n_samples, int R, int slot, int& i,
+                                          int& r0, int& r1) {
+  int lo = 0, hi = n_samples - 1;  // the last i with slot_base(i) <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_base(cu, mid, R) <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  i = lo;
+  r0 = cu[i] + (slot - slot_base(cu, i, R)) * R;
+  r1 = min(r0 + R, cu[i + 1]);
+}
+
+template <typename T, int NU>
+__global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int C, int R, int n_slots,
+    const T* __restrict__ x, const T* __restrict__ scale, const T* __restrict__ dy,
+    T* __restrict__ dx, float* __restrict__ partial, float eps) {
+  typedef typename Vec8<T>::type V8;
+  const int slot = blockIdx.x * (kChainThreads / 64) + (threadIdx.x >> 6);
+  if (slot >= n_slots) return;
+  int i, r0, r1;
+  slot_rows(cu, n_samples, R, slot, i, r0, r1);
+  if (r0 >= r1) return;
+  const int lane = threadIdx.x & 63;
+  const int upr = C / 8;
+  const float inv_c = 1.f / C;
+  V8 sc[NU];  // scale_i of this lane's columns
+  f32x8 acc0[NU], acc1[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    V8 z = {};
+    sc[k] = u < upr ? load8<T>(scale + (size_t)i * C + u * 8) : z;
+    acc0[k] = f32x8{};
+    acc1[k] = f32x8{};
+  }
+  // the next row's x and dy are loaded while this row is computed
+  V8 xn[NU], dn[NU];
+  auto fetch = [&](int r) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = lane + 64 * k;
+      V8 z = {};
+      xn[k] = u < upr ? load8<T>(x + (size_t)r * C + u * 8) : z;
+      dn[k] = u < upr ? load8<T>(dy + (size_t)r * C + u * 8) : z;
+    }
+  };
+  fetch(r0);
+  for (int r = r0; r < r1; ++r) {
+    const size_t ro = (size_t)r * C;
+    f32x8 v[NU];
+    V8 d[NU];
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      v[k] = to_f32x8(xn[k]);
+      d[k] = dn[k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += v[k][e];
+    }
+    if (r + 1 < r1) fetch(r + 1);
+    const float mean = wave_sum(sum) * inv_c;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = lane + 64 * k;
+      if (u < upr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = v[k][e] - mean;
+          ss += t * t;
+        }
+      }
+    }
+    const float rstd = 1.0f / __builtin_sqrtf(wave_sum(ss) * inv_c + eps);
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = lane + 64 * k;
+      if (u < upr) {
+        const f32x8 dd = to_f32x8(d[k]), a = to_f32x8(sc[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[k][e] = (v[k][e] - mean) * rstd;  // xhat from here on
+          const float g = dd[e] * (1.f + a[e]);
+          sg += g;
+          sgx += g * v[k][e];
+          acc0[k][e] += dd[e];
+          acc1[k][e] += dd[e] * v[k][e];
+        }
+      }
+    }
+    const float mg = wave_sum(sg) * inv_c, mgx = wave_sum(sgx) * inv_c;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = lane + 64 * k;
+      if (u < upr) {
+        const f32x8 dd = to_f32x8(d[k]), a = to_f32x8(sc[k]);
+        f32x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rstd * (dd[e] * (1.f + a[e]) - mg - v[k][e] * mgx);
+        store8<T>(dx + ro + u * 8, from_f32x8<T>(o));
+      }
+    }
+  }
+  float* p0 = partial + (size_t)slot * 2 * C;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = lane + 64 * k;
+    if (u < upr) {
+      *reinterpret_cast<f32x8*>(p0 + u * 8) = acc0[k];
+      *reinterpret_cast<f32x8*>(p0 + C + u * 8) = acc1[k];
+    }
+  }
+}
+
+// final pass over partial slots: 4 waves per (kind, sample, column chunk);
+// wave w adds the sample's slots w, w+4, ..., then wave 0 adds the four wave
+// sums in order (a fixed order: deterministic).  Slot layout [slot][kind][C].
+__global__ __launch_bounds__(256) void seg_final_slots_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int C, int R, int kinds,
+    const float* __restrict__ partial, float* __restrict__ out0, float* __restrict__ out1) {
+  __shared__ f32x8 red[3][64];
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int s = (blockIdx.x / nchunk) % n_samples;
+  const int kind = blockIdx.x / (nchunk * n_samples);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = chunk * kColChunk + lane * 8;
+  const bool active = col < C;
+  const int nsl = (cu[s + 1] - cu[s] + R - 1) / R;
+  f32x8 acc = {};
+  if (active) {
+    const float* p = partial + ((size_t)slot_base(cu, s, R) * kinds + kind) * C + col;
+    for (int k = wave; k < nsl; k += 4) acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * kinds * C);
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && active) {
+    acc += red[0][lane];
+    acc += red[1][lane];
+    acc += red[2][lane];
+    *reinterpret_cast<f32x8*>((kind ? out1 : out0) + (size_t)s * C + col) = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -285,10 +472,27 @@ int chain_splits(int max_sample_rows) {
   return s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
 }
 
+// units per lane for a row of C columns (C / 8 units over 64 lanes)
+static int units_per_lane(int C) { return (C / 8 + 63) / 64; }
+
+// the one-pass adaptive-layer-norm backward holds the column sums of a lane
+// in registers: rows up to 3072 columns
+static bool one_pass(int C) { return units_per_lane(C) <= 6; }
+
+// rows per wave of the one-pass backward: about 8 waves per CU over the
+// stream, at least 8 and at most 64 rows each
+static int rows_per_wave(int rows) {
+  const int r = rows / (256 * 8);
+  return r < 8 ? 8 : (r > 64 ? 64 : r);
+}
+static int n_slots(int rows, int n_samples, int R) { return rows / R + n_samples + 1; }
+
 size_t chain_workspace_bytes(int n_samples, int C, int rows, int mode, int splits) {
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  if (mode == 0 && one_pass(C))
+    return al((size_t)n_slots(rows, n_samples, rows_per_wave(rows)) * 2 * C * sizeof(float));
   const size_t part = (size_t)(mode == 0 ? 2 : 1) * n_samples * splits * C * sizeof(float);
   const size_t st = mode == 0 ? (size_t)rows * sizeof(float2) : 0;
-  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
   return al(part) + al(st);
 }
 
@@ -299,6 +503,14 @@ static void adaln_fwd_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int ro
                                                        (const T*)scale, (T*)y, eps);
 }
 template <typename T, int NU>
+static void adaln_bwd_1p_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int C, int R, int ns,
+                           const void* x, const void* scale, const void* dy, void* dx,
+                           float* partial, float eps) {
+  adaln_bwd_kernel<T, NU><<<g, kChainThreads, 0, st>>>(cu, B, C, R, ns, (const T*)x,
+                                                       (const T*)scale, (const T*)dy, (T*)dx,
+                                                       partial, eps);
+}
+template <typename T, int NU>
 static void adaln_bwd_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int rows, int C,
                         const void* x, const void* scale, const void* dy, void* dx, float2* stats,
                         float eps) {
@@ -306,8 +518,14 @@ static void adaln_bwd_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int ro
       cu, B, rows, C, (const T*)x, (const T*)scale, (const T*)dy, (T*)dx, stats, eps);
 }
 
-// units per lane for a row of C columns (C / 8 units over 64 lanes)
-static int units_per_lane(int C) { return (C / 8 + 63) / 64; }
+#define PVJ_NU_DISPATCH6(FN, T, ...)                 \
+  do {                                               \
+    const int nu = units_per_lane(C);                \
+    if (nu <= 1) FN<T, 1>(__VA_ARGS__);              \
+    else if (nu <= 2) FN<T, 2>(__VA_ARGS__);         \
+    else if (nu <= 4) FN<T, 4>(__VA_ARGS__);         \
+    else FN<T, 6>(__VA_ARGS__);                      \
+  } while (0)
 
 #define PVJ_NU_DISPATCH(FN, T, ...)                  \
   do {                                               \
@@ -358,10 +576,27 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
   const int B = m.n_samples;
   if (B == 0) return hipSuccess;
   const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  const bool bf = p->desc.dtype == PVJ_BF16;
+  if (one_pass(C)) {
+    const int R = rows_per_wave(rows), ns = n_slots(rows, B, R);
+    float* partial = static_cast<float*>(ws);
+    if (rows > 0) {
+      const dim3 g((ns + 3) / 4);
+      if (bf)
+        PVJ_NU_DISPATCH6(adaln_bwd_1p_t, bf16, g, st, cu, B, C, R, ns, x, scale, dy, dx, partial,
+                         eps);
+      else
+        PVJ_NU_DISPATCH6(adaln_bwd_1p_t, float, g, st, cu, B, C, R, ns, x, scale, dy, dx, partial,
+                         eps);
+    }
+    const int nchunk = (C + kColChunk - 1) / kColChunk;
+    seg_final_slots_kernel<<<2 * B * nchunk, 256, 0, st>>>(cu, B, C, R, 2, partial, dshift,
+                                                            dscale);
+    return hipGetLastError();
+  }
   const size_t part = (size_t)2 * B * splits * C * sizeof(float);
   float* partial = static_cast<float*>(ws);
   float2* stats = reinterpret_cast<float2*>(static_cast<char*>(ws) + (part + 255) / 256 * 256);
-  const bool bf = p->desc.dtype == PVJ_BF16;
   if (rows > 0) {
     const dim3 g((rows + 3) / 4);
     if (bf)
