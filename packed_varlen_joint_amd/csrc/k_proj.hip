@@ -13,7 +13,7 @@
 // operand is a tile of W rows (output features), the B operand a tile of
 // token rows, so every lane owns one token and its registers hold runs of 4
 // consecutive output features (the RoPE pairs are lane-local).  Workgroup
-// tile 128 features x 128 tokens, 4 waves of 64 x 64, K in stages of 64
+// tile 256 features x 256 tokens, 8 waves of 128 x 64, K in stages of 64
 // through double-buffered LDS filled by direct buffer copies (per-lane byte
 // offsets fixed once, the stage as an SGPR offset, rows past the end outside
 // the buffer resource and read as zeros).  Tile order: each XCD keeps its
@@ -156,19 +156,31 @@ __global__ __launch_bounds__(CF::THREADS) void proj_kernel(
     __builtin_amdgcn_sched_barrier(0);
     const char* wt = reinterpret_cast<const char*>(B ? w_b1 : w_b0);
     const char* xt = reinterpret_cast<const char*>(B ? x_b1 : x_b0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 fa[NB], fb[MB];
+    // operand fragments double-buffered over the four k-steps: the reads of
+    // step kk + 1 are issued ahead of the products of step kk
+    bf16x8 fa[2][NB], fb[2][MB];
+    auto frags = [&](int kk, bf16x8 (&a_)[NB], bf16x8 (&b_)[MB]) {
 #pragma unroll
       for (int a = 0; a < NB; ++a)
-        fa[a] = *reinterpret_cast<const bf16x8*>(wt + ra[kk] + a * 32 * 64 * sizeof(bf16));
+        a_[a] = *reinterpret_cast<const bf16x8*>(wt + ra[kk] + a * 32 * 64 * sizeof(bf16));
 #pragma unroll
       for (int b = 0; b < MB; ++b)
-        fb[b] = *reinterpret_cast<const bf16x8*>(xt + rb[kk] + b * 32 * 64 * sizeof(bf16));
+        b_[b] = *reinterpret_cast<const bf16x8*>(xt + rb[kk] + b * 32 * 64 * sizeof(bf16));
+    };
+    frags(0, fa[0], fb[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
       for (int a = 0; a < NB; ++a)
 #pragma unroll
-        for (int b = 0; b < MB; ++b) mma16(acc[a][b], fa[a], fb[b]);
+        for (int b = 0; b < MB; ++b) mma16(acc[a][b], fa[kk & 1][a], fb[kk & 1][b]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);
     }
     wait_dma();
     __syncthreads();
