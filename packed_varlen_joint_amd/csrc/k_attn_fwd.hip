@@ -240,17 +240,18 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
           if (key >= L) s[kb][r] = -INFINITY;
         }
     }
-    // online softmax (base 2); max and sum as short independent chains
+    // online softmax (base 2); max and sum as short independent chains (the
+    // maxima associated so that they become three-input v_max3_f32)
     float mx4[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      mx4[c] = fmaxf(fmaxf(s[c >> 1][8 * (c & 1)], s[c >> 1][8 * (c & 1) + 1]),
-                     fmaxf(s[c >> 1][8 * (c & 1) + 2], s[c >> 1][8 * (c & 1) + 3]));
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 4; r < 8; ++r) mx4[c] = fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    for (int c = 0; c < 4; ++c) {
+      float t = fmaxf(fmaxf(s[c >> 1][8 * (c & 1)], s[c >> 1][8 * (c & 1) + 1]),
+                      s[c >> 1][8 * (c & 1) + 2]);
+      t = fmaxf(fmaxf(t, s[c >> 1][8 * (c & 1) + 3]), s[c >> 1][8 * (c & 1) + 4]);
+      t = fmaxf(fmaxf(t, s[c >> 1][8 * (c & 1) + 5]), s[c >> 1][8 * (c & 1) + 6]);
+      mx4[c] = fmaxf(t, s[c >> 1][8 * (c & 1) + 7]);
+    }
+    float mx = fmaxf(fmaxf(fmaxf(mx4[0], mx4[1]), mx4[2]), mx4[3]);
     mx = max_pair32(mx) * scale_log2;
     // Rescale only when some query's max grew by more than 2^8: otherwise keep
     // the stale reference max (p <= 256, far from overflow).  O / l is exact
