@@ -20,10 +20,11 @@
 //  * wider rows, and the gate backward: adaln_bwd_rows writes dx and the
 //    row's mean and 1/std; the column sums (dshift, dscale; dgate = sum dout
 //    y, with dy = gate_i * dout written by the same pass) come from
-//    seg_partial, where every sample's rows are cut into `splits`
-//    fixed ranges (about 32 rows each for the stream's longest sample), one
-//    wave per (sample, range, 512-column chunk) writes a partial sum with four
-//    rows in flight, and seg_final adds the partials in a fixed order.
+//    seg_partial, where every sample's rows are cut into `splits` fixed
+//    ranges (about 16 rows each for the stream's longest sample, at most 256
+//    ranges), one wave per (sample, range, 512-column chunk) writes a partial
+//    sum with four rows in flight, and seg_final adds the partials in a fixed
+//    order.
 // A row's sample i is found by binary search in the stream's cumulative
 // offsets (cu_text or cu_img of the plan).
 
@@ -34,7 +35,7 @@ namespace pvj {
 
 constexpr int kChainThreads = 256;     // 4 waves, one row each
 constexpr int kColChunk = 512;         // columns per reduction wave (8 per lane)
-constexpr int kRowsPerSplit = 32;      // target rows per reduction wave
+constexpr int kRowsPerSplit = 16;      // target rows per reduction wave
 constexpr int kMaxSplit = 256;
 
 // sum over the wave, in every lane, without LDS round trips: DPP within
