@@ -46,7 +46,7 @@ def _src_hash(*names):
 KERNEL_SOURCES = {
     "attn_fwd": ("k_attn_fwd.hip", "pvj_device.h"),
     "attn_bwd": ("k_attn_bwd.hip", "pvj_device.h"),
-    "attn_bwd_dq": ("k_attn_bwd.hip", "pvj_device.h"),
+    "attn_bwd_dq": ("k_attn_dq.hip", "pvj_device.h"),
 }
 
 

@@ -1,0 +1,300 @@
+// Packed variable-length joint attention, backward dQ pass, for gfx950.
+//
+// Gradient of sum(O * dO) with respect to Q, per sample and head (Mage-Flow
+// review page, section "Kernel fusion": training runs forward + backward
+// through the joint attention):
+//   P = exp(s Q'K'^T - LSE); dP = dO V^T; dS = P * (dP - Delta);
+//   dQ' = s dS K'; with RoPE, dQ = R^T dQ'.
+//
+// attn_bwd_dq_kernel: one workgroup per (sample, head, 128-query tile);
+// 4 waves x 32 queries with Q' and dO in registers; streams 64-key tiles of
+// K' and V through double-buffered LDS like the forward.  S^T = K'Q'^T and
+// dP^T = V dO^T put one query per lane (LSE and Delta are per-lane scalars);
+// dQ'^T += K'^T dS^T takes dS^T straight from the accumulators and K'^T by
+// transposing reads.  The epilogue scales, applies R^T (rotation pairs are in
+// one lane) and stores dQ in the output dtype.  No atomics: each dQ row is
+// written by exactly one workgroup.
+
+#include <type_traits>
+
+#include "pvj_device.h"
+#include "pvj_launch.h"
+
+namespace pvj {
+
+constexpr int kDqBM = 128;  // queries per dQ workgroup (= forward tile, uses fwd_items)
+constexpr int kDqBN = 64;   // keys per streamed tile
+constexpr int kDqThreads = kTileThreads;
+
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int UPR = D / 8;
+  static constexpr int NK = kDqBN * UPR / kDqThreads;  // units per thread per tile (K and V)
+  static constexpr int TILE = kDqBN * D;
+};
+
+// bf16 fits two waves per SIMD (two workgroups per CU, 64 KB of LDS each)
+template <typename T, int D>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(
+    sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_bwd_dq_kernel(
+    Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
+    T* __restrict__ dQ, float scale, float scale_log2, int rope) {
+  typedef typename Vec8<T>::type V8;
+  typedef DqCfg<T, D> C;
+  constexpr int KS = D / 16, DB = D / 32, UPR = C::UPR, NK = C::NK;
+
+  // separate static buffers (see the dK/dV kernel)
+  __shared__ __align__(16) T k_b0[C::TILE], k_b1[C::TILE], v_b0[C::TILE], v_b1[C::TILE];
+  auto ks_of = [&](int b) { return b ? k_b1 : k_b0; };
+  auto vs_of = [&](int b) { return b ? v_b1 : v_b0; };
+
+  const Item it = m.fwd_items[blockIdx.x];
+  if (it.sample < 0) return;
+  const SampleInfo si = m.sinfo[it.sample];
+  const int L = si.len;
+  const size_t RS = (size_t)m.n_heads * D;
+  const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qi = it.tile * kDqBM + wave * 32 + l32;  // this lane's query
+
+  V8 qf[KS], gf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int unit = 2 * ks + hi;
+    V8 z = {};
+    qf[ks] = qi < L ? load8<T>(Q + base + (size_t)qi * RS + unit * 8) : z;
+    gf[ks] = qi < L ? load8<T>(dO + base + (size_t)qi * RS + unit * 8) : z;
+  }
+  const float lse2 = qi < L ? LSE[(size_t)it.head * m.n_tokens + si.start + qi] *
+                                  1.4426950408889634f : INFINITY;
+  const float delta = qi < L ? DELTA[(size_t)it.head * m.n_tokens + si.start + qi] : 0.f;
+
+  const int k_unit = tid % UPR;
+  const int k_row0 = tid / UPR;
+  constexpr int K_ROW_STEP = kDqThreads / UPR;
+  constexpr bool DMA = sizeof(T) == 2;
+  V8 kreg[DMA ? 1 : NK], vreg[DMA ? 1 : NK];
+  // direct copies (K and V tiles share one layout; rows past the end are zeros)
+  typedef DmaTile<D, kDqBN> DT;
+  const DT dma(RS);
+  const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
+  auto load_kv = [&](int kv0, int b) {
+    if constexpr (DMA) {
+      dma.copy(ks_of(b), rk, RS, kv0);
+      dma.copy(vs_of(b), rv, RS, kv0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int kk = kv0 + k_row0 + i * K_ROW_STEP;
+        V8 z = {};
+        kreg[i] = kk < L ? load8<T>(K + base + (size_t)kk * RS + k_unit * 8) : z;
+        vreg[i] = kk < L ? load8<T>(V + base + (size_t)kk * RS + k_unit * 8) : z;
+      }
+    }
+  };
+  auto store_kv = [&](int b) {
+    if constexpr (DMA) {
+      wait_dma();
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int rho = bsigma(k_row0 + i * K_ROW_STEP);
+        store8<T>(ks_of(b) + toff<D>(rho, k_unit * 8), kreg[i]);
+        store8<T>(vs_of(b) + toff<D>(rho, k_unit * 8), vreg[i]);
+      }
+    }
+  };
+  auto sig = [](int k) { return bsigma(k); };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  // Per-lane LDS addresses, fixed for the whole loop (bf16): row l32 at unit
+  // 2kk+hi of the K and V tiles (same layout), and the K^T fragment bases of
+  // output block db and half t; the 32-key block, the 16-key half and the
+  // buffer add compile-time offsets.  The empty asm keeps them in registers.
+  uint32_t ka[KS], va[DB][2];
+  if constexpr (DMA) {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      ka[kk] = (uint32_t)(toff<D>(l32, (2 * kk + hi) * 8) * sizeof(T));
+      asm volatile("" : "+v"(ka[kk]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        va[db][t] = (uint32_t)(toff<D>(bsigma(8 * (g >> 1) + 4 * t + (sl >> 2)),
+                                       db * 32 + 16 * (g & 1) + 4 * (sl & 3)) * sizeof(T));
+        asm volatile("" : "+v"(va[db][t]));
+      }
+  }
+
+  const int nkv = (L + kDqBN - 1) / kDqBN;
+  load_kv(0, 0);
+  store_kv(0);
+  __syncthreads();
+  auto step = [&](int j, auto bc, auto mc) {
+    constexpr int B = decltype(bc)::value;
+    constexpr bool MASK = decltype(mc)::value;
+    const int kv0 = j * kDqBN;
+    if (j + 1 < nkv) load_kv(kv0 + kDqBN, B ^ 1);
+    const T* ks = B ? k_b1 : k_b0;
+    const T* vs = B ? v_b1 : v_b0;
+    V8 sfr[2][2];  // dS^T fragments [32-key block][16-key step]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // the products run at raised wave priority: the SIMD's other wave (another
+      // workgroup) then fills the gaps with its softmax work instead of
+      // delaying these matrix-core issues
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 s = {}, dp = {};
+      const int rho = kb * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        V8 kf, vf;
+        if constexpr (DMA) {
+          const uint32_t o = ka[kk] + kb * 32 * D * sizeof(T);
+          kf = *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(ks) + o);
+          vf = *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(vs) + o);
+        } else {
+          const int off = toff<D>(rho, (2 * kk + hi) * 8);
+          kf = load8<T>(ks + off);
+          vf = load8<T>(vs + off);
+        }
+        mma16(s, kf, qf[kk]);
+        mma16(dp, vf, gf[kk]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+        // the last tile's rows past the sample end read as zeros: zero weight
+        if constexpr (MASK)
+          if (kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7) >= L) p = 0.f;
+        sfr[kb][r >> 3][r & 7] = (T)(p * (dp[r] - delta));
+      }
+    }
+    // dQ'^T += K'^T dS^T
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          V8 kt;
+          if constexpr (DMA) {
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const uint32_t o = (uint32_t)((kb * 32 + 16 * st) * D * sizeof(T));
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(reinterpret_cast<const char*>(ks) + va[db][t] + o));
+              const bf16x4 h = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) kt[4 * t + e] = h[e];
+            }
+          } else {
+            kt = frag_t<D>(ks, kb * 32 + 16 * st, db * 32, sig);
+          }
+          mma16(acc[db], kt, sfr[kb][st]);
+        }
+    __builtin_amdgcn_s_setprio(0);
+    if (j + 1 < nkv) store_kv(B ^ 1);
+    __syncthreads();
+  };
+  // full tiles in pairs (buffers 0, 1), a leftover full tile, then the
+  // partial tile with the key mask
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<bool, false> NoMask;
+  typedef std::integral_constant<bool, true> Mask;
+  const int nfull = L / kDqBN;
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    step(j, B0{}, NoMask{});
+    step(j + 1, B1{}, NoMask{});
+  }
+  if (j < nfull) {
+    step(j, B0{}, NoMask{});
+    ++j;
+  }
+  if (j < nkv) {
+    if (j & 1) step(j, B1{}, Mask{});
+    else step(j, B0{}, Mask{});
+  }
+
+  // ---- epilogue: dQ = R^T (s dQ'); lane holds query qi, d = 32db + 8g + 4hi + e ----
+  if (qi < L) {
+    const RopePos qp = rope ? token_pos3(qi, si) : RopePos{0, 0, 0};
+    T* row = dQ + base + (size_t)qi * RS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hi;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * scale;
+        if (rope) {
+          // pairs (d0, d0+1), (d0+2, d0+3) of unit d0 / 8
+          const size_t to =
+              (size_t)axis_pos(qp, unit_axis(d0 >> 3, m)) * m.n_pairs + (d0 >> 1);
+          const f32x2 cs = *reinterpret_cast<const f32x2*>(m.cos_tab + to);
+          const f32x2 sn = *reinterpret_cast<const f32x2*>(m.sin_tab + to);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float a = x[2 * q], bb = x[2 * q + 1];
+            x[2 * q] = a * cs[q] + bb * sn[q];        // rotate by -angle
+            x[2 * q + 1] = -a * sn[q] + bb * cs[q];
+          }
+        }
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)x[e];
+          *reinterpret_cast<bf16x4*>(row + d0) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = x[e];
+          *reinterpret_cast<f32x4*>(row + d0) = w;
+        }
+      }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_dq_t(const Meta& m, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const float* delta, void* dq,
+                              float scale, bool rope, hipStream_t stream) {
+  if (m.n_fwd > 0)
+    attn_bwd_dq_kernel<T, D><<<dim3(m.n_fwd), dim3(kDqThreads), 0, stream>>>(
+        m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
+        scale * 1.4426950408889634f, rope ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq(const pvj_plan* p, const Meta& m, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, float scale, bool rope,
+                              hipStream_t stream) {
+  const bool bf = p->desc.dtype == PVJ_BF16;
+  const int D = p->desc.head_dim;
+#define PVJ_DQ(TT, DD) \
+  return launch_dq_t<TT, DD>(m, q, k, v, dout, lse, delta, dq, scale, rope, stream)
+  if (bf && D == 128) PVJ_DQ(bf16, 128);
+  if (bf && D == 64) PVJ_DQ(bf16, 64);
+  if (!bf && D == 128) PVJ_DQ(float, 128);
+  PVJ_DQ(float, 64);
+#undef PVJ_DQ
+}
+
+}  // namespace pvj

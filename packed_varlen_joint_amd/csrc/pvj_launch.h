@@ -26,6 +26,11 @@ hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const vo
                            const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dq, void* dk, void* dv, float scale,
                            bool rope, hipStream_t stream);
+// the dQ kernel alone (launch_attn_bwd with which = 1 calls it)
+hipError_t launch_attn_bwd_dq(const pvj_plan* p, const Meta& m, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, float scale, bool rope,
+                              hipStream_t stream);
 
 // memory-bound chains on one stream (which: 0 text, 1 image) of C columns
 // row ranges per sample of the per-sample reductions, from the stream's
