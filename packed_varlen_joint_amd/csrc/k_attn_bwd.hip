@@ -227,13 +227,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
       mma16(s, rowfrag(qs, ks), kf[ks]);
       mma16(dp, rowfrag(gs, ks), vfrag(ks));
     }
-    // keep six operand reads in flight ahead of the products
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
   };
   // P = 2^(s*scale*log2e - LSE*log2e) and dS = P (dP - Delta) for element r
   // (query 16(r/8) + 8 hi + r%8) into the A fragments of dV and dK
@@ -266,8 +259,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
     const T* qs = B ? q_b1 : q_b0;
     const T* gs = B ? g_b1 : g_b0;
     const float* lb = B ? l_b1 : l_b0;
-    // the matrix phases run at raised wave priority: the SIMD's other wave
-    // (another workgroup) fills their gaps with its softmax work
+    // S and dP run at raised wave priority, so the SIMD's other wave (another
+    // workgroup) fills their gaps with its softmax and dV/dK work (measured:
+    // raising it for the dV/dK products too, or for neither, is slower)
     f32x16 sacc = {}, dpacc = {};
     V8 pf[2], sf[2];
     __builtin_amdgcn_s_setprio(1);
@@ -275,9 +269,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) elem(lb, r, sacc, dpacc, pf, sf);
-    __builtin_amdgcn_s_setprio(1);
     dvdk(qs, gs, pf, sf);
-    __builtin_amdgcn_s_setprio(0);
     if (qt + 1 < nq) store_q(B ^ 1);
     __syncthreads();
   };
