@@ -6,8 +6,9 @@
 //   P = exp(s Q'K'^T - LSE); dP = dO V^T; dS = P * (dP - Delta);
 //   dQ' = s dS K'; with RoPE, dQ = R^T dQ'.
 //
-// attn_bwd_dq_kernel: one workgroup per (sample, head, 128-query tile);
-// 4 waves x 32 queries with Q' and dO in registers; streams 64-key tiles of
+// attn_bwd_dq_kernel: one workgroup per (sample, head, query tile of the
+// forward: 256 bf16, 128 fp32), one wave per 32 queries with Q' and dO in
+// registers; streams 64-key tiles of
 // K' and V through double-buffered LDS like the forward.  S^T = K'Q'^T and
 // dP^T = V dO^T put one query per lane (LSE and Delta are per-lane scalars);
 // dQ'^T += K'^T dS^T takes dS^T straight from the accumulators and K'^T by
@@ -22,20 +23,22 @@
 
 namespace pvj {
 
-constexpr int kDqBM = 128;  // queries per dQ workgroup (= forward tile, uses fwd_items)
-constexpr int kDqBN = 64;   // keys per streamed tile
-constexpr int kDqThreads = kTileThreads;
+constexpr int kDqBN = 64;  // keys per streamed tile
 
 template <typename T, int D>
 struct DqCfg {
+  // queries per workgroup = the forward tile (the kernel walks fwd_items):
+  // bf16 8 waves x 32 queries share each K'/V tile copy; fp32 4 waves
+  static constexpr int BM = sizeof(T) == 2 ? 256 : 128;
+  static constexpr int THREADS = BM * 2;
   static constexpr int UPR = D / 8;
-  static constexpr int NK = kDqBN * UPR / kDqThreads;  // units per thread per tile (K and V)
+  static constexpr int NK = kDqBN * UPR / THREADS;  // units per thread per tile (K and V)
   static constexpr int TILE = kDqBN * D;
 };
 
-// bf16 fits two waves per SIMD (two workgroups per CU, 64 KB of LDS each)
+// bf16 runs two waves per SIMD (one 8-wave workgroup per CU, 64 KB of LDS)
 template <typename T, int D>
-__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(
+__global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves_per_eu(
     sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_bwd_dq_kernel(
     Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int qi = it.tile * kDqBM + wave * 32 + l32;  // this lane's query
+  const int qi = it.tile * C::BM + wave * 32 + l32;  // this lane's query
 
   V8 qf[KS], gf[KS];
 #pragma unroll
@@ -75,11 +78,11 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(
 
   const int k_unit = tid % UPR;
   const int k_row0 = tid / UPR;
-  constexpr int K_ROW_STEP = kDqThreads / UPR;
+  constexpr int K_ROW_STEP = C::THREADS / UPR;
   constexpr bool DMA = sizeof(T) == 2;
   V8 kreg[DMA ? 1 : NK], vreg[DMA ? 1 : NK];
   // direct copies (K and V tiles share one layout; rows past the end are zeros)
-  typedef DmaTile<D, kDqBN> DT;
+  typedef DmaTile<D, kDqBN, C::THREADS> DT;
   const DT dma(RS);
   const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
   auto load_kv = [&](int kv0, int b) {
@@ -276,7 +279,7 @@ static hipError_t launch_dq_t(const Meta& m, const void* q, const void* k, const
                               const void* dout, const float* lse, const float* delta, void* dq,
                               float scale, bool rope, hipStream_t stream) {
   if (m.n_fwd > 0)
-    attn_bwd_dq_kernel<T, D><<<dim3(m.n_fwd), dim3(kDqThreads), 0, stream>>>(
+    attn_bwd_dq_kernel<T, D><<<dim3(m.n_fwd), dim3(DqCfg<T, D>::THREADS), 0, stream>>>(
         m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
         scale * 1.4426950408889634f, rope ? 1 : 0);
   return hipGetLastError();

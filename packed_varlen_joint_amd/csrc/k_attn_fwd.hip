@@ -5,9 +5,11 @@
 // by per-sample cumulative offsets (no block-diagonal mask); HF paper page,
 // "Highlights": per-sample 2D RoPE, applied here on load when requested.
 //
-// One workgroup = one work item (sample, head, 128-query tile); 4 waves, each
-// owning 32 queries.  The KV loop streams 64-key tiles of the item's own
-// sample only, through double-buffered LDS (separate static buffers).
+// One workgroup = one work item (sample, head, query tile); one wave per 32
+// queries: bf16 tiles of 256 queries (8 waves, two per SIMD, all eight
+// sharing each K/V tile copy), fp32 tiles of 128.  The KV loop streams 64-key
+// tiles of the item's own sample only, through double-buffered LDS (separate
+// static buffers).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16; fp32 inputs use eight
 // v_mfma_f32_32x32x2_f32 per k-step of 16):
@@ -39,21 +41,23 @@
 
 namespace pvj {
 
-constexpr int kFwdBM = 128;  // query rows per workgroup (must match fwd_tile_rows)
-constexpr int kFwdBN = 64;   // keys per KV tile
-constexpr int kFwdThreads = kTileThreads;
+constexpr int kFwdBN = 64;  // keys per KV tile
 
 template <typename T, int D>
 struct FwdTile {
-  static constexpr int UPR = D / 8;                      // 8-element units per row
-  static constexpr int NK = kFwdBN * UPR / kFwdThreads;  // units per thread per tile (staged)
+  // query rows per workgroup (must match fwd_tile_rows): bf16 8 waves x 32
+  // queries, so the eight share each K/V tile copy; fp32 4 waves
+  static constexpr int BM = sizeof(T) == 2 ? 256 : 128;
+  static constexpr int THREADS = BM * 2;               // one wave per 32 queries
+  static constexpr int UPR = D / 8;                    // 8-element units per row
+  static constexpr int NK = kFwdBN * UPR / THREADS;    // units per thread per tile (staged)
   static constexpr int TILE = kFwdBN * D;
 };
 
-// bf16 tiles fit two waves per SIMD, so two workgroups share a CU and one's
+// bf16 runs two waves per SIMD (one 8-wave workgroup per CU), so one wave's
 // softmax VALU work overlaps the other's matrix-core work.
 template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
+__global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_waves_per_eu(
     sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(
     Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, float scale_log2) {
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int qi = it.tile * kFwdBM + wave * 32 + l32;  // this lane's query (local index)
+  const int qi = it.tile * C::BM + wave * 32 + l32;  // this lane's query (local index)
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load if ROPE ----
   V8 qf[KS];
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   // staged path (K with RoPE, fp32): rows k_row0 + i * K_ROW_STEP, one unit each
   const int k_unit = tid % UPR;
   const int k_row0 = tid / UPR;
-  constexpr int K_ROW_STEP = kFwdThreads / UPR;
+  constexpr int K_ROW_STEP = C::THREADS / UPR;
   constexpr int NKR = K_DMA ? 1 : NK;
   constexpr int NVR = DMA ? 1 : NK;
   V8 kreg[NKR], vreg[NVR];
@@ -115,8 +119,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
   const int k_axis = unit_axis(k_unit, m);
   // direct copies: per-thread offsets (K and V tiles share one layout) and
   // one buffer resource per operand spanning this head's L rows
-  const DmaTile<D, kFwdBN> dma(RS);
-  typedef DmaTile<D, kFwdBN> DT;
+  typedef DmaTile<D, kFwdBN, C::THREADS> DT;
+  const DT dma(RS);
   const typename DT::Src rk = DT::src(Kh, RS, L), rv = DT::src(Vh, RS, L);
 
   // the KV loop is unrolled by two so that every LDS address is a fixed
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(
 template <typename T, int D, bool ROPE>
 static hipError_t launch_fwd_t(const Meta& m, const void* q, const void* k, const void* v, void* o,
                                float* lse, float scale_log2, hipStream_t stream) {
-  attn_fwd_kernel<T, D, ROPE><<<dim3(m.n_fwd), dim3(kFwdThreads), 0, stream>>>(
+  attn_fwd_kernel<T, D, ROPE><<<dim3(m.n_fwd), dim3(FwdTile<T, D>::THREADS), 0, stream>>>(
       m, (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, scale_log2);
   return hipGetLastError();
 }

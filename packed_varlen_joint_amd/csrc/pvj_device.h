@@ -207,7 +207,8 @@ __device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, Ro
 }
 
 // Direct global -> LDS copy (buffer_load_dwordx4 ... lds, no VGPR round trip)
-// of a [ROWS][D] bf16 tile: rows row0 .. row0+ROWS-1 of one (sample, head),
+// of a [ROWS][D] bf16 tile by a workgroup of THREADS threads: rows row0 ..
+// row0+ROWS-1 of one (sample, head),
 // stored in LDS row sigma(r) with the tsw swizzle.  Each instruction writes
 // one wave's 64 consecutive 16-byte LDS slots in lane order, so every lane
 // loads the global unit that belongs in its slot.  The copies complete
@@ -220,10 +221,10 @@ __device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, Ro
 // resource, so the hardware returns zeros for them (no clamp, no data from
 // another sample).  The planner keeps a sample's span below 2 GiB, so the
 // 32-bit offsets never wrap.
-template <int D, int ROWS>
+template <int D, int ROWS, int THREADS = kTileThreads>
 struct DmaTile {
   static constexpr int UPR = D / 8;
-  static constexpr int PER = ROWS * UPR / kTileThreads;
+  static constexpr int PER = ROWS * UPR / THREADS;
   uint32_t off[PER];
   int wave;
   __device__ __forceinline__ explicit DmaTile(size_t RS) {
@@ -231,7 +232,7 @@ struct DmaTile {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int slot = (i * (kTileThreads / 64) + wave) * 64 + lane;
+      const int slot = (i * (THREADS / 64) + wave) * 64 + lane;
       const int rho = slot / UPR;
       const int u = (slot % UPR) ^ tsw<D>(rho);
       off[i] = (uint32_t)(((size_t)bsigma(rho) * RS + (size_t)u * 8) * sizeof(bf16));
@@ -254,22 +255,23 @@ struct DmaTile {
 // The resource-building copy is a free function template: kept out of the
 // kernels' own bodies, the host-side compile of the kernel templates does not
 // see the resource type.
-template <int D, int ROWS>
+template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void dma_copy(const uint32_t* off, int wave, void* tile, const bf16* g,
                                          int bytes, uint32_t soff) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g), (short)0, bytes, 0x00020000);
   bf16* t = static_cast<bf16*>(tile);
 #pragma unroll
-  for (int i = 0; i < DmaTile<D, ROWS>::PER; ++i)
+  for (int i = 0; i < DmaTile<D, ROWS, THREADS>::PER; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(t + (i * (kTileThreads / 64) + wave) * 512),
+        r, (__attribute__((address_space(3))) void*)(t + (i * (THREADS / 64) + wave) * 512),
         16, off[i], soff, 0, 0);
 }
-template <int D, int ROWS>
-__device__ __forceinline__ void DmaTile<D, ROWS>::copy(void* tile, Src sr, size_t RS,
-                                                      int row0) const {
-  dma_copy<D, ROWS>(off, wave, tile, sr.g, sr.bytes, (uint32_t)((size_t)row0 * RS * sizeof(bf16)));
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::copy(void* tile, Src sr, size_t RS,
+                                                               int row0) const {
+  dma_copy<D, ROWS, THREADS>(off, wave, tile, sr.g, sr.bytes,
+                             (uint32_t)((size_t)row0 * RS * sizeof(bf16)));
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

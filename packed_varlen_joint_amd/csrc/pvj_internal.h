@@ -15,8 +15,8 @@ constexpr int kMaxLatentSide = 32767;  // h_lat, w_lat, n_frames limit (bounds t
 // Rows of one attention work item.  Forward: query rows per workgroup.
 // Backward: key rows per workgroup.
 inline int fwd_tile_rows(int dtype, int head_dim) {
-  (void)dtype; (void)head_dim;
-  return 128;
+  (void)head_dim;
+  return dtype == PVJ_BF16 ? 256 : 128;
 }
 inline int bwd_tile_rows(int dtype, int head_dim) {
   (void)dtype; (void)head_dim;
