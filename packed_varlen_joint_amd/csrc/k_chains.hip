@@ -343,13 +343,14 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
   }
 }
 
-// final pass over partial slots: 4 waves per (kind, sample, column chunk);
-// wave w adds the sample's slots w, w+4, ..., then wave 0 adds the four wave
-// sums in order (a fixed order: deterministic).  Slot layout [slot][kind][C].
-__global__ __launch_bounds__(256) void seg_final_slots_kernel(
+// final pass over partial slots: 16 waves per (kind, sample, column chunk);
+// wave w adds the sample's slots w, w+32, ... and w+16, w+48, ... in two
+// chains (two loads in flight), then wave 0 adds the sixteen wave sums in
+// order (a fixed order: deterministic).  Slot layout [slot][kind][C].
+__global__ __launch_bounds__(1024) void seg_final_slots_kernel(
     const int32_t* __restrict__ cu, int n_samples, int C, int R, int kinds,
     const float* __restrict__ partial, float* __restrict__ out0, float* __restrict__ out1) {
-  __shared__ f32x8 red[3][64];
+  __shared__ f32x8 red[15][64];
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   const int chunk = blockIdx.x % nchunk;
   const int s = (blockIdx.x / nchunk) % n_samples;
@@ -358,17 +359,22 @@ __global__ __launch_bounds__(256) void seg_final_slots_kernel(
   const int col = chunk * kColChunk + lane * 8;
   const bool active = col < C;
   const int nsl = (cu[s + 1] - cu[s] + R - 1) / R;
-  f32x8 acc = {};
+  f32x8 acc = {}, acc2 = {};
   if (active) {
     const float* p = partial + ((size_t)slot_base(cu, s, R) * kinds + kind) * C + col;
-    for (int k = wave; k < nsl; k += 4) acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * kinds * C);
+    int k = wave;
+    for (; k + 16 < nsl; k += 32) {
+      acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * kinds * C);
+      acc2 += *reinterpret_cast<const f32x8*>(p + (size_t)(k + 16) * kinds * C);
+    }
+    if (k < nsl) acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * kinds * C);
+    acc += acc2;
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
   if (wave == 0 && active) {
-    acc += red[0][lane];
-    acc += red[1][lane];
-    acc += red[2][lane];
+#pragma unroll
+    for (int w = 0; w < 15; ++w) acc += red[w][lane];
     *reinterpret_cast<f32x8*>((kind ? out1 : out0) + (size_t)s * C + col) = acc;
   }
 }
@@ -591,8 +597,8 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
                          eps);
     }
     const int nchunk = (C + kColChunk - 1) / kColChunk;
-    seg_final_slots_kernel<<<2 * B * nchunk, 256, 0, st>>>(cu, B, C, R, 2, partial, dshift,
-                                                            dscale);
+    seg_final_slots_kernel<<<2 * B * nchunk, 1024, 0, st>>>(cu, B, C, R, 2, partial, dshift,
+                                                             dscale);
     return hipGetLastError();
   }
   const size_t part = (size_t)2 * B * splits * C * sizeof(float);
