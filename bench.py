@@ -110,27 +110,42 @@ class PackStep:
         self.plan = plan
 
 
-def inference_bench(steps, warmup=2):
-    """The multi-prompt classifier-free-guidance inference pack (6 prompts x
-    cond/uncond, forward only: plan, pack with RoPE, attention forward, unpack
-    O), timed like the main step."""
+def pack_bench(name, steps, warmup=2):
+    """One of the other packs (the multi-prompt CFG inference pack, the 1024^2
+    CFG pack, the extreme-shape pack), timed like the main step: plan, pack with
+    RoPE, attention forward, unpack O, and for training packs pack dO, attention
+    backward and unpack the gradients.  Reports the step rate and the attention
+    kernels' own rate (events on the launch stream)."""
     import torch
+    import packed_varlen_joint_amd as pvj
     from pvj_inputs import workload
-    wl = workload("infer_multi")
+    wl = workload(name)
     step = PackStep(wl, 0)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    pvj.profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    kms = {}
+    for k in ("attn_fwd", "attn_bwd", "attn_bwd_dq"):
+        tot, n = pvj.profile_read(k)
+        if n:
+            kms[k] = tot / steps
+    pvj.profile_enable(False)
     cu = step.plan.cu_seqlens
     S2 = float(sum((cu[i + 1] - cu[i]) ** 2 for i in range(len(wl.samples))))
-    f = 4.0 * wl.n_heads * wl.head_dim * S2
+    f = (14.0 if wl.backward else 4.0) * wl.n_heads * wl.head_dim * S2
+    kt = sum(kms.values())
     return {"workload": wl.name, "n_samples": len(wl.samples), "n_tokens": wl.n_tokens,
-            "ms_per_step": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+            "backward": wl.backward, "ms_per_step": round(ms, 4),
+            "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+            "attn_kernel_tflops": round(f / (kt * 1e-3) / 1e12, 2) if kt else None,
+            "attn_kernel_frac_of_peak": round(f / (kt * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            if kt else None,
             "tokens_per_s": round(wl.n_tokens / (ms * 1e-3), 1)}
 
 
@@ -407,7 +422,8 @@ def main():
         roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
-        out["inference"] = inference_bench(5)
+        out["inference"] = pack_bench("infer_multi", 5)
+        out["other_packs"] = {n: pack_bench(n, 5) for n in ("cfg_1024", "extreme")}
         if wl.dtype == "bf16":
             out["projections"] = proj_bench(wl, 5)
     if not args.no_cpu_baseline:
