@@ -183,3 +183,23 @@ def test_bwd_fused_chain_step_vs_oracle():
     assert_close("dq", to_np(dq), rq, dt)
     assert_close("dk", to_np(dk), rk, dt)
     assert_close("dv", to_np(dv), rv, dt)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_fwd_bwd_tile_boundaries(D):
+    # sample lengths on either side of the work-item tiles (bf16: 256 queries
+    # per forward / dQ workgroup, 128 keys per dK/dV workgroup, 64-key and
+    # 32-query streamed tiles), text-only and image samples mixed
+    samples = [(0, 0, 255), (0, 0, 256), (0, 0, 257), (16, 16, 0), (16, 16, 1), (0, 0, 127),
+               (0, 0, 129), (8, 8, 447), (0, 0, 31), (0, 0, 33), (16, 32, 0)]
+    H, dt = 2, "bf16"
+    plan = _plan(samples, H, D, dt)
+    say("fwd+bwd tile boundaries D=%d T=%d" % (D, plan.n_tokens))
+    q, k, v, do = draw_tensors(plan.n_tokens, H, D, dt, 97, n=4)
+    o, _, dq, dk, dv = _fwd_bwd(plan, *(to_dev(x, dt) for x in (q, k, v, do)), True, dt)
+    ro, _ = oracle.attn_fwd(q, k, v, samples, rope=True)
+    assert_close("o", to_np(o), ro, dt)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, samples, rope=True)
+    assert_close("dq", to_np(dq), rq, dt)
+    assert_close("dk", to_np(dk), rk, dt)
+    assert_close("dv", to_np(dv), rv, dt)
