@@ -486,18 +486,26 @@ static int units_per_lane(int C) { return (C / 8 + 63) / 64; }
 // in registers: rows up to 3072 columns
 static bool one_pass(int C) { return units_per_lane(C) <= 6; }
 
-// rows per wave of the one-pass backward: about 8 waves per CU over the
-// stream, at least 8 and at most 64 rows each
-static int rows_per_wave(int rows) {
-  const int r = rows / (256 * 8);
-  return r < 8 ? 8 : (r > 64 ? 64 : r);
+// rows per wave of the one-pass LayerNorm backward: as few as fill the chip's
+// waves in a single round (a second, partial round costs a whole round's time;
+// measured: 0.31 -> 0.25 ms on the training pack).  The waves that fit at once
+// follow the kernel's register use per head-dim width (one wave per SIMD at
+// six units per lane, two at four, three at two, four at one); at least 8
+// rows per wave.  Correctness does not depend on it.
+static int rows_per_wave(int rows, int n_samples, int C) {
+  const int nu = units_per_lane(C);
+  const int per_simd = nu >= 6 ? 1 : (nu >= 4 ? 2 : (nu >= 2 ? 3 : 4));
+  const int slots = 256 * 4 * per_simd - n_samples - 1;
+  const int r = (rows + slots - 1) / slots;
+  return r < 8 ? 8 : r;
 }
 static int n_slots(int rows, int n_samples, int R) { return rows / R + n_samples + 1; }
 
 size_t chain_workspace_bytes(int n_samples, int C, int rows, int mode, int splits) {
   auto al = [](size_t b) { return (b + 255) / 256 * 256; };
   if (mode == 0 && one_pass(C))
-    return al((size_t)n_slots(rows, n_samples, rows_per_wave(rows)) * 2 * C * sizeof(float));
+    return al((size_t)n_slots(rows, n_samples, rows_per_wave(rows, n_samples, C)) * 2 * C *
+              sizeof(float));
   const size_t part = (size_t)(mode == 0 ? 2 : 1) * n_samples * splits * C * sizeof(float);
   const size_t st = mode == 0 ? (size_t)rows * sizeof(float2) : 0;
   return al(part) + al(st);
@@ -585,7 +593,7 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
   const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
   const bool bf = p->desc.dtype == PVJ_BF16;
   if (one_pass(C)) {
-    const int R = rows_per_wave(rows), ns = n_slots(rows, B, R);
+    const int R = rows_per_wave(rows, B, C), ns = n_slots(rows, B, R);
     float* partial = static_cast<float*>(ws);
     if (rows > 0) {
       const dim3 g((ns + 3) / 4);
