@@ -62,8 +62,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
   // direct-to-LDS copies from the current tile's reads
   __shared__ __align__(16) T q_b0[C::TILE], q_b1[C::TILE], g_b0[C::TILE], g_b1[C::TILE];
   __shared__ __align__(16) float l_b0[2 * BQ], l_b1[2 * BQ];  // LSE*log2(e), then Delta
+  // bf16: the key tile's V rows (B operands of dP); after the loop the same
+  // LDS stages the epilogue, 64 keys of fp32 at a time
   __shared__ __align__(16) T v_t[DMA ? kBwdBN * D : 8];
   __shared__ __align__(16) float stage_own[DMA ? 8 : kBwdBN / 2 * D];
+  static_assert(!DMA || sizeof(v_t) >= kBwdBN / 2 * D * sizeof(float), "epilogue staging");
   float* const stage = DMA ? reinterpret_cast<float*>(v_t) : stage_own;
 
   const Item it = m.bwd_items[blockIdx.x];
@@ -78,9 +81,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // this wave's 32 keys as B operands (registers); rows past the end are zero
-  // and need no mask: their dK, dV rows are never stored, and dS feeds only
-  // dK of its own key
+  // this wave's 32 keys of K' (and of V for fp32) as B operands in registers;
+  // rows past the end are zero and need no mask: their dK, dV rows are never
+  // stored, and dS feeds only dK of its own key
   const int my_key = kv0 + wave * 32 + l32;
   V8 kf[KS], vf[DMA ? 1 : KS];
 #pragma unroll
@@ -165,9 +168,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
 
   // Per-lane LDS addresses, fixed for the whole loop (bf16): row l32 at unit
   // 2ks+hi of the Q' and dO tiles (same layout), and the transposed fragment
-  // bases of output block db and half t; the 32-query block, the 16-query
-  // half and the buffer add compile-time offsets.  The empty asm keeps them
-  // in registers.
+  // bases of output block db and half t; the 16-query half and the buffer add
+  // compile-time offsets.  The empty asm keeps them in registers.
   uint32_t qa[KS], fa[DB][2];
   if constexpr (DMA) {
     const int g = lane >> 4, sl = lane & 15;
