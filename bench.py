@@ -112,7 +112,8 @@ class PackStep:
 
 def pack_bench(name, steps, warmup=2):
     """One of the other packs (the multi-prompt CFG inference pack, the 1024^2
-    CFG pack, the extreme-shape pack), timed like the main step: plan, pack with
+    CFG pack, the extreme-shape pack, the two-frame editing pack with 3-axis
+    RoPE), timed like the main step: plan, pack with
     RoPE, attention forward, unpack O, and for training packs pack dO, attention
     backward and unpack the gradients.  Reports the step rate and the attention
     kernels' own rate (events on the launch stream)."""
@@ -423,7 +424,7 @@ def main():
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
         out["inference"] = pack_bench("infer_multi", 5)
-        out["other_packs"] = {n: pack_bench(n, 5) for n in ("cfg_1024", "extreme")}
+        out["other_packs"] = {n: pack_bench(n, 5) for n in ("cfg_1024", "extreme", "edit_1024")}
         if wl.dtype == "bf16":
             out["projections"] = proj_bench(wl, 5)
     if not args.no_cpu_baseline:
