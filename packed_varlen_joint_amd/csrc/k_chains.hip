@@ -380,16 +380,15 @@ __global__ __launch_bounds__(1024) void seg_final_slots_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// per-sample column sums: partial pass and final pass
-//   MODE 0 (adaln): p0 = sum dy, p1 = sum dy * (x - mean) rstd
-//   MODE 1 (gate):  p0 = sum dout * y, and dy = gate_s * dout is written
+// per-sample column sums of the LayerNorm backward for rows wider than the
+// one-pass kernel holds: p0 = sum dy, p1 = sum dy * (x - mean) rstd over a
+// range of one sample's rows per wave and 512-column chunk.
 // partial layout: [kind][sample][split][C] fp32
 // ---------------------------------------------------------------------------
-template <typename T, int MODE>
+template <typename T>
 __global__ __launch_bounds__(64) void seg_partial_kernel(
-    const int32_t* __restrict__ cu, int n_samples, int C, int splits, const T* __restrict__ a,
-    const T* __restrict__ b, const float2* __restrict__ stats, const T* __restrict__ gate,
-    T* __restrict__ dy_out, float* __restrict__ partial) {
+    const int32_t* __restrict__ cu, int n_samples, int C, int splits, const T* __restrict__ x,
+    const T* __restrict__ dy, const float2* __restrict__ stats, float* __restrict__ partial) {
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   const int chunk = blockIdx.x % nchunk;
   const int split = (blockIdx.x / nchunk) % splits;
@@ -400,26 +399,14 @@ __global__ __launch_bounds__(64) void seg_partial_kernel(
   const int col = chunk * kColChunk + threadIdx.x * 8;
   if (col >= C) return;
   f32x8 acc0[2] = {}, acc1[2] = {};
-  f32x8 w = {};
-  if (MODE == 1) w = ld8f(gate + (size_t)s * C + col);
-  auto row = [&](int r, int slot) {
+  auto row = [&](int r, int k) {
     const size_t o = (size_t)r * C + col;
-    const f32x8 va = ld8f(a + o), vb = ld8f(b + o);
-    if (MODE == 0) {
-      const float2 st = stats[r];
+    const f32x8 va = ld8f(x + o), vb = ld8f(dy + o);
+    const float2 st = stats[r];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc0[slot][e] += vb[e];                            // b = dy
-        acc1[slot][e] += vb[e] * ((va[e] - st.x) * st.y);  // a = x
-      }
-    } else {
-      f32x8 d;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc0[slot][e] += va[e] * vb[e];  // a = dout, b = y
-        d[e] = w[e] * va[e];
-      }
-      store8<T>(dy_out + o, from_f32x8<T>(d));
+    for (int e = 0; e < 8; ++e) {
+      acc0[k][e] += vb[e];
+      acc1[k][e] += vb[e] * ((va[e] - st.x) * st.y);
     }
   };
   int r = lo;
@@ -430,8 +417,44 @@ __global__ __launch_bounds__(64) void seg_partial_kernel(
   for (; r < hi; ++r) row(r, 0);
   const size_t po = ((size_t)s * splits + split) * C + col;
   *reinterpret_cast<f32x8*>(partial + po) = acc0[0] + acc0[1];
-  if (MODE == 0)
-    *reinterpret_cast<f32x8*>(partial + (size_t)n_samples * splits * C + po) = acc1[0] + acc1[1];
+  *reinterpret_cast<f32x8*>(partial + (size_t)n_samples * splits * C + po) = acc1[0] + acc1[1];
+}
+
+// gate + residual backward, rows in slots (the slots of the one-pass
+// LayerNorm backward): wave (slot, 512-column chunk) writes dy = gate_s * dout
+// for its R rows and the partial sum of dout * y over them
+template <typename T>
+__global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int C, int R, const T* __restrict__ dout,
+    const T* __restrict__ y, const T* __restrict__ gate, T* __restrict__ dy,
+    float* __restrict__ partial) {
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int slot = blockIdx.x / nchunk;
+  int s, lo, hi;
+  slot_rows(cu, n_samples, R, slot, s, lo, hi);
+  const int col = chunk * kColChunk + threadIdx.x * 8;
+  if (lo >= hi || col >= C) return;
+  f32x8 acc[2] = {};
+  const f32x8 w = ld8f(gate + (size_t)s * C + col);
+  auto row = [&](int r, int k) {
+    const size_t o = (size_t)r * C + col;
+    const f32x8 va = ld8f(dout + o), vb = ld8f(y + o);
+    f32x8 d;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[k][e] += va[e] * vb[e];
+      d[e] = w[e] * va[e];
+    }
+    store8<T>(dy + o, from_f32x8<T>(d));
+  };
+  int r = lo;
+  for (; r + 4 <= hi; r += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) row(r + k, k & 1);
+  }
+  for (; r < hi; ++r) row(r, 0);
+  *reinterpret_cast<f32x8*>(partial + (size_t)slot * C + col) = acc[0] + acc[1];
 }
 
 // final pass: 4 waves per (kind, sample, column chunk); wave w adds the
@@ -500,13 +523,25 @@ static int rows_per_wave(int rows, int n_samples, int C) {
   return r < 8 ? 8 : r;
 }
 static int n_slots(int rows, int n_samples, int R) { return rows / R + n_samples + 1; }
+// rows per slot of the gate backward: one round of its waves (64-lane
+// workgroups, one per slot and 512-column chunk; about 8192 fit the chip at
+// once), at least 8 rows each
+static int gate_rows_per_slot(int rows, int n_samples, int C) {
+  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  const int slots = 8192 / nchunk - n_samples - 1;
+  const int r = slots > 0 ? (rows + slots - 1) / slots : rows;
+  return r < 8 ? 8 : r;
+}
 
 size_t chain_workspace_bytes(int n_samples, int C, int rows, int mode, int splits) {
   auto al = [](size_t b) { return (b + 255) / 256 * 256; };
   if (mode == 0 && one_pass(C))
     return al((size_t)n_slots(rows, n_samples, rows_per_wave(rows, n_samples, C)) * 2 * C *
               sizeof(float));
-  const size_t part = (size_t)(mode == 0 ? 2 : 1) * n_samples * splits * C * sizeof(float);
+  if (mode == 1)
+    return al((size_t)n_slots(rows, n_samples, gate_rows_per_slot(rows, n_samples, C)) * C *
+              sizeof(float));
+  const size_t part = (size_t)2 * n_samples * splits * C * sizeof(float);
   const size_t st = mode == 0 ? (size_t)rows * sizeof(float2) : 0;
   return al(part) + al(st);
 }
@@ -621,11 +656,11 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
   }
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   if (bf)
-    seg_partial_kernel<bf16, 0><<<B * splits * nchunk, 64, 0, st>>>(
-        cu, B, C, splits, (const bf16*)x, (const bf16*)dy, stats, nullptr, nullptr, partial);
+    seg_partial_kernel<bf16><<<B * splits * nchunk, 64, 0, st>>>(
+        cu, B, C, splits, (const bf16*)x, (const bf16*)dy, stats, partial);
   else
-    seg_partial_kernel<float, 0><<<B * splits * nchunk, 64, 0, st>>>(
-        cu, B, C, splits, (const float*)x, (const float*)dy, stats, nullptr, nullptr, partial);
+    seg_partial_kernel<float><<<B * splits * nchunk, 64, 0, st>>>(
+        cu, B, C, splits, (const float*)x, (const float*)dy, stats, partial);
   seg_final_kernel<<<2 * B * nchunk, 256, 0, st>>>(B, C, splits, 2, partial, dshift, dscale);
   return hipGetLastError();
 }
@@ -636,17 +671,21 @@ hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, c
   const int B = m.n_samples;
   if (B == 0) return hipSuccess;
   const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  const int rows = which == 0 ? m.n_text : m.n_img;
   float* partial = static_cast<float*>(ws);
   const int nchunk = (C + kColChunk - 1) / kColChunk;
-  if (p->desc.dtype == PVJ_BF16)
-    seg_partial_kernel<bf16, 1><<<B * splits * nchunk, 64, 0, st>>>(
-        cu, B, C, splits, (const bf16*)dout, (const bf16*)y, nullptr, (const bf16*)gate,
-        (bf16*)dy, partial);
-  else
-    seg_partial_kernel<float, 1><<<B * splits * nchunk, 64, 0, st>>>(
-        cu, B, C, splits, (const float*)dout, (const float*)y, nullptr, (const float*)gate,
-        (float*)dy, partial);
-  seg_final_kernel<<<B * nchunk, 256, 0, st>>>(B, C, splits, 1, partial, dgate, nullptr);
+  (void)splits;
+  const int R = gate_rows_per_slot(rows, B, C), ns = n_slots(rows, B, R);
+  if (rows > 0) {
+    if (p->desc.dtype == PVJ_BF16)
+      gate_bwd_slots_kernel<bf16><<<ns * nchunk, 64, 0, st>>>(
+          cu, B, C, R, (const bf16*)dout, (const bf16*)y, (const bf16*)gate, (bf16*)dy, partial);
+    else
+      gate_bwd_slots_kernel<float><<<ns * nchunk, 64, 0, st>>>(
+          cu, B, C, R, (const float*)dout, (const float*)y, (const float*)gate, (float*)dy,
+          partial);
+  }
+  seg_final_slots_kernel<<<B * nchunk, 1024, 0, st>>>(cu, B, C, R, 1, partial, dgate, nullptr);
   return hipGetLastError();
 }
 
