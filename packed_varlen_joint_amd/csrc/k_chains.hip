@@ -512,15 +512,15 @@ static bool one_pass(int C) { return units_per_lane(C) <= 6; }
 // rows per wave of the one-pass LayerNorm backward: as few as fill the chip's
 // waves in a single round (a second, partial round costs a whole round's time;
 // measured: 0.31 -> 0.25 ms on the training pack).  The waves that fit at once
-// follow the kernel's register use per head-dim width (one wave per SIMD at
-// six units per lane, two at four, three at two, four at one); at least 8
+// follow the kernel's register use per row width (one wave per SIMD at
+// six units per lane, two at four, three at two, four at one); at least 4
 // rows per wave.  Correctness does not depend on it.
 static int rows_per_wave(int rows, int n_samples, int C) {
   const int nu = units_per_lane(C);
   const int per_simd = nu >= 6 ? 1 : (nu >= 4 ? 2 : (nu >= 2 ? 3 : 4));
   const int slots = 256 * 4 * per_simd - n_samples - 1;
   const int r = (rows + slots - 1) / slots;
-  return r < 8 ? 8 : r;
+  return r < 4 ? 4 : r;
 }
 static int n_slots(int rows, int n_samples, int R) { return rows / R + n_samples + 1; }
 // rows per slot of the gate backward: one round of its waves (64-lane
