@@ -307,6 +307,16 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
           }
           mma16(oacc[db], vf, pf[kb][st]);
         }
+    // bf16: keep the transposing reads of V four products ahead of them
+    // (measured: 1.3% on the forward)
+    if constexpr (sizeof(T) == 2) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 4 * DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
     if (j + 1 < nkv) store_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
     __syncthreads();
   };
