@@ -209,6 +209,16 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
           }
           mma16(acc[db], kt, sfr[kb][st]);
         }
+    // bf16: keep the transposing K' reads four products ahead of them
+    // (measured: 0.8% on this kernel)
+    if constexpr (sizeof(T) == 2) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 4 * DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
     if (j + 1 < nkv) store_kv(B ^ 1);
     __syncthreads();
