@@ -131,6 +131,12 @@ PVJ_API pvj_status_t pvj_plan_create_frames(const pvj_sample_frames_t* samples, 
 PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* plan, int64_t* n_tokens, int32_t* max_len,
                                    const int32_t** cu_seqlens_host, size_t* meta_bytes);
 
+/* Rows of the two modality streams of a plan: *n_text = sum of l_text, *n_image
+ * = sum of n_frames*h_lat*w_lat (review page, "Native-Resolution MMDiT": text
+ * and image keep separate streams around the joint attention).  Either output
+ * may be NULL. */
+PVJ_API pvj_status_t pvj_plan_streams(const pvj_plan_t* plan, int64_t* n_text, int64_t* n_image);
+
 /* Copy the plan's metadata into the caller-allocated device buffer `dev_meta`
  * (>= meta_bytes, 256-byte aligned) on `stream`, and record it in the plan.
  * Compute calls on this plan then read that buffer; it must stay allocated and

@@ -88,6 +88,7 @@ def load_library():
         "pvj_plan_rope_axes": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "pvj_plan_info": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I32),
                                 ctypes.POINTER(ctypes.POINTER(I32)), ctypes.POINTER(SZ)]),
+        "pvj_plan_streams": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
         "pvj_plan_upload": (I32, [P, P, SZ, P]),
         "pvj_plan_destroy": (None, [P]),
         "pvj_pack": (I32, [P, P, P, P, P]),
@@ -193,8 +194,11 @@ class Plan:
         self.max_len = ml.value
         self.cu_seqlens = [cu[i] for i in range(len(self.samples) + 1)]
         self.meta_bytes = mb.value
-        self.n_text = sum(s[2] for s in self.samples)
-        self.n_image = sum(s[0] * s[1] * (s[3] if len(s) == 4 else 1) for s in self.samples)
+        nt = ctypes.c_int64()
+        ni = ctypes.c_int64()
+        _check(lib.pvj_plan_streams(h, ctypes.byref(nt), ctypes.byref(ni)))
+        self.n_text = nt.value
+        self.n_image = ni.value
         self._meta = None
 
     @property
@@ -302,6 +306,15 @@ def _check_tokens(plan: Plan, name: str, t, rows: Optional[int] = None):
         raise ValueError("%s must be a contiguous device tensor" % name)
 
 
+def _check_lse(plan: Plan, lse):
+    torch = _torch()
+    want = (plan.n_heads, plan.n_tokens)
+    if tuple(lse.shape) != want:
+        raise ValueError("lse: shape %s, expected %s" % (tuple(lse.shape), want))
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 device tensor")
+
+
 def _empty_tokens(plan: Plan, like, rows=None):
     torch = _torch()
     rows = plan.n_tokens if rows is None else rows
@@ -362,6 +375,8 @@ def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused:
     _check_tokens(plan, "out", out)
     if lse is None and want_lse:
         lse = torch.empty((plan.n_heads, plan.n_tokens), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_lse(plan, lse)
     flags = PVJ_FLAG_ROPE_FUSED if rope_fused else 0
     _check(load_library().pvj_varlen_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                               _ptr(lse), float(softmax_scale), flags, _stream()))
@@ -378,12 +393,18 @@ def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tokens(plan, n, t)
+    _check_lse(plan, lse)
     dq = _empty_tokens(plan, q) if dq is None else dq
     dk = _empty_tokens(plan, q) if dk is None else dk
     dv = _empty_tokens(plan, q) if dv is None else dv
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tokens(plan, n, t)
     nbytes = plan.bwd_workspace_bytes()
     if workspace is None:
         workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=q.device)
+    elif (workspace.dtype != torch.uint8 or not workspace.is_cuda
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
     flags = (PVJ_FLAG_ROPE_FUSED if rope_fused else 0) | (
         PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0)
     _check(load_library().pvj_varlen_attn_bwd(

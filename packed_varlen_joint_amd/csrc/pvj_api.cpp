@@ -77,7 +77,12 @@ struct KernelTimer {
   hipEvent_t a = nullptr, b = nullptr;
   KernelTimer(int k, hipStream_t s) : kernel(k), stream(s) {
     if (!g_prof_on) return;
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    if (hipEventCreate(&a) != hipSuccess) {
+      a = nullptr;
+      return;
+    }
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
       a = b = nullptr;
       return;
     }
@@ -99,6 +104,66 @@ struct KernelTimer {
   } while (0)
 
 }  // namespace
+
+namespace pvj {
+
+size_t attn_bwd_delta_bytes(const pvj_plan* p) { return ws_delta_bytes(p); }
+
+pvj_status_t check_attn_bwd_args(const pvj_plan* p, const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout,
+                                 const void* dq, const void* dk, const void* dv,
+                                 float softmax_scale, uint32_t flags) {
+  PVJ_TRY(check_plan(p));
+  const bool need = p->n_tokens > 0;
+  PVJ_TRY(check_ptr(q, "q", need));
+  PVJ_TRY(check_ptr(k, "k", need));
+  PVJ_TRY(check_ptr(v, "v", need));
+  PVJ_TRY(check_ptr(o, "o", need));
+  PVJ_TRY(check_ptr(lse, "lse", need));
+  PVJ_TRY(check_ptr(dout, "dout", need));
+  PVJ_TRY(check_ptr(dq, "dq", need));
+  PVJ_TRY(check_ptr(dk, "dk", need));
+  PVJ_TRY(check_ptr(dv, "dv", need));
+  if (flags & ~(PVJ_FLAG_ROPE_FUSED | PVJ_FLAG_ROPE_PREROTATED))
+    return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & PVJ_FLAG_ROPE_FUSED) && (flags & PVJ_FLAG_ROPE_PREROTATED))
+    return fail(PVJ_ERR_INVALID_ARG, "ROPE_FUSED and ROPE_PREROTATED exclude each other");
+  if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
+  return PVJ_OK;
+}
+
+pvj_status_t run_attn_bwd(const pvj_plan* p, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                          void* dv, float* delta, void* qr, void* kr, float softmax_scale,
+                          uint32_t flags, void* stream) {
+  if (p->n_tokens == 0) return PVJ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Meta m = device_meta(p);
+  // fused: rotate Q and K in the preprocess; pre-rotated: take them as given.
+  // Either way the epilogues rotate dQ' and dK' back (dX = R^T dX').
+  const bool rope = (flags & PVJ_FLAG_ROPE_FUSED) != 0;
+  const bool unrotate = rope || (flags & PVJ_FLAG_ROPE_PREROTATED) != 0;
+  const float scale = resolve_scale(p, softmax_scale);
+  {
+    KernelTimer t(PVJ_KERNEL_BWD_PRE, s);
+    PVJ_TRY(launched(t.done(launch_bwd_pre(p, m, o, dout, q, k, delta, qr, kr, rope, s)),
+                     "bwd preprocess"));
+  }
+  const void* qq = rope ? qr : q;
+  const void* kk = rope ? kr : k;
+  {
+    KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
+    PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, 0, qq, kk, v, dout, lse, delta, dq, dk, dv,
+                                            scale, unrotate, s)),
+                     "varlen_attn_bwd dK/dV"));
+  }
+  KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
+  return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
+                                         unrotate, s)),
+                  "varlen_attn_bwd dQ");
+}
+
+}  // namespace pvj
 
 extern "C" {
 
@@ -217,59 +282,19 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
                                          const void* dout, void* dq, void* dk, void* dv,
                                          void* workspace, size_t ws_bytes, float softmax_scale,
                                          uint32_t flags, void* stream) {
-  PVJ_TRY(check_plan(p));
-  const bool need = p->n_tokens > 0;
-  PVJ_TRY(check_ptr(q, "q", need));
-  PVJ_TRY(check_ptr(k, "k", need));
-  PVJ_TRY(check_ptr(v, "v", need));
-  PVJ_TRY(check_ptr(o, "o", need));
-  PVJ_TRY(check_ptr(lse, "lse", need));
-  PVJ_TRY(check_ptr(dout, "dout", need));
-  PVJ_TRY(check_ptr(dq, "dq", need));
-  PVJ_TRY(check_ptr(dk, "dk", need));
-  PVJ_TRY(check_ptr(dv, "dv", need));
-  if (flags & ~(PVJ_FLAG_ROPE_FUSED | PVJ_FLAG_ROPE_PREROTATED))
-    return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  if ((flags & PVJ_FLAG_ROPE_FUSED) && (flags & PVJ_FLAG_ROPE_PREROTATED))
-    return fail(PVJ_ERR_INVALID_ARG, "ROPE_FUSED and ROPE_PREROTATED exclude each other");
-  if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
+  PVJ_TRY(check_attn_bwd_args(p, q, k, v, o, lse, dout, dq, dk, dv, softmax_scale, flags));
   const size_t need_ws = ws_total(p);
-  if (need) {
+  if (p->n_tokens > 0) {
     if (!workspace) return fail(PVJ_ERR_INVALID_ARG, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
       return fail(PVJ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
     if (ws_bytes < need_ws)
       return fail(PVJ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need_ws);
   }
-  if (!need) return PVJ_OK;
-  const Meta m = device_meta(p);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // fused: rotate Q and K in the preprocess; pre-rotated: take them as given.
-  // Either way the epilogues rotate dQ' and dK' back (dX = R^T dX').
-  const bool rope = (flags & PVJ_FLAG_ROPE_FUSED) != 0;
-  const bool unrotate = rope || (flags & PVJ_FLAG_ROPE_PREROTATED) != 0;
-  const float scale = resolve_scale(p, softmax_scale);
   char* ws = static_cast<char*>(workspace);
-  float* delta = reinterpret_cast<float*>(ws);
-  void* qr = ws + ws_delta_bytes(p);
-  void* kr = ws + ws_delta_bytes(p) + ws_rot_bytes(p);
-  {
-    KernelTimer t(PVJ_KERNEL_BWD_PRE, s);
-    PVJ_TRY(launched(t.done(launch_bwd_pre(p, m, o, dout, q, k, delta, qr, kr, rope, s)),
-                     "bwd preprocess"));
-  }
-  const void* qq = rope ? qr : q;
-  const void* kk = rope ? kr : k;
-  {
-    KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
-    PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, 0, qq, kk, v, dout, lse, delta, dq, dk, dv,
-                                            scale, unrotate, s)),
-                     "varlen_attn_bwd dK/dV"));
-  }
-  KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
-  return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
-                                         unrotate, s)),
-                  "varlen_attn_bwd dQ");
+  return run_attn_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, reinterpret_cast<float*>(ws),
+                      ws + ws_delta_bytes(p), ws + ws_delta_bytes(p) + ws_rot_bytes(p),
+                      softmax_scale, flags, stream);
 }
 
 // ---- memory-bound chains --------------------------------------------------
@@ -482,22 +507,34 @@ PVJ_API pvj_status_t pvj_profile_enable(int32_t on) {
 PVJ_API pvj_status_t pvj_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
   if (kernel < 0 || kernel >= PVJ_KERNEL_COUNT)
     return fail(PVJ_ERR_INVALID_ARG, "kernel id %d out of range", kernel);
+  // entries are removed from the pending list as they are consumed, so a failure
+  // part-way leaves only the not yet consumed ones for a later read
+  pvj_status_t st = PVJ_OK;
   std::vector<EventPair> keep;
-  for (auto& e : g_prof_pending) {
+  size_t i = 0;
+  for (; i < g_prof_pending.size(); ++i) {
+    const EventPair& e = g_prof_pending[i];
     if (e.kernel != kernel) {
       keep.push_back(e);
       continue;
     }
-    if (hipEventSynchronize(e.stop) != hipSuccess) return fail(PVJ_ERR_HIP, "event sync");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess)
-      return fail(PVJ_ERR_HIP, "event elapsed time");
+    if (hipEventSynchronize(e.stop) != hipSuccess) {
+      st = fail(PVJ_ERR_HIP, "event sync");
+      break;
+    }
+    if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess) {
+      st = fail(PVJ_ERR_HIP, "event elapsed time");
+      break;
+    }
     g_prof_ms[kernel] += ms;
     g_prof_n[kernel] += 1;
     (void)hipEventDestroy(e.start);
     (void)hipEventDestroy(e.stop);
   }
+  for (; i < g_prof_pending.size(); ++i) keep.push_back(g_prof_pending[i]);
   g_prof_pending.swap(keep);
+  if (st != PVJ_OK) return st;
   if (total_ms) *total_ms = g_prof_ms[kernel];
   if (launches) *launches = g_prof_n[kernel];
   return PVJ_OK;

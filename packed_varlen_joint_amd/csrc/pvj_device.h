@@ -214,13 +214,15 @@ __device__ __forceinline__ f32x8 frag_t(const float* M, int kbase, int nbase, Ro
 // loads the global unit that belongs in its slot.  The copies complete
 // asynchronously: wait_dma() before the barrier that publishes the tile.
 //
-// The source is addressed through a buffer resource that spans exactly the
-// head's L rows (num_records = ((L-1) RS + D) * 2 bytes): each thread's byte
-// offset inside a tile is fixed (computed once), the tile's first row is a
-// uniform SGPR offset, and rows at or past the sample end fall outside the
-// resource, so the hardware returns zeros for them (no clamp, no data from
-// another sample).  The planner keeps a sample's span below 2 GiB, so the
-// 32-bit offsets never wrap.
+// The source is addressed through a buffer resource built per copy: its base
+// is the tile's first row and it spans exactly the sample's remaining rows
+// (num_records = ((L-1-row0) RS + D) * 2 bytes).  Each thread's byte offset
+// inside a tile is fixed (computed once) and is the only offset the hardware
+// range-checks (the scalar offset of a buffer access is outside the check, so
+// it is left at zero), hence rows at or past the sample end fall outside the
+// resource and read as zeros: no clamp, and no data from the next sample or
+// from past the end of the tensor.  The planner keeps a sample's span below
+// 2 GiB, so the 32-bit offsets never wrap.
 template <int D, int ROWS, int THREADS = kTileThreads>
 struct DmaTile {
   static constexpr int UPR = D / 8;
@@ -242,11 +244,11 @@ struct DmaTile {
   // is built where it is used: only device code handles the resource type)
   struct Src {
     const bf16* g;
-    int bytes;
+    int L;
   };
   __device__ __forceinline__ static Src src(const void* g, size_t RS, int L) {
-    return Src{static_cast<const bf16*>(g),
-               L > 0 ? (int)(((size_t)(L - 1) * RS + D) * sizeof(bf16)) : 0};
+    (void)RS;
+    return Src{static_cast<const bf16*>(g), L};
   }
   // copy rows row0 .. row0 + ROWS - 1 (dma_copy below)
   __device__ __forceinline__ void copy(void* tile, Src sr, size_t RS, int row0) const;
@@ -254,10 +256,11 @@ struct DmaTile {
 
 // The resource-building copy is a free function template: kept out of the
 // kernels' own bodies, the host-side compile of the kernel templates does not
-// see the resource type.
+// see the resource type.  g is the tile's first row; bytes spans the rows of
+// the sample from there on.
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void dma_copy(const uint32_t* off, int wave, void* tile, const bf16* g,
-                                         int bytes, uint32_t soff) {
+                                         int bytes) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g), (short)0, bytes, 0x00020000);
   bf16* t = static_cast<bf16*>(tile);
@@ -265,13 +268,16 @@ __device__ __forceinline__ void dma_copy(const uint32_t* off, int wave, void* ti
   for (int i = 0; i < DmaTile<D, ROWS, THREADS>::PER; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(t + (i * (THREADS / 64) + wave) * 512),
-        16, off[i], soff, 0, 0);
+        16, off[i], 0, 0, 0);
 }
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::copy(void* tile, Src sr, size_t RS,
                                                                int row0) const {
-  dma_copy<D, ROWS, THREADS>(off, wave, tile, sr.g, sr.bytes,
-                             (uint32_t)((size_t)row0 * RS * sizeof(bf16)));
+  // rows of the sample from row0 on (row0 < L at every call site; a tile at or
+  // past the end would get an empty resource and read zeros)
+  const int left = sr.L - row0;
+  const int bytes = left > 0 ? (int)(((size_t)(left - 1) * RS + D) * sizeof(bf16)) : 0;
+  dma_copy<D, ROWS, THREADS>(off, wave, tile, sr.g + (size_t)row0 * RS, bytes);
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -76,10 +76,31 @@ struct pvj_plan {
   int dev_id;
 };
 
+// return a failing status from the enclosing function
+#define PVJ_TRY_STATUS(x)              \
+  do {                                 \
+    const pvj_status_t st__ = (x);     \
+    if (st__ != PVJ_OK) return st__;   \
+  } while (0)
+
 namespace pvj {
 // thread-local error detail (pvj_last_error)
 pvj_status_t fail(pvj_status_t st, const char* fmt, ...);
 Meta device_meta(const pvj_plan* p);
+
+// attention backward, shared by the entry point with a caller workspace and
+// the allocation-free one: argument validation (everything but the
+// workspace), and the enqueue of preprocess, dK/dV and dQ with Delta at
+// `delta` ([H, T] fp32) and, with PVJ_FLAG_ROPE_FUSED, Q' and K' at qr, kr
+size_t attn_bwd_delta_bytes(const pvj_plan* p);
+pvj_status_t check_attn_bwd_args(const pvj_plan* p, const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout,
+                                 const void* dq, const void* dk, const void* dv,
+                                 float softmax_scale, uint32_t flags);
+pvj_status_t run_attn_bwd(const pvj_plan* p, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                          void* dv, float* delta, void* qr, void* kr, float softmax_scale,
+                          uint32_t flags, void* stream);
 
 template <typename T>
 inline const T* host_section(const pvj_plan* p, size_t off) {

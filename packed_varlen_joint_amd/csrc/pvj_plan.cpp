@@ -299,6 +299,13 @@ PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* p, int64_t* n_tokens, int32
   return PVJ_OK;
 }
 
+PVJ_API pvj_status_t pvj_plan_streams(const pvj_plan_t* p, int64_t* n_text, int64_t* n_image) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (n_text) *n_text = p->n_text;
+  if (n_image) *n_image = p->n_img;
+  return PVJ_OK;
+}
+
 PVJ_API void pvj_plan_destroy(pvj_plan_t* p) {
   if (!p) return;
   std::free(p->image);

@@ -312,7 +312,7 @@ def test_fwd_cfg_pack_equals_two_calls():
     _sampled_rows(wl, q, k, v, o, lse, np.random.default_rng(0), 4, 96)
 
 
-@pytest.mark.parametrize("name,seed", [("train_64k", 0), ("extreme", 0)])
+@pytest.mark.parametrize("name,seed", [("train_64k", 0), ("train_64k", 1), ("extreme", 0)])
 def test_fwd_large_workloads_sampled(name, seed):
     wl = workload(name, seed)
     say("fwd %s T=%d samples=%d" % (name, wl.n_tokens, len(wl.samples)))

@@ -95,31 +95,35 @@ def test_qkv_and_out_projection_vs_oracle(C, rope, frames):
     assert_close("y_image", to_np(yi), ryi, "bf16")
 
 
-def test_projection_backbone_width_sampled():
-    # the training pack's image stream at hidden 3072 (24 heads x 128): sampled
-    # rows of Q, K, V and of the output projection against the oracle
+@pytest.mark.parametrize("which", ["image", "text"])
+def test_projection_backbone_width_sampled(which):
+    # the training pack's streams at hidden 3072 (24 heads x 128): sampled rows
+    # of Q, K, V and of the output projection against the oracle
     wl = workload("train_64k")
     H, D = wl.n_heads, wl.head_dim
     HD, C = H * D, H * D
     plan = pvj.Plan(wl.samples, H, D, "bf16").upload()
-    say("projections train_64k image stream rows=%d hidden=%d" % (plan.n_image, C))
-    g = torch.Generator(device="cuda").manual_seed(3)
-    x = torch.randn(plan.n_image, C, device="cuda", generator=g).to(torch.bfloat16)
+    n = plan.n_image if which == "image" else plan.n_text
+    say("projections train_64k %s stream rows=%d hidden=%d" % (which, n, C))
+    g = torch.Generator(device="cuda").manual_seed(3 if which == "image" else 4)
+    x = torch.randn(n, C, device="cuda", generator=g).to(torch.bfloat16)
     w = (torch.randn(3 * HD, C, device="cuda", generator=g) * C ** -0.5).to(torch.bfloat16)
     b = (torch.randn(3 * HD, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
     q = torch.zeros(plan.n_tokens, H, D, dtype=torch.bfloat16, device="cuda")
     k, v = torch.zeros_like(q), torch.zeros_like(q)
-    pvj.qkv_proj_pack(plan, "image", x, w, b, q=q, k=k, v=v, rope=True)
+    pvj.qkv_proj_pack(plan, which, x, w, b, q=q, k=k, v=v, rope=True)
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, plan.n_image - 1], rng.integers(0, plan.n_image, 40)]))
-    # joint rows and positions of the sampled image rows
+    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 40)]))
+    # joint rows and positions of the sampled stream rows
     cu = oracle.cu_seqlens(wl.samples)
-    img_starts = np.cumsum([0] + [s[0] * s[1] for s in wl.samples])
+    sizes = [s[0] * s[1] if which == "image" else s[2] for s in wl.samples]
+    starts = np.cumsum([0] + sizes)
     jrows = []
     for r in rows:
-        i = int(np.searchsorted(img_starts, r, side="right") - 1)
-        jrows.append(int(cu[i]) + wl.samples[i][2] + int(r - img_starts[i]))
+        i = int(np.searchsorted(starts, r, side="right") - 1)
+        skip = wl.samples[i][2] if which == "image" else 0
+        jrows.append(int(cu[i]) + skip + int(r - starts[i]))
     jrows = np.array(jrows)
     pos = oracle.token_positions(wl.samples)[jrows]
     y = projection.linear(to_np(x[rows]), to_np(w), to_np(b))
@@ -129,7 +133,7 @@ def test_projection_backbone_width_sampled():
             ref = oracle.rope2d_at(ref, pos)
         assert_close("qkv"[part], to_np(t[jrows]), ref, "bf16")
     wo = (torch.randn(C, HD, device="cuda", generator=g) * HD ** -0.5).to(torch.bfloat16)
-    yo = pvj.out_proj_unpack(plan, "image", q, wo)
+    yo = pvj.out_proj_unpack(plan, which, q, wo)
     torch.cuda.synchronize()
     ref = projection.linear(to_np(q[jrows]).reshape(len(jrows), HD), to_np(wo))
     assert_close("y", to_np(yo[rows]), ref, "bf16")
