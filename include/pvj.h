@@ -227,6 +227,32 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* plan, const void* q, 
                                          void* workspace, size_t ws_bytes, float softmax_scale,
                                          uint32_t flags, void* stream);
 
+/* ---- attention backward without device allocation -----------------------------
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Computes exactly what pvj_varlen_attn_bwd computes, with the
+ * same kernels and the same bits, but its scratch buffer (Delta, fp32 [H, T])
+ * lives in a static device array the library owns: PVJ_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends.  Limits, checked before anything is enqueued:
+ *  - align256(H * T * 4) <= PVJ_NOALLOC_SCRATCH_BYTES (16 MiB: H * T up to
+ *    4,194,304, e.g. 24 heads x 174,762 tokens), else WORKSPACE_TOO_SMALL;
+ *  - PVJ_FLAG_ROPE_FUSED is UNSUPPORTED (its rotated Q', K' would not fit);
+ *    pass Q, K pre-rotated (pvj_pack_rope) with PVJ_FLAG_ROPE_PREROTATED.
+ * The caller still owns q, k, v, o, lse, dout and the outputs dq, dk, dv.
+ * Nothing is allocated or freed (device or pinned host memory).  Every call on
+ * one GPU shares that GPU's scratch array: calls that overlap in time on one
+ * GPU (several streams or host threads) race and must be serialised by the
+ * caller; calls in order on one stream are safe.  The array keeps the last
+ * call's contents; nothing in it needs clearing between calls.
+ */
+#define PVJ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+PVJ_API pvj_status_t pvj_varlen_attn_bwd_noalloc(const pvj_plan_t* plan, const void* q,
+                                                 const void* k, const void* v, const void* o,
+                                                 const float* lse, const void* dout, void* dq,
+                                                 void* dk, void* dv, float softmax_scale,
+                                                 uint32_t flags, void* stream);
+
 /* ---- memory-bound chains around the attention ---------------------------------
  * Review page, "Kernel fusion": the backbone's memory-bound chains
  * (normalization, adaptive modulation, gating, residual addition) are fused so

@@ -22,7 +22,8 @@ import os
 from typing import Iterable, Optional, Sequence, Tuple
 
 __all__ = ["Plan", "PvjError", "pack", "unpack", "rope2d_apply", "varlen_attn_fwd",
-           "varlen_attn_bwd", "library_path", "load_library", "profile_enable", "profile_read"]
+           "varlen_attn_bwd", "varlen_attn_bwd_noalloc", "library_path", "load_library",
+           "profile_enable", "profile_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # PVJ_LIBRARY may point at another build of the same library (same ABI)
@@ -99,6 +100,7 @@ def load_library():
         "pvj_varlen_attn_fwd": (I32, [P, P, P, P, P, P, F, U32, P]),
         "pvj_varlen_attn_bwd_workspace": (I32, [P, ctypes.POINTER(SZ)]),
         "pvj_varlen_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, F, U32, P]),
+        "pvj_varlen_attn_bwd_noalloc": (I32, [P, P, P, P, P, P, P, P, P, P, F, U32, P]),
         "pvj_plan_work_items": (I32, [P, I32, ctypes.POINTER(ctypes.POINTER(I32)),
                                       ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "pvj_plan_rope_table": (I32, [P, ctypes.POINTER(ctypes.POINTER(ctypes.c_float)),
@@ -411,6 +413,25 @@ def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.
         plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), float(softmax_scale), flags,
         _stream()))
+    return dq, dk, dv
+
+
+def varlen_attn_bwd_noalloc(plan: Plan, q, k, v, o, lse, dout, dq, dk, dv,
+                            softmax_scale: float = 0.0, rope_prerotated: bool = False):
+    """``varlen_attn_bwd`` without any device allocation: the library keeps the
+    backward's scratch (Delta) in a fixed static device buffer (16 MiB per GPU,
+    so H * T <= 4,194,304) and the caller passes every tensor, outputs
+    included.  RoPE on load is not offered; pass Q, K pre-rotated with
+    ``rope_prerotated``.  Calls that overlap in time on one GPU race on the
+    shared buffer."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                 ("dk", dk), ("dv", dv)):
+        _check_tokens(plan, n, t)
+    _check_lse(plan, lse)
+    flags = PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0
+    _check(load_library().pvj_varlen_attn_bwd_noalloc(
+        plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+        _ptr(dk), _ptr(dv), float(softmax_scale), flags, _stream()))
     return dq, dk, dv
 
 

@@ -238,3 +238,15 @@ def test_bwd_workspace_size(lib):
     for dt, elt in (("f32", 4), ("bf16", 2)):
         p = _plan([(3, 3, 2)], H, D, dt)
         assert p.bwd_workspace_bytes() == al(T * H * 4) + 2 * al(T * H * D * elt)
+
+
+def test_noalloc_bwd_limits_before_any_device_call(lib):
+    # the allocation-free backward checks its fixed scratch size and flags
+    # before touching HIP (the plan is not even uploaded here)
+    too_big = _plan([(128, 128, 0)] * 8, 33, 128, "bf16")   # H * T = 4,325,376 floats
+    fits = _plan([(128, 128, 0)] * 8, 32, 128, "bf16")      # exactly 16 MiB of Delta
+    p = [16] * 9
+    assert lib.pvj_varlen_attn_bwd_noalloc(too_big.handle, *p, 0.0, 0, None) == 5
+    assert lib.pvj_varlen_attn_bwd_noalloc(fits.handle, *p, 0.0, 1, None) == 2   # ROPE_FUSED
+    assert lib.pvj_varlen_attn_bwd_noalloc(fits.handle, *p, 0.0, 0, None) == 4   # not uploaded
+    assert lib.pvj_varlen_attn_bwd_noalloc(None, *p, 0.0, 0, None) == 1
