@@ -369,6 +369,341 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward without RoPE on load: two wave groups offset by half a tile.
+//
+// The kernel above keeps all eight waves in step (one barrier per tile at the
+// same point of every wave), so the two waves of a SIMD run their score
+// products together, then their softmax together (the matrix cores idle
+// meanwhile), then their output products.  Here waves 0-3 (group 0) and 4-7
+// (group 1) have one wave on every SIMD each and take the one barrier per
+// tile at different points of the same instruction stream:
+//   M(k): S_k = K_k Q^T (k < n), then O^T += V_{k-1}^T P_{k-1}^T (k >= 1)
+//   V(k): online softmax of S_k into P_k (k < n)
+//   group 0: M(k) V(k) | barrier      group 1: M(k) | barrier V(k)
+// so after every barrier one wave of a SIMD issues its 32 products while the
+// other runs its softmax.  Pipeline set k (read in M(k) by both groups) holds
+// K_k and V_{k-1}; set k + 1 goes into the buffers of set k - 1, whose last
+// reader (M(k-1) of group 1) is done at barrier k - 1.  Group 0 copies all of
+// set k + 1 during its M(k), one copy instruction every few products: issued
+// in a burst by all eight waves after a barrier, the copies stalled the
+// issuing waves for hundreds of cycles (measured), and a group-1 wave issuing
+// them would delay its softmax, which is on the critical path.  Inside M(k)
+// the operand reads from LDS run four products ahead of the products.  Per row the
+// arithmetic is that of the kernel above, in the same order (O is scaled by
+// each tile's alpha before that tile's products are added), so both give the
+// same bits.
+// ---------------------------------------------------------------------------
+constexpr int kPpAhead = 4;  // operand fragments in flight ahead of the products
+
+// Scheduling groups of one M phase: N ops, the first NS of them score
+// products (one LDS read per operand), the rest output products (two
+// transposing reads per operand).  First the reads of the first AHEAD ops,
+// then per op its product and the reads of the op AHEAD further on.
+__host__ __device__ constexpr int pp_reads(int i, int ns) { return i < ns ? 1 : 2; }
+__host__ __device__ constexpr int pp_first_reads(int n, int ns, int ahead) {
+  int r = 0;
+  for (int i = 0; i < ahead && i < n; ++i) r += pp_reads(i, ns);
+  return r;
+}
+// Op i of N is followed by a tile copy instruction when pp_copy_after(i, N,
+// NC) (NC copies spread evenly over the N products).
+__host__ __device__ constexpr bool pp_copy_after(int i, int n, int nc) {
+  return nc > 0 && ((i + 1) * nc) / n != (i * nc) / n;
+}
+template <int I, int N, int NS, int AHEAD, int NC>
+__device__ __forceinline__ void pp_sched_ops() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + AHEAD < N)
+      __builtin_amdgcn_sched_group_barrier(0x100, pp_reads(I + AHEAD, NS), 0);
+    if constexpr (pp_copy_after(I, N, NC)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pp_sched_ops<I + 1, N, NS, AHEAD, NC>();
+  }
+}
+template <int N, int NS, int AHEAD, int NC>
+__device__ __forceinline__ void pp_sched() {
+  __builtin_amdgcn_sched_group_barrier(0x100, pp_first_reads(N, NS, AHEAD), 0);
+  pp_sched_ops<0, N, NS, AHEAD, NC>();
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                   const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
+                   float scale_log2) {
+  constexpr int BM = 256, THREADS = 512;
+  constexpr int KS = D / 16;  // k-steps of 16 over the head dim (score product)
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int TILE = kFwdBN * D;
+  static_assert(FwdTile<bf16, D>::BM == BM, "work items are 256-query tiles");
+
+  __shared__ __align__(16) bf16 k_b0[TILE], k_b1[TILE], v_b0[TILE], v_b1[TILE];
+
+  const Item it = m.fwd_items[blockIdx.x];
+  if (it.sample < 0) return;
+  const SampleInfo si = m.sinfo[it.sample];
+  const int L = si.len;
+  const size_t RS = (size_t)m.n_heads * D;
+  const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int group = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int qi = it.tile * BM + wave * 32 + l32;  // this lane's query (local index)
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 v = {};
+    if (qi < L) v = load8<bf16>(Q + base + (size_t)qi * RS + (2 * ks + hi) * 8);
+    qf[ks] = v;
+  }
+
+  // the copies are issued by group 0 (256 threads) only
+  typedef DmaTile<D, kFwdBN, THREADS / 2> DT;
+  constexpr int NC = 2 * DT::PER;  // copy instructions per set and wave
+  const DT dma(RS);
+  const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
+  const int n = (L + kFwdBN - 1) / kFwdBN;  // key tiles
+  // copy instruction c of set k into buffer pair B: c < PER copies part c of
+  // K_k, the rest part c - PER of V_{k-1}.  A tile at or past the sample end
+  // gets an empty buffer resource (it reads zeros, into a buffer no later
+  // product reads).
+  auto copy_part = [&](int k, auto bc, int c) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    if (c < DT::PER) dma.part(B ? k_b1 : k_b0, rk, RS, k * kFwdBN, c);
+    else dma.part(B ? v_b1 : v_b0, rv, RS, (k - 1) * kFwdBN, c - DT::PER);
+  };
+
+  // per-lane LDS byte offsets of the operand reads (see the kernel above)
+  uint32_t ka[KS], va[DB][2];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      ka[kk] = (uint32_t)(toff<D>(l32, (2 * kk + hi) * 8) * sizeof(bf16));
+      asm volatile("" : "+v"(ka[kk]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        va[db][t] = (uint32_t)(toff<D>(bsigma(8 * (g >> 1) + 4 * t + (sl >> 2)),
+                                       db * 32 + 16 * (g & 1) + 4 * (sl & 3)) * sizeof(bf16));
+        asm volatile("" : "+v"(va[db][t]));
+      }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 sacc[2];
+  bf16x8 pf[2][2];
+
+  // M(k): the products of pipeline set k.  Op i < NS is the score product
+  // (kb = i & 1, kk = i >> 1: the two 32-key chains interleaved); op NS + j
+  // the output product (db = j % DB, st = (j / DB) & 1, kb = j / (2 DB):
+  // every O block still adds its four terms in the order kb0 st0, kb0 st1,
+  // kb1 st0, kb1 st1).  Operand fragments are read kPpAhead ops ahead.
+  auto mphase = [&](auto gc, int k, auto bc, auto hs, auto hp) __attribute__((always_inline)) {
+    constexpr int G = decltype(gc)::value;
+    constexpr int B = decltype(bc)::value;
+    constexpr int NS = decltype(hs)::value ? 2 * KS : 0;
+    constexpr int NP = decltype(hp)::value ? 4 * DB : 0;
+    constexpr int N = NS + NP;
+    // group 0 copies set k + 1 (into the other buffer pair) during M(k), k < n
+    constexpr int NCH = (G == 0 && NS > 0) ? NC : 0;
+    const char* ks = reinterpret_cast<const char*>(B ? k_b1 : k_b0);
+    const char* vs = reinterpret_cast<const char*>(B ? v_b1 : v_b0);
+    auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      if (i < NS) {
+        return *reinterpret_cast<const bf16x8*>(ks + ka[i >> 1] + (i & 1) * 32 * D * sizeof(bf16));
+      } else {
+        const int j = i - NS;
+        const int db = j % DB, st = (j / DB) & 1, kb = j / (2 * DB);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const uint32_t o = (uint32_t)((kb * 32 + 16 * st) * D * sizeof(bf16));
+        bf16x8 f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + va[db][t] + o));
+          const bf16x4 h = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[4 * t + e] = h[e];
+        }
+        return f;
+      }
+    };
+    if constexpr (NS > 0) {
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+    }
+    bf16x8 fr[kPpAhead];
+#pragma unroll
+    for (int i = 0; i < kPpAhead; ++i)
+      if (i < N) fr[i] = fetch(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 a = fr[i % kPpAhead];
+      if (i + kPpAhead < N) fr[i % kPpAhead] = fetch(i + kPpAhead);
+      if (i < NS) {
+        mma16(sacc[i & 1], a, qf[i >> 1]);
+      } else {
+        const int j = i - NS;
+        mma16(oacc[j % DB], a, pf[j / (2 * DB)][(j / DB) & 1]);
+      }
+      if (pp_copy_after(i, N, NCH))
+        copy_part(k + 1, std::integral_constant<int, B ^ 1>{}, ((i + 1) * NCH) / N - 1);
+    }
+    // keep the reads kPpAhead ops ahead of the products, the copies spread
+    pp_sched<N, NS, kPpAhead, NCH>();
+  };
+
+  // V(k): online softmax of S_k (base 2, lazy rescale; see the kernel above)
+  auto vphase = [&](int k, auto mc) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mc)::value;
+    const int kv0 = k * kFwdBN;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+          if (key >= L) sacc[kb][r] = -INFINITY;
+        }
+    }
+    float mx4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& sv = sacc[c >> 1];
+      const int o = 8 * (c & 1);
+      float t = fmaxf(fmaxf(sv[o], sv[o + 1]), sv[o + 2]);
+      t = fmaxf(fmaxf(t, sv[o + 3]), sv[o + 4]);
+      t = fmaxf(fmaxf(t, sv[o + 5]), sv[o + 6]);
+      mx4[c] = fmaxf(t, sv[o + 7]);
+    }
+    float mx = fmaxf(fmaxf(fmaxf(mx4[0], mx4[1]), mx4[2]), mx4[3]);
+    mx = max_pair32(mx) * scale_log2;
+    if (__any(mx > m_run + 8.f)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    float ls4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_run));
+        ls4[r & 3] += p;
+        pf[kb][r >> 3][r & 7] = (bf16)p;
+      }
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    // Materialise the phase's results here: their first use is the next M
+    // phase, and without these empty asm statements the optimizer sinks the
+    // whole softmax below group 0's barrier, which puts both groups back in
+    // step.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        i32x4 w = __builtin_bit_cast(i32x4, pf[kb][st]);
+        asm volatile("" : "+v"(w));
+        pf[kb][st] = __builtin_bit_cast(bf16x8, w);
+      }
+    asm volatile("" : "+v"(m_run), "+v"(l_run));
+  };
+
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<bool, false> F;
+  typedef std::integral_constant<bool, true> Tr;
+  // One iteration of group G: M(k), then V(k); group 1 takes its barrier
+  // between them, group 0 after V(k) (having waited for its copies of set
+  // k + 1).  Each group runs its own copy of the loop.
+  auto iter = [&](auto gc, int k, auto bc, auto hs, auto hp, auto hv, auto mc)
+                  __attribute__((always_inline)) {
+    constexpr int G = decltype(gc)::value;
+    // the phases stay whole: nothing is scheduled across their boundaries
+    __builtin_amdgcn_sched_barrier(0);
+    mphase(gc, k, bc, hs, hp);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (G == 1) __syncthreads();
+    if constexpr (decltype(hv)::value) vphase(k, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (G == 0) {
+      wait_dma();  // set k + 1, copied during M(k)
+      __syncthreads();
+    }
+  };
+  // k = 0: scores only; full tiles 1 .. n-2 in pairs (buffers 1, 0); the last
+  // key tile n-1 (masked when partial); k = n: the last output product only
+  const bool tail_mask = (L % kFwdBN) != 0;
+  auto run = [&](auto gc) __attribute__((always_inline)) {
+    if (n == 1) {
+      if (tail_mask) iter(gc, 0, B0{}, Tr{}, F{}, Tr{}, Tr{});
+      else iter(gc, 0, B0{}, Tr{}, F{}, Tr{}, F{});
+    } else {
+      iter(gc, 0, B0{}, Tr{}, F{}, Tr{}, F{});
+      int k = 1;
+      for (; k + 1 < n - 1; k += 2) {
+        iter(gc, k, B1{}, Tr{}, Tr{}, Tr{}, F{});
+        iter(gc, k + 1, B0{}, Tr{}, Tr{}, Tr{}, F{});
+      }
+      if (k < n - 1) {  // one more full tile (odd k)
+        iter(gc, k, B1{}, Tr{}, Tr{}, Tr{}, F{});
+        ++k;
+      }
+      // k == n - 1
+      if (k & 1) {
+        if (tail_mask) iter(gc, k, B1{}, Tr{}, Tr{}, Tr{}, Tr{});
+        else iter(gc, k, B1{}, Tr{}, Tr{}, Tr{}, F{});
+      } else {
+        if (tail_mask) iter(gc, k, B0{}, Tr{}, Tr{}, Tr{}, Tr{});
+        else iter(gc, k, B0{}, Tr{}, Tr{}, Tr{}, F{});
+      }
+    }
+    if (n & 1) iter(gc, n, B1{}, F{}, Tr{}, F{}, F{});
+    else iter(gc, n, B0{}, F{}, Tr{}, F{}, F{});
+  };
+
+  if (group == 0) {
+#pragma unroll
+    for (int c = 0; c < DT::PER; ++c) copy_part(0, B0{}, c);
+    wait_dma();
+  }
+  __syncthreads();
+  if (group == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+
+  // ---- epilogue: O = O^T / l, LSE ----
+  const float l_tot = sum_pair32(l_run);
+  if (qi < L) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = O + base + (size_t)qi * RS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hi;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d) = w;
+      }
+    if (hi == 0 && LSE)
+      LSE[(size_t)it.head * m.n_tokens + si.start + qi] =
+          (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  }
+}
+
 template <typename T, int D, bool ROPE>
 static hipError_t launch_fwd_t(const Meta& m, const void* q, const void* k, const void* v, void* o,
                                float* lse, float scale_log2, hipStream_t stream) {
@@ -387,6 +722,15 @@ hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, cons
 #define PVJ_FWD(TT, DD)                                                                    \
   return rope ? launch_fwd_t<TT, DD, true>(m, q, k, v, o, lse, sl2, stream)                \
               : launch_fwd_t<TT, DD, false>(m, q, k, v, o, lse, sl2, stream)
+  if (bf && !rope && (D == 128 || D == 64)) {
+    if (D == 128)
+      attn_fwd_pp_kernel<128><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
+          m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
+    else
+      attn_fwd_pp_kernel<64><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
+          m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
+    return hipGetLastError();
+  }
   if (bf && D == 128) PVJ_FWD(bf16, 128);
   if (bf && D == 64) PVJ_FWD(bf16, 64);
   if (!bf && D == 128) PVJ_FWD(float, 128);

@@ -17,6 +17,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Eight consecutive elements of a row: the unit every kernel moves and the
 // operand one lane feeds to one 32x32 matrix-core k-step of 16.
@@ -252,6 +253,9 @@ struct DmaTile {
   }
   // copy rows row0 .. row0 + ROWS - 1 (dma_copy below)
   __device__ __forceinline__ void copy(void* tile, Src sr, size_t RS, int row0) const;
+  // only the i-th of the PER copy instructions of that tile, so a kernel can
+  // spread one tile's copies over its instruction stream
+  __device__ __forceinline__ void part(void* tile, Src sr, size_t RS, int row0, int i) const;
 };
 
 // The resource-building copy is a free function template: kept out of the
@@ -269,6 +273,23 @@ __device__ __forceinline__ void dma_copy(const uint32_t* off, int wave, void* ti
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(t + (i * (THREADS / 64) + wave) * 512),
         16, off[i], 0, 0, 0);
+}
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void dma_copy_one(uint32_t off, int wave, int i, void* tile,
+                                             const bf16* g, int bytes) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g), (short)0, bytes, 0x00020000);
+  bf16* t = static_cast<bf16*>(tile);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(t + (i * (THREADS / 64) + wave) * 512), 16,
+      off, 0, 0, 0);
+}
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::part(void* tile, Src sr, size_t RS,
+                                                               int row0, int i) const {
+  const int left = sr.L - row0;
+  const int bytes = left > 0 ? (int)(((size_t)(left - 1) * RS + D) * sizeof(bf16)) : 0;
+  dma_copy_one<D, ROWS, THREADS>(off[i], wave, i, tile, sr.g + (size_t)row0 * RS, bytes);
 }
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::copy(void* tile, Src sr, size_t RS,
