@@ -66,12 +66,19 @@ def _traffic(kernel):
 
 
 class PackStep:
-    def __init__(self, wl, seed, rope="pack"):
+    """One pass of the hot path over one pack.  `backward` overrides the
+    workload's own (a training pack timed forward only); `reuse_plan` builds
+    and uploads the plan once (an inference loop over denoising steps keeps
+    the same per-sample resolutions), otherwise every step plans again."""
+
+    def __init__(self, wl, seed, rope="pack", backward=None, reuse_plan=False):
         import torch
         import packed_varlen_joint_amd as pvj
         self.pvj = pvj
         self.wl = wl
         self.rope = rope
+        self.backward = wl.backward if backward is None else backward
+        self.reuse_plan = reuse_plan
         H, D = wl.n_heads, wl.head_dim
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         probe = pvj.Plan(wl.samples, H, D, wl.dtype)
@@ -93,14 +100,17 @@ class PackStep:
 
     def __call__(self):
         pvj, wl, j = self.pvj, self.wl, self.joint
-        plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+        if self.reuse_plan and self.plan is not None:
+            plan = self.plan
+        else:
+            plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
         in_pack = self.rope == "pack"
         for x in ("q", "k", "v"):
             pvj.pack(plan, *self.streams[x], joint=j[x], rope=in_pack and x != "v")
         pvj.varlen_attn_fwd(plan, j["q"], j["k"], j["v"], rope_fused=not in_pack, out=j["o"],
                             lse=self.lse)
         pvj.unpack(plan, j["o"], *self.out_streams["o"])
-        if wl.backward:
+        if self.backward:
             pvj.pack(plan, *self.streams["do"], joint=j["do"])
             pvj.varlen_attn_bwd(plan, j["q"], j["k"], j["v"], j["o"], self.lse, j["do"],
                                 rope_fused=not in_pack, rope_prerotated=in_pack,
@@ -110,18 +120,16 @@ class PackStep:
         self.plan = plan
 
 
-def pack_bench(name, steps, warmup=2):
-    """One of the other packs (the multi-prompt CFG inference pack, the 1024^2
-    CFG pack, the extreme-shape pack, the two-frame editing pack with 3-axis
-    RoPE), timed like the main step: plan, pack with
-    RoPE, attention forward, unpack O, and for training packs pack dO, attention
-    backward and unpack the gradients.  Reports the step rate and the attention
-    kernels' own rate (events on the launch stream)."""
+def _sum_len_sq(plan, n):
+    cu = plan.cu_seqlens
+    return float(sum((cu[i + 1] - cu[i]) ** 2 for i in range(n)))
+
+
+def time_step(step, steps, warmup):
+    """Mean wall time of `steps` steps (synchronised around the loop) and the
+    attention kernels' mean times per step (HIP events on the launch stream)."""
     import torch
-    import packed_varlen_joint_amd as pvj
-    from pvj_inputs import workload
-    wl = workload(name)
-    step = PackStep(wl, 0)
+    pvj = step.pvj
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -137,17 +145,125 @@ def pack_bench(name, steps, warmup=2):
         if n:
             kms[k] = tot / steps
     pvj.profile_enable(False)
-    cu = step.plan.cu_seqlens
-    S2 = float(sum((cu[i + 1] - cu[i]) ** 2 for i in range(len(wl.samples))))
-    f = (14.0 if wl.backward else 4.0) * wl.n_heads * wl.head_dim * S2
+    return ms, kms
+
+
+def pack_bench(name, steps, warmup=2, seed=0, backward=None, reuse_plan=False):
+    """One of the other packs (the multi-prompt CFG inference pack, the 1024^2
+    packs, the extreme-shape pack, the two-frame editing pack with 3-axis
+    RoPE, other training-pack seeds), timed like the main step: plan, pack
+    with RoPE, attention forward, unpack O, and for training packs pack dO,
+    attention backward and unpack the gradients.  Reports the step rate and
+    the attention kernels' own rate (events on the launch stream)."""
+    from pvj_inputs import workload
+    wl = workload(name, seed)
+    step = PackStep(wl, seed, backward=backward, reuse_plan=reuse_plan)
+    ms, kms = time_step(step, steps, warmup)
+    S2 = _sum_len_sq(step.plan, len(wl.samples))
+    bwd = step.backward
+    f = (14.0 if bwd else 4.0) * wl.n_heads * wl.head_dim * S2
     kt = sum(kms.values())
-    return {"workload": wl.name, "n_samples": len(wl.samples), "n_tokens": wl.n_tokens,
-            "backward": wl.backward, "ms_per_step": round(ms, 4),
-            "tflops": round(f / (ms * 1e-3) / 1e12, 2),
-            "attn_kernel_tflops": round(f / (kt * 1e-3) / 1e12, 2) if kt else None,
-            "attn_kernel_frac_of_peak": round(f / (kt * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-            if kt else None,
-            "tokens_per_s": round(wl.n_tokens / (ms * 1e-3), 1)}
+    out = {"workload": wl.name, "seed": seed, "n_samples": len(wl.samples),
+           "n_tokens": wl.n_tokens, "sum_len_sq": int(S2), "backward": bwd,
+           "plan": "built once, reused" if reuse_plan else "built every step",
+           "ms_per_step": round(ms, 4),
+           "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+           "attn_kernel_ms": round(kt, 4) if kt else None,
+           "attn_kernel_tflops": round(f / (kt * 1e-3) / 1e12, 2) if kt else None,
+           "attn_kernel_frac_of_peak": round(f / (kt * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+           if kt else None,
+           "tokens_per_s": round(wl.n_tokens / (ms * 1e-3), 1)}
+    if "attn_fwd" in kms:
+        out["fwd_ms"] = round(kms["attn_fwd"], 4)
+        out["fwd_tflops"] = round(4.0 * wl.n_heads * wl.head_dim * S2 /
+                                  (kms["attn_fwd"] * 1e-3) / 1e12, 2)
+    if bwd and "attn_bwd" in kms and "attn_bwd_dq" in kms:
+        tb = kms["attn_bwd"] + kms["attn_bwd_dq"]
+        out["bwd_ms"] = round(tb, 4)
+        out["bwd_tflops"] = round(10.0 * wl.n_heads * wl.head_dim * S2 / (tb * 1e-3) / 1e12, 2)
+    return out
+
+
+def seeds_bench(name, seeds, steps, warmup=2):
+    """The training pack for several draws (seeds), forward + backward, and the
+    mean of the per-seed rates."""
+    import torch
+    per = []
+    for sd in seeds:
+        per.append(pack_bench(name, steps, warmup, seed=sd))
+        torch.cuda.empty_cache()
+    keys = ("ms_per_step", "tflops", "attn_kernel_tflops", "attn_kernel_frac_of_peak",
+            "fwd_tflops", "bwd_tflops", "tokens_per_s", "n_tokens")
+    mean = {k: round(sum(r[k] for r in per) / len(per), 4) for k in keys}
+    return {"per_seed": per, "mean": mean}
+
+
+def cfg_packed_vs_separate(steps, warmup=2):
+    """The 1024^2 CFG pack (cond + uncond in one pack) against the two samples
+    as separate single-sample calls, each a full forward step (plan, pack with
+    RoPE, forward, unpack); kernel-level and step-level times and their ratio
+    (separate / packed)."""
+    from pvj_inputs import workload, Workload
+    wl = workload("cfg_1024")
+    packed = PackStep(wl, 0)
+    parts = [PackStep(Workload("cfg_1024_part%d" % i, [s], wl.n_heads, wl.head_dim, wl.dtype,
+                               False, wl.seed), 0) for i, s in enumerate(wl.samples)]
+
+    def both():
+        for p in parts:
+            p()
+    both.pvj = packed.pvj
+    ms_p, k_p = time_step(packed, steps, warmup)
+    ms_s, k_s = time_step(both, steps, warmup)
+    kp, ks = k_p.get("attn_fwd", 0.0), k_s.get("attn_fwd", 0.0)
+    return {"packed_step_ms": round(ms_p, 4), "separate_step_ms": round(ms_s, 4),
+            "step_ratio": round(ms_s / ms_p, 4),
+            "packed_attn_kernel_ms": round(kp, 4), "separate_attn_kernel_ms": round(ks, 4),
+            "attn_kernel_ratio": round(ks / kp, 4) if kp else None,
+            "_note": "separate = the two samples as two single-sample plans and calls per step; "
+                     "ratio > 1 means the pack is faster"}
+
+
+def median_steps(step, n):
+    """Median, min and max of n individually synchronised steps (ms)."""
+    import torch
+    ts = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    ts.sort()
+    return {"n": n, "median_ms": round(ts[n // 2], 4), "min_ms": round(ts[0], 4),
+            "max_ms": round(ts[-1], 4), "total_s": round(sum(ts) / 1e3, 3)}
+
+
+def rope_bench(wl, reps):
+    """The standalone per-sample 2D RoPE kernel on one [T, H, D] tensor of the
+    pack (out of place): algorithmic bytes = one read and one write."""
+    import torch
+    import packed_varlen_joint_amd as pvj
+    plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+    dt = plan.torch_dtype
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn(plan.n_tokens, wl.n_heads, wl.head_dim, device="cuda", generator=g).to(dt)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        pvj.rope2d_apply(plan, x, y)
+    torch.cuda.synchronize()
+    pvj.profile_enable(True)
+    for _ in range(reps):
+        pvj.rope2d_apply(plan, x, y)
+    torch.cuda.synchronize()
+    tot, n = pvj.profile_read("rope2d")
+    pvj.profile_enable(False)
+    ms = tot / n
+    nbytes = 2 * x.numel() * x.element_size()
+    return {"ms": round(ms, 4), "bytes": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "_note": "[%d, %d, %d] %s, read + write once, mean of %d launches (events)" % (
+                plan.n_tokens, wl.n_heads, wl.head_dim, wl.dtype, reps)}
 
 
 def chain_bench(wl, reps):
@@ -296,6 +412,31 @@ def cpu_baseline(wl, seconds):
                       "workload pack, sample lengths %s, %.1f s" % (len(done), lens, dt)}
 
 
+def cpu_baseline_one_thread(seconds):
+    """The oracle's forward on the single 1024^2 sample (4,352 tokens), one BLAS
+    thread, head by head for about `seconds`."""
+    import numpy as np
+    import oracle
+    from pvj_inputs import draw_tensors, workload
+    from threadpoolctl import threadpool_limits
+    wl = workload("single_1024")
+    L = int(oracle.sample_lengths(wl.samples)[0])
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for h in range(wl.n_heads):
+            q, k, v = draw_tensors(L, 1, wl.head_dim, wl.dtype, 11 + h, n=3)
+            oracle.attn_fwd(q, k, v, wl.samples, rope=True)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    flops = 4.0 * wl.head_dim * L * L * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "fp64 oracle forward (RoPE) of %d of the 24 heads of the single 1024^2 "
+                      "sample (L = %d), one BLAS thread, %.1f s" % (done, L, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +454,9 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 512 MiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--only", choices=("rope", "cfg_1024", "single_1024", "infer_multi",
+                                       "extreme_fwd", "chains"),
+                    help="run just this measurement (for profiling) and print its JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the pack is one GPU's data-parallel share "
@@ -332,6 +476,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.only:
+        if args.only == "rope":
+            res = rope_bench(workload(args.workload, args.seed), 20)
+        elif args.only == "chains":
+            res = chain_bench(workload(args.workload, args.seed), 10)
+        elif args.only == "extreme_fwd":
+            res = pack_bench("extreme", args.steps, args.warmup, backward=False)
+        else:
+            res = pack_bench(args.only, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "result": res}), flush=True)
         return
     wl = workload(args.workload, args.seed)
     H, D = wl.n_heads, wl.head_dim
@@ -421,14 +576,32 @@ def main():
         ceil = pvj.diag_mfma_peak()
         roof["measured_ceiling"] = round(ceil, 1)
         roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
+    # the same step, 50 times, each synchronised and timed on its own
+    out["median_of_50_steps"] = median_steps(step, 50)
+    del step
+    torch.cuda.empty_cache()
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
+        out["rope_standalone"] = rope_bench(wl, 20)
         out["inference"] = pack_bench("infer_multi", 5)
-        out["other_packs"] = {n: pack_bench(n, 5) for n in ("cfg_1024", "extreme", "edit_1024")}
+        out["inference_reused_plan"] = pack_bench("infer_multi", 5, reuse_plan=True)
+        out["other_packs"] = {
+            "cfg_1024": pack_bench("cfg_1024", 20),
+            "cfg_1024_reused_plan": pack_bench("cfg_1024", 20, reuse_plan=True),
+            "single_1024": pack_bench("single_1024", 20),
+            "extreme": pack_bench("extreme", 5),
+            "extreme_fwd": pack_bench("extreme", 10, backward=False),
+            "edit_1024": pack_bench("edit_1024", 5),
+        }
+        out["cfg_packed_vs_separate"] = cfg_packed_vs_separate(20)
+        if args.workload == "train_64k":
+            out["train_64k_seeds"] = seeds_bench("train_64k", range(5), 10)
+        torch.cuda.empty_cache()
         if wl.dtype == "bf16":
             out["projections"] = proj_bench(wl, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline_one_thread"] = cpu_baseline_one_thread(5.0)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -396,37 +396,6 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
 // ---------------------------------------------------------------------------
 constexpr int kPpAhead = 4;  // operand fragments in flight ahead of the products
 
-// Scheduling groups of one M phase: N ops, the first NS of them score
-// products (one LDS read per operand), the rest output products (two
-// transposing reads per operand).  First the reads of the first AHEAD ops,
-// then per op its product and the reads of the op AHEAD further on.
-__host__ __device__ constexpr int pp_reads(int i, int ns) { return i < ns ? 1 : 2; }
-__host__ __device__ constexpr int pp_first_reads(int n, int ns, int ahead) {
-  int r = 0;
-  for (int i = 0; i < ahead && i < n; ++i) r += pp_reads(i, ns);
-  return r;
-}
-// Op i of N is followed by a tile copy instruction when pp_copy_after(i, N,
-// NC) (NC copies spread evenly over the N products).
-__host__ __device__ constexpr bool pp_copy_after(int i, int n, int nc) {
-  return nc > 0 && ((i + 1) * nc) / n != (i * nc) / n;
-}
-template <int I, int N, int NS, int AHEAD, int NC>
-__device__ __forceinline__ void pp_sched_ops() {
-  if constexpr (I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (I + AHEAD < N)
-      __builtin_amdgcn_sched_group_barrier(0x100, pp_reads(I + AHEAD, NS), 0);
-    if constexpr (pp_copy_after(I, N, NC)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    pp_sched_ops<I + 1, N, NS, AHEAD, NC>();
-  }
-}
-template <int N, int NS, int AHEAD, int NC>
-__device__ __forceinline__ void pp_sched() {
-  __builtin_amdgcn_sched_group_barrier(0x100, pp_first_reads(N, NS, AHEAD), 0);
-  pp_sched_ops<0, N, NS, AHEAD, NC>();
-}
-
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ K,
@@ -559,7 +528,7 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
         copy_part(k + 1, std::integral_constant<int, B ^ 1>{}, ((i + 1) * NCH) / N - 1);
     }
     // keep the reads kPpAhead ops ahead of the products, the copies spread
-    pp_sched<N, NS, kPpAhead, NCH>();
+    pp_sched<N, NS, N, kPpAhead, NCH>();
   };
 
   // V(k): online softmax of S_k (base 2, lazy rescale; see the kernel above)

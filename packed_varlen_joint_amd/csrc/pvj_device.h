@@ -302,5 +302,39 @@ __device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::copy(void* tile, Src 
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Scheduling groups of one product phase of the phase-shifted attention
+// kernels: N products, of which those in [D0, D1) read their operand with two
+// transposing reads (ds_read_b64_tr_b16) and the others with one row read
+// (ds_read_b128).  First the reads of the first AHEAD products, then per
+// product the product and the reads of the product AHEAD further on, and
+// after some products one tile copy instruction (NC spread evenly).
+__host__ __device__ constexpr int pp_reads(int i, int d0, int d1) {
+  return (i >= d0 && i < d1) ? 2 : 1;
+}
+__host__ __device__ constexpr int pp_first_reads(int n, int d0, int d1, int ahead) {
+  int r = 0;
+  for (int i = 0; i < ahead && i < n; ++i) r += pp_reads(i, d0, d1);
+  return r;
+}
+// Product i of N is followed by a tile copy instruction when pp_copy_after(i,
+// N, NC) (NC copies spread evenly over the N products).
+__host__ __device__ constexpr bool pp_copy_after(int i, int n, int nc) {
+  return nc > 0 && ((i + 1) * nc) / n != (i * nc) / n;
+}
+template <int I, int N, int D0, int D1, int AHEAD, int NC>
+__device__ __forceinline__ void pp_sched_ops() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + AHEAD < N)
+      __builtin_amdgcn_sched_group_barrier(0x100, pp_reads(I + AHEAD, D0, D1), 0);
+    if constexpr (pp_copy_after(I, N, NC)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pp_sched_ops<I + 1, N, D0, D1, AHEAD, NC>();
+  }
+}
+template <int N, int D0, int D1, int AHEAD, int NC>
+__device__ __forceinline__ void pp_sched() {
+  __builtin_amdgcn_sched_group_barrier(0x100, pp_first_reads(N, D0, D1, AHEAD), 0);
+  pp_sched_ops<0, N, D0, D1, AHEAD, NC>();
+}
 
 }  // namespace pvj
