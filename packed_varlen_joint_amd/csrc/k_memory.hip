@@ -312,6 +312,54 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __re
   }
 }
 
+// Delta alone (no RoPE): a plain streaming read of O and dO.  Each wave takes
+// NB consecutive groups of 64 units; the D/8 lanes of one (token, head) row
+// are consecutive and sum their dot products with DPP inside the 16-lane row
+// (no LDS); one lane per (token, head) stores Delta[h, t].  No per-row
+// bookkeeping: Delta does not depend on the sample.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <typename T, int D, int NB>
+__global__ __launch_bounds__(kThreads) void delta_kernel(const T* __restrict__ o,
+                                                         const T* __restrict__ dout,
+                                                         float* __restrict__ delta, int n_tokens,
+                                                         int n_heads) {
+  constexpr int UPH = D / 8;    // units per (token, head) row: 16 or 8
+  constexpr int RPG = 64 / UPH;  // rows per group of 64 units
+  const int lane = threadIdx.x & 63;
+  const long n_rows = (long)n_tokens * n_heads;
+  const long g0 = ((long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * NB;
+  f32x8 a[NB], b[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const long hr = (g0 + k) * RPG + lane / UPH;
+    a[k] = f32x8{};
+    b[k] = f32x8{};
+    if (hr < n_rows) {
+      const size_t off = (size_t)hr * D + (size_t)(lane % UPH) * 8;
+      a[k] = to_f32x8(load8<T>(o + off));
+      b[k] = to_f32x8(load8<T>(dout + off));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += a[k][i] * b[k][i];
+    sum += dpp_f<0xB1>(sum);    // quad_perm 1,0,3,2
+    sum += dpp_f<0x4E>(sum);    // quad_perm 2,3,0,1
+    sum += dpp_f<0x141>(sum);   // row_half_mirror: the other quad of 8 lanes
+    if (UPH == 16) sum += dpp_f<0x140>(sum);  // row_mirror: the other 8 of 16
+    const long hr = (g0 + k) * RPG + lane / UPH;
+    if (lane % UPH == 0 && hr < n_rows) {
+      const int t = (int)(hr / n_heads), h = (int)(hr - (long)t * n_heads);
+      delta[(size_t)h * n_tokens + t] = sum;
+    }
+  }
+}
+
 template <typename T, bool ROPE>
 static void pre_b(const Meta& m, BlockShape bs, dim3 grid, const void* o, const void* dout,
                   const void* q, const void* k, float* delta, void* qr, void* kr,
@@ -333,6 +381,20 @@ hipError_t launch_bwd_pre(const pvj_plan* p, const Meta& m, const void* o, const
                           bool rope, hipStream_t stream) {
   if (m.n_tokens == 0) return hipSuccess;
   const bool bf = p->desc.dtype == PVJ_BF16;
+  if (!rope) {
+    constexpr int NB = 4;  // groups of 64 units per wave
+    const long units = (long)m.n_tokens * m.n_heads * m.head_dim / 8;
+    const dim3 g((unsigned)((units + 64L * NB * (kThreads / 64) - 1) / (64L * NB * (kThreads / 64))));
+#define PVJ_DELTA(TT, DD)                                                                   \
+  delta_kernel<TT, DD, NB><<<g, kThreads, 0, stream>>>((const TT*)o, (const TT*)dout, delta, \
+                                                        m.n_tokens, m.n_heads)
+    if (bf && m.head_dim == 128) PVJ_DELTA(bf16, 128);
+    else if (bf) PVJ_DELTA(bf16, 64);
+    else if (m.head_dim == 128) PVJ_DELTA(float, 128);
+    else PVJ_DELTA(float, 64);
+#undef PVJ_DELTA
+    return hipGetLastError();
+  }
   const BlockShape bs = block_shape(m, bf ? 2 : 4);
   const dim3 grid((m.n_tokens + bs.rows - 1) / bs.rows);
   if (bf) {
