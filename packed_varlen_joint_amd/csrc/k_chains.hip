@@ -58,6 +58,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <typename T>
 __device__ __forceinline__ f32x8 ld8f(const T* p) { return to_f32x8(load8<T>(p)); }
 
+// row outputs are written once and not read again here: non-temporal stores
+template <typename T>
+__device__ __forceinline__ void st8nt(T* p, f32x8 v) {
+  __builtin_nontemporal_store(from_f32x8<T>(v), reinterpret_cast<typename Vec8<T>::type*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // forward: adaptive layer norm
 // ---------------------------------------------------------------------------
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kChainThreads) void adaln_fwd_kernel(
       f32x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (v[k][e] - mean) * rstd * (1.f + a[e]) + b[e];
-      store8<T>(yr + u * 8, from_f32x8<T>(o));
+      st8nt<T>(yr + u * 8, o);
     }
   }
 }
@@ -137,14 +143,30 @@ __global__ __launch_bounds__(kChainThreads) void gate_fwd_kernel(
   }
   const int s = find_sample(cu, n_samples, row);
   const T* g = gate + (size_t)s * C;
-  for (int u = lane; u < upr; u += 64) {
-    const f32x8 a = u == lane ? to_f32x8(x0) : ld8f(x + ro + u * 8);
-    const f32x8 b = u == lane ? to_f32x8(y0) : ld8f(y + ro + u * 8);
-    const f32x8 w = ld8f(g + u * 8);
-    f32x8 o;
+  // four units per lane at a time: all their loads go out before the stores
+  // (out may be x or y: every element is read before this lane writes it)
+  for (int u0 = lane; u0 < upr; u0 += 256) {
+    typename Vec8<T>::type a[4], b[4], w[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = a[e] + w[e] * b[e];
-    store8<T>(out + ro + u * 8, from_f32x8<T>(o));
+    for (int k = 0; k < 4; ++k) {
+      const int u = u0 + 64 * k;
+      typename Vec8<T>::type z = {};
+      a[k] = u < upr ? (u == lane ? x0 : load8<T>(x + ro + u * 8)) : z;
+      b[k] = u < upr ? (u == lane ? y0 : load8<T>(y + ro + u * 8)) : z;
+      w[k] = u < upr ? load8<T>(g + u * 8) : z;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = u0 + 64 * k;
+      if (u < upr) {
+        const f32x8 fa = to_f32x8(a[k]), fb = to_f32x8(b[k]), fw = to_f32x8(w[k]);
+        f32x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fa[e] + fw[e] * fb[e];
+        st8nt<T>(out + ro + u * 8, o);
+      }
+    }
   }
 }
 
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_rows_kernel(
       f32x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = rstd * (g[k][e] - mg - v[k][e] * mgx);
-      store8<T>(dx + ro + u * 8, from_f32x8<T>(o));
+      st8nt<T>(dx + ro + u * 8, o);
     }
   }
   if (lane == 0) stats[row] = make_float2(mean, rstd);
@@ -328,7 +350,7 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
         f32x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = rstd * (dd[e] * (1.f + a[e]) - mg - v[k][e] * mgx);
-        store8<T>(dx + ro + u * 8, from_f32x8<T>(o));
+        st8nt<T>(dx + ro + u * 8, o);
       }
     }
   }
@@ -399,10 +421,7 @@ __global__ __launch_bounds__(64) void seg_partial_kernel(
   const int col = chunk * kColChunk + threadIdx.x * 8;
   if (col >= C) return;
   f32x8 acc0[2] = {}, acc1[2] = {};
-  auto row = [&](int r, int k) {
-    const size_t o = (size_t)r * C + col;
-    const f32x8 va = ld8f(x + o), vb = ld8f(dy + o);
-    const float2 st = stats[r];
+  auto add = [&](int k, const f32x8& va, const f32x8& vb, float2 st) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       acc0[k][e] += vb[e];
@@ -411,10 +430,24 @@ __global__ __launch_bounds__(64) void seg_partial_kernel(
   };
   int r = lo;
   for (; r + 4 <= hi; r += 4) {
+    f32x8 va[4], vb[4];
+    float2 st[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) row(r + k, k & 1);
+    for (int k = 0; k < 4; ++k) {
+      const size_t o = (size_t)(r + k) * C + col;
+      va[k] = ld8f(x + o);
+      vb[k] = ld8f(dy + o);
+      st[k] = stats[r + k];
+    }
+    // the four rows' loads stay ahead of their uses (see gate_bwd_slots_kernel)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add(k & 1, va[k], vb[k], st[k]);
   }
-  for (; r < hi; ++r) row(r, 0);
+  for (; r < hi; ++r) {
+    const size_t o = (size_t)r * C + col;
+    add(0, ld8f(x + o), ld8f(dy + o), stats[r]);
+  }
   const size_t po = ((size_t)s * splits + split) * C + col;
   *reinterpret_cast<f32x8*>(partial + po) = acc0[0] + acc0[1];
   *reinterpret_cast<f32x8*>(partial + (size_t)n_samples * splits * C + po) = acc1[0] + acc1[1];
@@ -437,23 +470,41 @@ __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
   if (lo >= hi || col >= C) return;
   f32x8 acc[2] = {};
   const f32x8 w = ld8f(gate + (size_t)s * C + col);
-  auto row = [&](int r, int k) {
+  // four rows' loads go out before their stores
+  int r = lo;
+  for (; r + 4 <= hi; r += 4) {
+    f32x8 va[4], vb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t o = (size_t)(r + k) * C + col;
+      va[k] = ld8f(dout + o);
+      vb[k] = ld8f(y + o);
+    }
+    // (without this fence the scheduler sinks each load to its first use and
+    // waits for it there: one request in flight per wave)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f32x8 d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[k & 1][e] += va[k][e] * vb[k][e];
+        d[e] = w[e] * va[k][e];
+      }
+      st8nt<T>(dy + (size_t)(r + k) * C + col, d);
+    }
+  }
+  for (; r < hi; ++r) {
     const size_t o = (size_t)r * C + col;
     const f32x8 va = ld8f(dout + o), vb = ld8f(y + o);
     f32x8 d;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      acc[k][e] += va[e] * vb[e];
+      acc[0][e] += va[e] * vb[e];
       d[e] = w[e] * va[e];
     }
-    store8<T>(dy + o, from_f32x8<T>(d));
-  };
-  int r = lo;
-  for (; r + 4 <= hi; r += 4) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) row(r + k, k & 1);
+    st8nt<T>(dy + o, d);
   }
-  for (; r < hi; ++r) row(r, 0);
   *reinterpret_cast<f32x8*>(partial + (size_t)slot * C + col) = acc[0] + acc[1];
 }
 
