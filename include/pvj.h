@@ -127,7 +127,10 @@ PVJ_API pvj_status_t pvj_plan_create_frames(const pvj_sample_frames_t* samples, 
 
 /* Sizes of a plan.  Any output pointer may be NULL.  *cu_seqlens_host points
  * into the plan (B+1 int32, valid until destroy); *meta_bytes is the size of
- * the device metadata buffer pvj_plan_upload needs. */
+ * the device metadata buffer pvj_plan_upload needs: the metadata itself, then
+ * (bf16 plans with samples of 1,985 to 8,192 tokens) the partial-result slots
+ * of the forward's split query tiles, (head_dim + 2) * 256 * 4 bytes each (see
+ * pvj_varlen_attn_fwd). */
 PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* plan, int64_t* n_tokens, int32_t* max_len,
                                    const int32_t** cu_seqlens_host, size_t* meta_bytes);
 
@@ -139,8 +142,10 @@ PVJ_API pvj_status_t pvj_plan_streams(const pvj_plan_t* plan, int64_t* n_text, i
 
 /* Copy the plan's metadata into the caller-allocated device buffer `dev_meta`
  * (>= meta_bytes, 256-byte aligned) on `stream`, and record it in the plan.
- * Compute calls on this plan then read that buffer; it must stay allocated and
- * unmodified while they run.  Calling it again re-targets the plan. */
+ * Compute calls on this plan then read that buffer (and the forward writes its
+ * partial-result slots, which are not uploaded and need no initialisation); it
+ * must stay allocated and otherwise unmodified while they run.  Calling it
+ * again re-targets the plan. */
 PVJ_API pvj_status_t pvj_plan_upload(pvj_plan_t* plan, void* dev_meta, size_t bytes, void* stream);
 
 /* Free the plan (host memory only).  Work already enqueued that uses the plan's
@@ -195,6 +200,13 @@ PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* plan, const void* x, voi
  * fp32 accumulation and fp32 online softmax; fp32 inputs use fp32 matrix cores.
  * o must not overlap q, k, v.  Deterministic: the same inputs give the same
  * bits, and a sample's result does not depend on the rest of the pack.
+ * Work split (bf16 plans): the last 256-query tile of each (sample, head) of a
+ * sample of 1,985 to 8,192 tokens (32 to 128 tiles of 64 keys) is computed as
+ * min(4, floor(tiles / 16)) ranges of its keys (a function of the sample
+ * length only) whose partial softmax states go to the
+ * plan buffer's slots and are merged in a fixed order by a second kernel on
+ * the same stream; so two forward calls on one uploaded plan must not run at
+ * the same time (on different streams).
  */
 PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* plan, const void* q, const void* k,
                                          const void* v, void* o, float* lse,
@@ -304,10 +316,15 @@ PVJ_API pvj_status_t pvj_gate_residual_bwd(const pvj_plan_t* plan, int32_t which
 
 /* ---- introspection (pure host; used by tests and tooling) -------------------- */
 
-/* Attention work list of the plan: which = 0 forward, 1 backward.  *items
- * points to n_items int32 quadruples {sample, head, tile, 0} in launch order
- * (sample = -1 marks an idle slot); *tile_rows is the rows of one tile
- * (query rows forward, key rows backward).  Valid until destroy. */
+/* Attention work list of the plan: which = 0 forward, 1 backward dK/dV, 2
+ * backward dQ (the forward's query tiles, none split), 3 the forward's split
+ * tiles.  *items points to n_items int32 quadruples {sample, head, tile,
+ * split} in launch order (sample = -1 marks an idle slot); split = 0 for a
+ * whole tile, else bits 0-3 = parts - 1, bits 4-7 = this part (lists 0), bits
+ * 8-31 = the tile's first partial-result slot; part j of n covers key tiles
+ * [nkt j / n, nkt (j + 1) / n) of 64 keys, nkt = ceil(L / 64).  *tile_rows is
+ * the rows of one tile (query rows forward and dQ, key rows dK/dV).  Valid
+ * until destroy. */
 PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* plan, int32_t which,
                                          const int32_t** items, int32_t* n_items,
                                          int32_t* tile_rows);

@@ -226,7 +226,8 @@ class Plan:
         return self
 
     def work_items(self, which: int):
-        """(items [n][4] list, tile_rows) of the forward (0) or backward (1) work list."""
+        """(items [n][4] list, tile_rows) of a work list: 0 forward (with split
+        tiles), 1 backward dK/dV, 2 backward dQ, 3 the forward's split tiles."""
         lib = load_library()
         p = ctypes.POINTER(ctypes.c_int32)()
         n = ctypes.c_int32()

@@ -27,7 +27,7 @@ constexpr int kDqBN = 64;  // keys per streamed tile
 
 template <typename T, int D>
 struct DqCfg {
-  // queries per workgroup = the forward tile (the kernel walks fwd_items):
+  // queries per workgroup = the forward tile (the kernel walks dq_items):
   // bf16 8 waves x 32 queries share each K'/V tile copy; fp32 4 waves
   static constexpr int BM = sizeof(T) == 2 ? 256 : 128;
   static constexpr int THREADS = BM * 2;
@@ -52,7 +52,7 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   auto ks_of = [&](int b) { return b ? k_b1 : k_b0; };
   auto vs_of = [&](int b) { return b ? v_b1 : v_b0; };
 
-  const Item it = m.fwd_items[blockIdx.x];
+  const Item it = m.dq_items[blockIdx.x];
   if (it.sample < 0) return;
   const SampleInfo si = m.sinfo[it.sample];
   const int L = si.len;
@@ -288,8 +288,8 @@ template <typename T, int D>
 static hipError_t launch_dq_t(const Meta& m, const void* q, const void* k, const void* v,
                               const void* dout, const float* lse, const float* delta, void* dq,
                               float scale, bool rope, hipStream_t stream) {
-  if (m.n_fwd > 0)
-    attn_bwd_dq_kernel<T, D><<<dim3(m.n_fwd), dim3(DqCfg<T, D>::THREADS), 0, stream>>>(
+  if (m.n_dq > 0)
+    attn_bwd_dq_kernel<T, D><<<dim3(m.n_dq), dim3(DqCfg<T, D>::THREADS), 0, stream>>>(
         m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
         scale * 1.4426950408889634f, rope ? 1 : 0);
   return hipGetLastError();

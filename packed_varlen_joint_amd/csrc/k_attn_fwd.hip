@@ -54,6 +54,27 @@ struct FwdTile {
   static constexpr int TILE = kFwdBN * D;
 };
 
+// Partial state of one key range of a split tile (bf16, 256 queries): O^T
+// unnormalised at slot[d * 256 + q], the reference max m (base 2) at
+// slot[D * 256 + q] and the sum l at slot[(D + 1) * 256 + q], for every query
+// q of the tile (rows past the sample end too; the merge skips them).  Lane
+// (l32, hi) of wave w holds query 32 w + l32 and the d of its accumulators.
+template <int DB>
+__device__ __forceinline__ void store_partial(float* slot, int ql, int hi, const f32x16 (&oacc)[DB],
+                                              float m_run, float l_tot) {
+  constexpr int D = DB * 32;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) slot[(db * 32 + 8 * g + 4 * hi + e) * 256 + ql] = oacc[db][4 * g + e];
+  if (hi == 0) {
+    slot[D * 256 + ql] = m_run;
+    slot[(D + 1) * 256 + ql] = l_tot;
+  }
+}
+
 // bf16 runs two waves per SIMD (one 8-wave workgroup per CU), so one wave's
 // softmax VALU work overlaps the other's matrix-core work.
 template <typename T, int D, bool ROPE>
@@ -174,9 +195,13 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
   };
   auto sig = [](int k) { return bsigma(k); };
 
+  // key tiles [kt0, kt1) of this item: all of them, or one part of a split tile
   const int nkv = (L + kFwdBN - 1) / kFwdBN;
-  load_tile(0, std::integral_constant<int, 0>{});
-  store_tile(0, std::integral_constant<int, 0>{});
+  const int kt0 = it.split ? fwd_split_begin(nkv, split_part(it.split), split_parts(it.split)) : 0;
+  const int kt1 =
+      it.split ? fwd_split_begin(nkv, split_part(it.split) + 1, split_parts(it.split)) : nkv;
+  load_tile(kt0 * kFwdBN, std::integral_constant<int, 0>{});
+  store_tile(kt0 * kFwdBN, std::integral_constant<int, 0>{});
   __syncthreads();
 
   f32x16 oacc[DB];
@@ -212,7 +237,7 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
     constexpr int B = decltype(bc)::value;
     constexpr bool MASK = decltype(mc)::value;
     const int kv0 = j * kFwdBN;
-    if (j + 1 < nkv) load_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
+    if (j + 1 < kt1) load_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
     const T* ks = B ? k_b1 : k_b0;
     const T* vs = B ? v_b1 : v_b0;
 
@@ -317,7 +342,7 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
         if (i < 4 * DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
-    if (j + 1 < nkv) store_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
+    if (j + 1 < kt1) store_tile(kv0 + kFwdBN, std::integral_constant<int, B ^ 1>{});
     __syncthreads();
   };
   // full tiles in pairs (buffers 0, 1), then a leftover full tile, then the
@@ -326,23 +351,31 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
   typedef std::integral_constant<int, 1> B1;
   typedef std::integral_constant<bool, false> NoMask;
   typedef std::integral_constant<bool, true> Mask;
-  const int nfull = L / kFwdBN;
-  int j = 0;
-  for (; j + 1 < nfull; j += 2) {
+  const int jf = min(kt1, L / kFwdBN);  // tiles [kt0, jf) need no mask
+  int j = kt0;
+  for (; j + 1 < jf; j += 2) {
     step(j, B0{}, NoMask{});
     step(j + 1, B1{}, NoMask{});
   }
-  if (j < nfull) {
+  if (j < jf) {
     step(j, B0{}, NoMask{});
     ++j;
   }
-  if (j < nkv) {
-    if (j & 1) step(j, B1{}, Mask{});
+  if (j < kt1) {
+    if ((j - kt0) & 1) step(j, B1{}, Mask{});
     else step(j, B0{}, Mask{});
   }
 
-  // ---- epilogue: O = O^T / l, LSE ----
+  // ---- epilogue: O = O^T / l, LSE (a split part: its partial state) ----
   const float l_tot = sum_pair32(l_run);
+  if constexpr (sizeof(T) == 2) {
+    if (it.split) {
+      store_partial<DB>(m.fwd_part + (size_t)(split_slot(it.split) + split_part(it.split)) *
+                                         fwd_part_floats(D),
+                        wave * 32 + l32, hi, oacc, m_run, l_tot);
+      return;
+    }
+  }
   if (qi < L) {
     const float inv = 1.f / l_tot;
     T* orow = Oh + (size_t)qi * RS;
@@ -434,8 +467,17 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   typedef DmaTile<D, kFwdBN, THREADS / 2> DT;
   constexpr int NC = 2 * DT::PER;  // copy instructions per set and wave
   const DT dma(RS);
-  const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
-  const int n = (L + kFwdBN - 1) / kFwdBN;  // key tiles
+  // key tiles kt0 .. kt1 - 1 of the sample: all of them, or one part of a split
+  // tile.  Keys are counted from the first one of the part (k below counts
+  // tiles from kt0): Lk keys of the sample lie at or after it.
+  const int nkv = (L + kFwdBN - 1) / kFwdBN;
+  const int kt0 = it.split ? fwd_split_begin(nkv, split_part(it.split), split_parts(it.split)) : 0;
+  const int kt1 =
+      it.split ? fwd_split_begin(nkv, split_part(it.split) + 1, split_parts(it.split)) : nkv;
+  const int n = kt1 - kt0;
+  const int Lk = L - kt0 * kFwdBN;
+  const size_t kbase = base + (size_t)kt0 * kFwdBN * RS;
+  const typename DT::Src rk = DT::src(K + kbase, RS, Lk), rv = DT::src(V + kbase, RS, Lk);
   // copy instruction c of set k into buffer pair B: c < PER copies part c of
   // K_k, the rest part c - PER of V_{k-1}.  A tile at or past the sample end
   // gets an empty buffer resource (it reads zeros, into a buffer no later
@@ -541,7 +583,7 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-          if (key >= L) sacc[kb][r] = -INFINITY;
+          if (key >= Lk) sacc[kb][r] = -INFINITY;
         }
     }
     float mx4[4];
@@ -614,7 +656,7 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   };
   // k = 0: scores only; full tiles 1 .. n-2 in pairs (buffers 1, 0); the last
   // key tile n-1 (masked when partial); k = n: the last output product only
-  const bool tail_mask = (L % kFwdBN) != 0;
+  const bool tail_mask = kt1 == nkv && (L % kFwdBN) != 0;
   auto run = [&](auto gc) __attribute__((always_inline)) {
     if (n == 1) {
       if (tail_mask) iter(gc, 0, B0{}, Tr{}, F{}, Tr{}, Tr{});
@@ -652,8 +694,14 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   if (group == 0) run(std::integral_constant<int, 0>{});
   else run(std::integral_constant<int, 1>{});
 
-  // ---- epilogue: O = O^T / l, LSE ----
+  // ---- epilogue: O = O^T / l, LSE (a split part: its partial state) ----
   const float l_tot = sum_pair32(l_run);
+  if (it.split) {
+    store_partial<DB>(m.fwd_part + (size_t)(split_slot(it.split) + split_part(it.split)) *
+                                       fwd_part_floats(D),
+                      wave * 32 + l32, hi, oacc, m_run, l_tot);
+    return;
+  }
   if (qi < L) {
     const float inv = 1.f / l_tot;
     bf16* orow = O + base + (size_t)qi * RS;
@@ -673,6 +721,54 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   }
 }
 
+
+// Merge of the split tiles' partial states, in part order (so deterministic):
+// with M = max_j m_j and w_j = 2^(m_j - M), O = sum_j w_j O_j / sum_j w_j l_j
+// and LSE = (M + log2 sum_j w_j l_j) ln 2 (the online-softmax combination of
+// disjoint key ranges).  Grid: (split tile, 32 columns of the head dim); one
+// thread per query of the tile.
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(Meta m, bf16* __restrict__ O,
+                                                             float* __restrict__ LSE) {
+  constexpr size_t PS = (size_t)(D + 2) * 256;  // floats per slot
+  const Item st = m.split_tiles[blockIdx.x];
+  const int S = split_parts(st.split);
+  const float* part = m.fwd_part + (size_t)split_slot(st.split) * PS;
+  const SampleInfo si = m.sinfo[st.sample];
+  const int ql = threadIdx.x;
+  const int qi = st.tile * 256 + ql;
+  if (qi >= si.len) return;
+  const int d0 = blockIdx.y * 32;
+  float M = -INFINITY;  // (parts past S re-read the last one: loads issued together)
+#pragma unroll
+  for (int j = 0; j < kMaxFwdSplit; ++j) M = fmaxf(M, part[min(j, S - 1) * PS + D * 256 + ql]);
+  // one part at a time, its 32 loads issued together
+  float lt = 0.f, acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+  for (int j = 0; j < S; ++j) {
+    const float* pj = part + j * PS;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = pj[(size_t)(d0 + i) * 256 + ql];
+    const float wj = fast_exp2(pj[D * 256 + ql] - M);
+    lt += wj * pj[(D + 1) * 256 + ql];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] += wj * x[i];
+  }
+  const float inv = 1.f / lt;
+  bf16* orow = O + (size_t)(si.start + qi) * m.n_heads * D + (size_t)st.head * D + d0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    bf16x8 o8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] = (bf16)(acc[8 * c + e] * inv);
+    *reinterpret_cast<bf16x8*>(orow + 8 * c) = o8;
+  }
+  if (blockIdx.y == 0 && LSE)
+    LSE[(size_t)st.head * m.n_tokens + si.start + qi] = (M + __log2f(lt)) * 0.69314718055994531f;
+}
+
 template <typename T, int D, bool ROPE>
 static hipError_t launch_fwd_t(const Meta& m, const void* q, const void* k, const void* v, void* o,
                                float* lse, float scale_log2, hipStream_t stream) {
@@ -689,21 +785,29 @@ hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, cons
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int D = p->desc.head_dim;
 #define PVJ_FWD(TT, DD)                                                                    \
-  return rope ? launch_fwd_t<TT, DD, true>(m, q, k, v, o, lse, sl2, stream)                \
-              : launch_fwd_t<TT, DD, false>(m, q, k, v, o, lse, sl2, stream)
-  if (bf && !rope && (D == 128 || D == 64)) {
+  (rope ? launch_fwd_t<TT, DD, true>(m, q, k, v, o, lse, sl2, stream)                      \
+        : launch_fwd_t<TT, DD, false>(m, q, k, v, o, lse, sl2, stream))
+  hipError_t e = hipSuccess;
+  if (bf && !rope) {
     if (D == 128)
       attn_fwd_pp_kernel<128><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
           m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
     else
       attn_fwd_pp_kernel<64><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
           m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
-    return hipGetLastError();
+    e = hipGetLastError();
+  } else if (bf) {
+    e = D == 128 ? PVJ_FWD(bf16, 128) : PVJ_FWD(bf16, 64);
+  } else {
+    return D == 128 ? PVJ_FWD(float, 128) : PVJ_FWD(float, 64);
   }
-  if (bf && D == 128) PVJ_FWD(bf16, 128);
-  if (bf && D == 64) PVJ_FWD(bf16, 64);
-  if (!bf && D == 128) PVJ_FWD(float, 128);
-  PVJ_FWD(float, 64);
+  // split tiles (bf16 plans only): combine their parts
+  if (e != hipSuccess || m.n_split == 0) return e;
+  if (D == 128)
+    attn_fwd_merge_kernel<128><<<dim3(m.n_split, 4), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
+  else
+    attn_fwd_merge_kernel<64><<<dim3(m.n_split, 2), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
+  return hipGetLastError();
 #undef PVJ_FWD
 }
 

@@ -172,9 +172,9 @@ PVJ_API pvj_status_t pvj_plan_upload(pvj_plan_t* p, void* dev_meta, size_t bytes
   if (!dev_meta) return fail(PVJ_ERR_INVALID_ARG, "dev_meta is NULL");
   if (reinterpret_cast<uintptr_t>(dev_meta) % kMetaAlign)
     return fail(PVJ_ERR_INVALID_ARG, "dev_meta is not %zu-byte aligned", kMetaAlign);
-  if (bytes < p->image_bytes)
+  if (bytes < p->image_bytes + p->part_bytes)
     return fail(PVJ_ERR_WORKSPACE_TOO_SMALL, "metadata buffer %zu < %zu bytes", bytes,
-                p->image_bytes);
+                p->image_bytes + p->part_bytes);
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PVJ_ERR_HIP, "hipGetDevice failed");
   hipError_t e = hipMemcpyAsync(dev_meta, p->image, p->image_bytes, hipMemcpyHostToDevice,

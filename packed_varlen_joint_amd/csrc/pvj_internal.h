@@ -6,6 +6,14 @@
 
 #include "pvj.h"
 
+// helpers used by the host planner (a plain C++ translation unit) and by the
+// kernels alike
+#ifdef __HIP__
+#define PVJ_HD __host__ __device__
+#else
+#define PVJ_HD
+#endif
+
 namespace pvj {
 
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs; workgroups are dealt round-robin
@@ -24,8 +32,40 @@ inline int bwd_tile_rows(int dtype, int head_dim) {
 }
 
 struct Item {  // one attention work item; sample < 0 marks an idle slot
-  int32_t sample, head, tile, pad;
+  int32_t sample, head, tile;
+  // forward: 0 = the tile against all of its sample's keys; otherwise one key
+  // range of a split tile: bits 0-3 = parts - 1, bits 4-7 = this part, bits
+  // 8-31 = the tile's first partial-result slot.  Backward lists: 0.
+  int32_t split;
 };
+
+// Forward tail split.  The last query tile of a (sample, head) of a short
+// sample (L <= kFwdSplitMaxLen) is cut into up to kMaxFwdSplit ranges of
+// consecutive 64-key tiles (each >= kFwdSplitMinTiles tiles); the parts are
+// small items that fill the last round of a launch, and a merge pass combines
+// their partial softmax states.  Long samples' items run first in the
+// largest-first order, so splitting them would only add partial traffic.  The
+// part count depends on the sample length only, so a sample's result never
+// depends on the rest of the pack.  bf16 plans only.
+constexpr int kMaxFwdSplit = 4;
+constexpr int kFwdSplitMinTiles = 16;
+constexpr int kFwdSplitMaxLen = 8192;
+constexpr int kFwdKeyTile = 64;
+PVJ_HD inline int fwd_key_tiles(int32_t L) { return (L + kFwdKeyTile - 1) / kFwdKeyTile; }
+PVJ_HD inline int fwd_splits(int dtype, int32_t L) {
+  if (dtype != PVJ_BF16 || L > kFwdSplitMaxLen) return 1;
+  const int s = fwd_key_tiles(L) / kFwdSplitMinTiles;
+  return s < 1 ? 1 : (s > kMaxFwdSplit ? kMaxFwdSplit : s);
+}
+// key tiles [first, end) of part j of n parts over nkt key tiles
+// (nkt < 2^25 and j < 16: the product fits 32 bits)
+PVJ_HD inline int fwd_split_begin(int nkt, int j, int n) { return nkt * j / n; }
+PVJ_HD inline int split_parts(int32_t split) { return (split & 15) + 1; }
+PVJ_HD inline int split_part(int32_t split) { return (split >> 4) & 15; }
+PVJ_HD inline int split_slot(int32_t split) { return split >> 8; }
+// one partial-result slot: O^T unnormalised [D][256 queries], then the
+// reference max m (base 2) and the sum l of the 256 queries, fp32
+PVJ_HD inline size_t fwd_part_floats(int head_dim) { return (size_t)(head_dim + 2) * 256; }
 
 struct SampleInfo {  // per-sample metadata read by the kernels
   int32_t start;   // first packed row (cu_seqlens[i])
@@ -44,10 +84,13 @@ struct Meta {
   const SampleInfo* sinfo;  // [B]
   const float* cos_tab;     // [n_pos][n_pairs]
   const float* sin_tab;     // [n_pos][n_pairs]
-  const Item* fwd_items;    // [n_fwd]
-  const Item* bwd_items;    // [n_bwd]
+  const Item* fwd_items;    // [n_fwd] forward, with split tiles
+  const Item* bwd_items;    // [n_bwd] dK/dV
+  const Item* dq_items;     // [n_dq] dQ: the forward tiles, none split
+  const Item* split_tiles;  // [n_split] {sample, head, tile, slot << 8 | parts - 1}
+  float* fwd_part;          // partial-result slots of the split tiles
   int32_t n_samples, n_tokens, n_heads, head_dim;
-  int32_t n_pos, n_pairs, n_fwd, n_bwd;
+  int32_t n_pos, n_pairs, n_fwd, n_bwd, n_dq, n_split;
   int32_t fwd_tile, bwd_tile, n_text, n_img;
   // RoPE axis of head-dim unit u (dims 8u .. 8u+7): row if u < rope_u0, column
   // if u < rope_u1, frame otherwise
@@ -66,11 +109,14 @@ struct pvj_plan {
   int32_t rope_axes, rope_dims[3];
   int32_t n_text, n_img;
   int32_t fwd_tile, bwd_tile;
-  int32_t n_fwd, n_bwd;
-  // host image of the device metadata and section offsets into it
+  int32_t n_fwd, n_bwd, n_dq, n_split, n_slots;
+  // host image of the device metadata and section offsets into it; the device
+  // buffer continues past the image with the forward's partial-result slots
+  // (off_part, part_bytes), which are not uploaded
   uint8_t* image;
   size_t image_bytes;
   size_t off_cu, off_cu_text, off_cu_img, off_sinfo, off_cos, off_sin, off_fwd, off_bwd;
+  size_t off_dq, off_split, off_part, part_bytes;
   // device copy (set by pvj_plan_upload)
   void* dev_meta;
   int dev_id;

@@ -35,14 +35,19 @@ pvj_status_t fail(pvj_status_t st, const char* fmt, ...) {
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Work list for one attention pass.  An item is one tile of `tile_rows` rows of
-// one (sample, head); its cost is proportional to the sample length (every
-// item streams the whole sample on the other side).  Groups = (sample, head)
-// are dealt to the 8 XCDs greedily, largest cost first (LPT), so each group's
-// items share one XCD's L2 for the K/V (or Q/dO) they all stream.  Inside an
-// XCD the items run largest sample first.  Launch slot b runs on XCD b % 8,
-// so the per-XCD lists are interleaved, with idle slots (sample = -1) where a
-// list is shorter than the longest one.
-static std::vector<Item> build_items(const std::vector<int32_t>& len, int n_heads, int tile_rows) {
+// one (sample, head); its cost is proportional to the keys (or queries) it
+// streams on the other side: the whole sample, or for a forward split tile
+// (fwd_splits) the part's key range.  Groups = (sample, head) are dealt to
+// the 8 XCDs greedily, largest cost first (LPT), so each group's items share
+// one XCD's L2 for the K/V (or Q/dO) they all stream.  Inside an XCD the
+// items run largest cost first, so the split parts fill the end.  Launch slot
+// b runs on XCD b % 8, so the per-XCD lists are interleaved, with idle slots
+// (sample = -1) where a list is shorter than the longest one.  With `split`,
+// the split tiles are appended to *split_tiles and their partial-result
+// slots numbered from *n_slots on.
+static std::vector<Item> build_items(const std::vector<int32_t>& len, int n_heads, int tile_rows,
+                                     int dtype, bool split, std::vector<Item>* split_tiles,
+                                     int64_t* n_slots) {
   struct Group { int32_t sample, head, n_tiles; int64_t cost; };
   std::vector<Group> groups;
   for (int32_t i = 0; i < (int32_t)len.size(); ++i) {
@@ -55,22 +60,42 @@ static std::vector<Item> build_items(const std::vector<int32_t>& len, int n_head
     if (len[a.sample] != len[b.sample]) return len[a.sample] > len[b.sample];
     return false;
   });
-  std::vector<std::vector<Item>> per_xcd(kNumXcd);
+  struct Work { Item it; int64_t cost; };
+  std::vector<std::vector<Work>> per_xcd(kNumXcd);
   int64_t load[kNumXcd] = {0};
   for (const Group& g : groups) {
     int best = 0;
     for (int x = 1; x < kNumXcd; ++x)
       if (load[x] < load[best]) best = x;
     load[best] += g.cost;
-    for (int t = 0; t < g.n_tiles; ++t) per_xcd[best].push_back({g.sample, g.head, t, 0});
+    const int32_t L = len[g.sample];
+    const int S = split ? fwd_splits(dtype, L) : 1;
+    for (int t = 0; t < g.n_tiles; ++t) {
+      if (t + 1 < g.n_tiles || S == 1) {
+        per_xcd[best].push_back({{g.sample, g.head, t, 0}, L});
+        continue;
+      }
+      const int nkt = fwd_key_tiles(L);
+      const int32_t slot = (int32_t)*n_slots;
+      *n_slots += S;
+      split_tiles->push_back({g.sample, g.head, t, (slot << 8) | (S - 1)});
+      for (int j = 0; j < S; ++j) {
+        const int64_t k0 = (int64_t)fwd_split_begin(nkt, j, S) * kFwdKeyTile;
+        const int64_t k1 = std::min<int64_t>((int64_t)fwd_split_begin(nkt, j + 1, S) * kFwdKeyTile, L);
+        per_xcd[best].push_back({{g.sample, g.head, t, (slot << 8) | (j << 4) | (S - 1)}, k1 - k0});
+      }
+    }
   }
   size_t longest = 0;
-  for (auto& l : per_xcd) longest = std::max(longest, l.size());
+  for (auto& l : per_xcd) {
+    std::stable_sort(l.begin(), l.end(), [](const Work& a, const Work& b) { return a.cost > b.cost; });
+    longest = std::max(longest, l.size());
+  }
   std::vector<Item> out;
   out.reserve(longest * kNumXcd);
   for (size_t s = 0; s < longest; ++s)
     for (int x = 0; x < kNumXcd; ++x)
-      out.push_back(s < per_xcd[x].size() ? per_xcd[x][s] : Item{-1, 0, 0, 0});
+      out.push_back(s < per_xcd[x].size() ? per_xcd[x][s].it : Item{-1, 0, 0, 0});
   return out;
 }
 
@@ -85,6 +110,10 @@ Meta device_meta(const pvj_plan* p) {
   m.sin_tab = reinterpret_cast<const float*>(b + p->off_sin);
   m.fwd_items = reinterpret_cast<const Item*>(b + p->off_fwd);
   m.bwd_items = reinterpret_cast<const Item*>(b + p->off_bwd);
+  m.dq_items = reinterpret_cast<const Item*>(b + p->off_dq);
+  m.split_tiles = reinterpret_cast<const Item*>(b + p->off_split);
+  m.fwd_part = p->n_slots ? reinterpret_cast<float*>(static_cast<uint8_t*>(p->dev_meta) + p->off_part)
+                          : nullptr;
   m.n_samples = p->n_samples;
   m.n_tokens = (int32_t)p->n_tokens;
   m.n_heads = p->desc.n_heads;
@@ -95,6 +124,8 @@ Meta device_meta(const pvj_plan* p) {
   m.rope_u1 = (p->rope_dims[0] + p->rope_dims[1]) / 8;
   m.n_fwd = p->n_fwd;
   m.n_bwd = p->n_bwd;
+  m.n_dq = p->n_dq;
+  m.n_split = p->n_split;
   m.fwd_tile = p->fwd_tile;
   m.bwd_tile = p->bwd_tile;
   m.n_text = p->n_text;
@@ -211,10 +242,25 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
   p->dev_meta = nullptr;
   p->dev_id = -1;
 
-  std::vector<Item> fwd = build_items(len, desc->n_heads, p->fwd_tile);
-  std::vector<Item> bwd = build_items(len, desc->n_heads, p->bwd_tile);
+  std::vector<Item> split_tiles;
+  int64_t n_slots = 0;
+  std::vector<Item> fwd =
+      build_items(len, desc->n_heads, p->fwd_tile, desc->dtype, true, &split_tiles, &n_slots);
+  std::vector<Item> bwd =
+      build_items(len, desc->n_heads, p->bwd_tile, desc->dtype, false, nullptr, &n_slots);
+  std::vector<Item> dq =
+      build_items(len, desc->n_heads, p->fwd_tile, desc->dtype, false, nullptr, &n_slots);
+  // the slot index has 24 bits in an item
+  if (n_slots >= (int64_t(1) << 23)) {
+    delete p;
+    return fail(PVJ_ERR_UNSUPPORTED, "%lld forward partial-result slots (limit %d)",
+                (long long)n_slots, (1 << 23) - 1);
+  }
   p->n_fwd = (int32_t)fwd.size();
   p->n_bwd = (int32_t)bwd.size();
+  p->n_dq = (int32_t)dq.size();
+  p->n_split = (int32_t)split_tiles.size();
+  p->n_slots = (int32_t)n_slots;
 
   size_t off = 0;
   auto section = [&](size_t bytes) {
@@ -231,7 +277,11 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
   p->off_sin = section(tab);
   p->off_fwd = section(fwd.size() * sizeof(Item));
   p->off_bwd = section(bwd.size() * sizeof(Item));
+  p->off_dq = section(dq.size() * sizeof(Item));
+  p->off_split = section(split_tiles.size() * sizeof(Item));
   p->image_bytes = off;
+  p->off_part = off;
+  p->part_bytes = (size_t)n_slots * fwd_part_floats(D) * sizeof(float);
   p->image = static_cast<uint8_t*>(std::calloc(off, 1));
   if (!p->image) {
     delete p;
@@ -259,6 +309,9 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
   }
   if (!fwd.empty()) std::memcpy(p->image + p->off_fwd, fwd.data(), fwd.size() * sizeof(Item));
   if (!bwd.empty()) std::memcpy(p->image + p->off_bwd, bwd.data(), bwd.size() * sizeof(Item));
+  if (!dq.empty()) std::memcpy(p->image + p->off_dq, dq.data(), dq.size() * sizeof(Item));
+  if (!split_tiles.empty())
+    std::memcpy(p->image + p->off_split, split_tiles.data(), split_tiles.size() * sizeof(Item));
   *out = p;
   return PVJ_OK;
 }
@@ -295,7 +348,7 @@ PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* p, int64_t* n_tokens, int32
   if (n_tokens) *n_tokens = p->n_tokens;
   if (max_len) *max_len = p->max_len;
   if (cu_seqlens_host) *cu_seqlens_host = host_section<int32_t>(p, p->off_cu);
-  if (meta_bytes) *meta_bytes = p->image_bytes;
+  if (meta_bytes) *meta_bytes = p->image_bytes + p->part_bytes;
   return PVJ_OK;
 }
 
@@ -316,10 +369,13 @@ PVJ_API pvj_status_t pvj_plan_work_items(const pvj_plan_t* p, int32_t which,
                                          const int32_t** items, int32_t* n_items,
                                          int32_t* tile_rows) {
   if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
-  if (which != 0 && which != 1) return fail(PVJ_ERR_INVALID_ARG, "which must be 0 or 1");
-  if (items) *items = host_section<int32_t>(p, which == 0 ? p->off_fwd : p->off_bwd);
-  if (n_items) *n_items = which == 0 ? p->n_fwd : p->n_bwd;
-  if (tile_rows) *tile_rows = which == 0 ? p->fwd_tile : p->bwd_tile;
+  if (which < 0 || which > 3) return fail(PVJ_ERR_INVALID_ARG, "which must be 0, 1, 2 or 3");
+  static const int kTileOf[4] = {0, 1, 0, 0};
+  const size_t off[4] = {p->off_fwd, p->off_bwd, p->off_dq, p->off_split};
+  const int32_t n[4] = {p->n_fwd, p->n_bwd, p->n_dq, p->n_split};
+  if (items) *items = host_section<int32_t>(p, off[which]);
+  if (n_items) *n_items = n[which];
+  if (tile_rows) *tile_rows = kTileOf[which] ? p->bwd_tile : p->fwd_tile;
   return PVJ_OK;
 }
 

@@ -48,29 +48,68 @@ def test_plan_offsets_match_oracle(lib, name):
     assert p.max_len == max(oracle.sample_lengths(wl.samples))
 
 
+def _expected_splits(p, L):
+    # the forward's tail split: the last query tile of a (sample, head) of a
+    # sample of at most 8192 tokens is cut into parts of >= 16 key tiles of 64,
+    # at most 4, bf16 plans only; the count depends on the sample length alone
+    if p.dtype_code != pvj.PVJ_BF16 or L > 8192:
+        return 1
+    return max(1, min(4, int(math.ceil(L / 64)) // 16))
+
+
 def _check_work_list(p, samples, which):
     items, tile = p.work_items(which)
     lens = oracle.sample_lengths(samples)
     assert len(items) % 8 == 0
-    seen = {}
+    ranges = {}
     group_xcd = {}
-    for b, (s, h, t, pad) in enumerate(items):
+    cost = {x: [] for x in range(8)}
+    for b, (s, h, t, split) in enumerate(items):
         if s < 0:
             continue
-        assert 0 <= s < len(samples) and 0 <= h < p.n_heads and pad == 0
+        assert 0 <= s < len(samples) and 0 <= h < p.n_heads
         assert 0 <= t * tile < lens[s]
-        key = (s, h, t)
-        assert key not in seen, key
-        seen[key] = b
+        L = int(lens[s])
+        nkt = int(math.ceil(L / 64))
+        if split == 0:
+            kr = (0, nkt)
+        else:
+            # only forward items are split, and only the last query tile
+            assert which == 0 and t == int(math.ceil(L / tile)) - 1
+            S, j = (split & 15) + 1, (split >> 4) & 15
+            assert S == _expected_splits(p, L) >= 2 and j < S
+            kr = (nkt * j // S, nkt * (j + 1) // S)
+        ranges.setdefault((s, h, t), []).append((kr, split))
         # every tile of a (sample, head) lands on the same XCD (slot % 8)
         assert group_xcd.setdefault((s, h), b % 8) == b % 8
+        cost[b % 8].append(min(kr[1] * 64, L) - kr[0] * 64)
     want = {(s, h, t) for s in range(len(samples)) for h in range(p.n_heads)
             for t in range(int(math.ceil(lens[s] / tile)))}
-    assert set(seen) == want
-    # inside each XCD, longer samples run first (LPT)
+    assert set(ranges) == want
+    slots = []
+    for (s, h, t), rs in ranges.items():
+        # the key ranges of a tile partition its sample's key tiles
+        rs.sort()
+        assert rs[0][0][0] == 0 and rs[-1][0][1] == int(math.ceil(lens[s] / 64))
+        assert all(a[0][1] == b[0][0] for a, b in zip(rs, rs[1:]))
+        if which == 0 and t == int(math.ceil(lens[s] / tile)) - 1:
+            assert len(rs) == _expected_splits(p, int(lens[s]))
+        if len(rs) > 1:
+            assert len({r[1] >> 8 for r in rs}) == 1
+            slots.append((rs[0][1] >> 8, len(rs), (s, h, t)))
+    if which == 0:
+        # partial-result slots of the split tiles are disjoint and dense
+        slots.sort()
+        at = 0
+        for first, n, _ in slots:
+            assert first == at
+            at += n
+        split_list, _ = p.work_items(3)
+        assert sorted(((it[3] >> 8), (it[3] & 15) + 1, tuple(it[:3])) for it in split_list) == slots
     for x in range(8):
-        ls = [lens[s] for (s, h, t, _) in items[x::8] if s >= 0]
-        assert all(a >= b for a, b in zip(ls, ls[1:]))
+        # inside each XCD the costlier items run first (LPT)
+        c = cost[x]
+        assert all(a >= b for a, b in zip(c, c[1:]))
         # idle slots only at the end of an XCD's list
         flags = [s >= 0 for (s, _, _, _) in items[x::8]]
         assert flags == sorted(flags, reverse=True)
@@ -80,8 +119,8 @@ def _check_work_list(p, samples, which):
 def test_work_lists_cover_every_tile_once(lib, name):
     wl = workload(name)
     p = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
-    _check_work_list(p, wl.samples, 0)
-    _check_work_list(p, wl.samples, 1)
+    for which in (0, 1, 2):
+        _check_work_list(p, wl.samples, which)
 
 
 def test_work_lists_random_packs(lib):
@@ -89,15 +128,33 @@ def test_work_lists_random_packs(lib):
     for _ in range(20):
         samples = random_small_pack(rng, int(rng.integers(0, 12)), max_side=40, max_text=300)
         p = _plan(samples, int(rng.integers(1, 5)), 128, "bf16")
-        _check_work_list(p, samples, 0)
-        _check_work_list(p, samples, 1)
+        for which in (0, 1, 2):
+            _check_work_list(p, samples, which)
+
+
+def test_forward_split_depends_on_the_sample_only(lib):
+    # a sample's forward items (tile, key range) are the same in any pack, and
+    # the metadata buffer holds one partial-result slot per split part
+    a, b = (40, 52, 30), (66, 66, 9)
+    H, D = 2, 128
+    def parts(p, s):
+        items, _ = p.work_items(0)
+        return sorted((h, t, it & 0xFF) for (ss, h, t, it) in items if ss == s)
+    alone = _plan([b], H, D, "bf16")
+    pack = _plan([a, (0, 0, 5), b], H, D, "bf16")
+    assert parts(alone, 0) == parts(pack, 2)
+    n_slots = sum((it[3] & 15) + 1 for it in pack.work_items(3)[0])
+    assert n_slots == H * (2 + 4)
+    assert pack.meta_bytes > n_slots * (D + 2) * 256 * 4
+    # fp32 plans split nothing
+    assert _plan([a, (0, 0, 5), b], H, D, "f32").work_items(3)[0] == []
 
 
 def test_work_list_xcd_balance(lib):
     # the (sample, head) groups are dealt so no XCD carries much more than its share
     wl = workload("train_64k", 3)
     p = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
-    items, tile = p.work_items(0)
+    items, tile = p.work_items(2)  # the forward tiles, unsplit
     lens = oracle.sample_lengths(wl.samples)
     load = [sum(int(lens[s]) for (s, h, t, _) in items[x::8] if s >= 0) for x in range(8)]
     assert max(load) <= 1.10 * (sum(load) / 8)

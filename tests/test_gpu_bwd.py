@@ -152,9 +152,10 @@ def test_nan_outside_a_sample_does_not_leak(rope):
     # (or rows past the end of the tensor): the middle sample and 128 rows
     # after the pack are NaN, and the other samples' outputs must be finite
     # and bitwise equal to calls on those samples alone (whose tensors are
-    # followed by NaN rows too).  Lengths 186 and 95 leave partial 32-, 64-,
-    # 128- and 256-row tiles.
-    samples = [(9, 17, 33), (0, 0, 100), (5, 7, 60)]
+    # followed by NaN rows too).  Lengths 186, 95 and 2110 leave partial 32-,
+    # 64-, 128- and 256-row tiles; the last one's last forward query tile is
+    # split into two key ranges.
+    samples = [(9, 17, 33), (0, 0, 100), (5, 7, 60), (40, 52, 30)]
     H, D, dt = 2, 128, "bf16"
     plan = _plan(samples, H, D, dt)
     cu = plan.cu_seqlens
@@ -170,7 +171,7 @@ def test_nan_outside_a_sample_does_not_leak(rope):
     o_m.copy_(o)
     g = pvj.varlen_attn_bwd(plan, q, k, v, o_m, lse, do, rope_fused=rope)
     torch.cuda.synchronize()
-    for i in (0, 2):
+    for i in (0, 2, 3):
         a, b = cu[i], cu[i + 1]
         p1 = _plan([samples[i]], H, D, dt)
         one = []

@@ -232,6 +232,45 @@ def test_fwd_edge_values():
     assert_lse(to_np(lse), rl, "bf16")
 
 
+# Samples long enough that the last query tile of each (sample, head) is cut
+# into key ranges whose partial states are merged: 2110 (2 parts, last query
+# tile 62 rows), 1100 (not split), 4365 (4 parts, last query tile 13 rows,
+# last key tile 13 keys), 2061 (2 parts).
+SPLIT = [(40, 52, 30), (0, 0, 1100), (66, 66, 9), (31, 64, 77)]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_fwd_split_tiles(D):
+    H, dt = 2, "bf16"
+    plan = _plan(SPLIT, H, D, dt)
+    assert len(plan.work_items(3)[0]) == 3 * H
+    say("fwd split tiles D=%d T=%d" % (D, plan.n_tokens))
+    q, k, v = draw_tensors(plan.n_tokens, H, D, dt, 17, n=3)
+    qd, kd, vd = (to_dev(x, dt) for x in (q, k, v))
+    # RoPE on load (one-group kernel) and on pre-rotated Q/K (phase-shifted
+    # kernel): same key ranges, same partial states, same bits
+    o1, l1 = _fwd(plan, qd, kd, vd, True, dt)
+    o2, l2 = _fwd(plan, pvj.rope2d_apply(plan, qd), pvj.rope2d_apply(plan, kd), vd, False, dt)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ro, rl = oracle.attn_fwd(q, k, v, SPLIT, rope=True)
+    assert_close("o", to_np(o1), ro, dt)
+    assert_lse(to_np(l1), rl, dt)
+    # a split sample alone: same bits; without an LSE output: same O
+    cu = plan.cu_seqlens
+    a, b = cu[2], cu[3]
+    p1 = _plan([SPLIT[2]], H, D, dt)
+    oi, li = pvj.varlen_attn_fwd(p1, qd[a:b].contiguous(), kd[a:b].contiguous(),
+                                 vd[a:b].contiguous(), rope_fused=True)
+    assert torch.equal(oi, o1[a:b]) and torch.equal(li, l1[:, a:b])
+    o3 = torch.empty_like(o1)
+    lib = pvj.load_library()
+    st = lib.pvj_varlen_attn_fwd(plan.handle, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                 o3.data_ptr(), None, 0.0, 1,
+                                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0 and torch.equal(o3, o1)
+
+
 # ----------------------------------------------------------------------------
 # bitwise properties
 # ----------------------------------------------------------------------------
