@@ -347,11 +347,34 @@ def proj_bench(wl, reps):
                            dtype=torch.bfloat16) for _ in range(3))
     ys = {w: torch.empty(xs[w].shape[0], C, device="cuda", dtype=torch.bfloat16) for w in xs}
     rows = plan.n_text + plan.n_image
+    # the unfused pair for comparison: the library GEMM (torch -> hipBLASLt) per
+    # stream and projection, then the separate pack (+RoPE) / unpack passes
+    import torch.nn.functional as F
+    wparts = {w: [wq[w][i * HD:(i + 1) * HD].contiguous() for i in range(3)] for w in xs}
+    st = {w: [torch.empty(xs[w].shape[0], wl.n_heads, wl.head_dim, device="cuda",
+                          dtype=torch.bfloat16) for _ in range(3)] for w in xs}
+    o_t = torch.empty(plan.n_text, wl.n_heads, wl.head_dim, device="cuda", dtype=torch.bfloat16)
+    o_i = torch.empty(plan.n_image, wl.n_heads, wl.head_dim, device="cuda", dtype=torch.bfloat16)
+
+    def qkv_unfused():
+        for w in xs:
+            for i in range(3):
+                torch.matmul(xs[w], wparts[w][i].t(), out=st[w][i].view(-1, HD))
+        for i, (dst, rope) in enumerate(((q, True), (k, True), (v, False))):
+            pvj.pack(plan, st["text"][i], st["image"][i], dst, rope=rope)
+
+    def out_unfused():
+        pvj.unpack(plan, q, o_t, o_i)
+        torch.matmul(o_t.view(-1, HD), wo["text"].t(), out=ys["text"])
+        torch.matmul(o_i.view(-1, HD), wo["image"].t(), out=ys["image"])
+
     ops = {
         "qkv_proj_pack": (2.0 * rows * C * 3 * HD, lambda: [pvj.qkv_proj_pack(
             plan, w, xs[w], wq[w], q=q, k=k, v=v, rope=True) for w in xs]),
         "out_proj_unpack": (2.0 * rows * HD * C, lambda: [pvj.out_proj_unpack(
             plan, w, q, wo[w], y=ys[w]) for w in xs]),
+        "qkv_library_gemm_then_pack": (2.0 * rows * C * 3 * HD, qkv_unfused),
+        "out_unpack_then_library_gemm": (2.0 * rows * HD * C, out_unfused),
     }
     out = {}
     for name, (flop, fn) in ops.items():
@@ -368,7 +391,12 @@ def proj_bench(wl, reps):
         tf = flop / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                      "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-    out["_note"] = "both streams per call, hidden %d, %d rows" % (C, rows)
+    out["fused_over_unfused_time"] = {
+        "qkv": round(out["qkv_proj_pack"]["ms"] / out["qkv_library_gemm_then_pack"]["ms"], 3),
+        "out": round(out["out_proj_unpack"]["ms"] / out["out_unpack_then_library_gemm"]["ms"], 3)}
+    out["_note"] = ("both streams per call, hidden %d, %d rows; *_library_* = torch matmul "
+                    "(hipBLASLt) per stream and projection plus the separate pack (+RoPE) or "
+                    "unpack pass" % (C, rows))
     return out
 
 
@@ -455,7 +483,7 @@ def main():
                     help="only run a plain 512 MiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     ap.add_argument("--only", choices=("rope", "cfg_1024", "single_1024", "infer_multi",
-                                       "extreme_fwd", "chains"),
+                                       "extreme_fwd", "chains", "projections"),
                     help="run just this measurement (for profiling) and print its JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -482,6 +510,8 @@ def main():
             res = rope_bench(workload(args.workload, args.seed), 20)
         elif args.only == "chains":
             res = chain_bench(workload(args.workload, args.seed), 10)
+        elif args.only == "projections":
+            res = proj_bench(workload(args.workload, args.seed), 5)
         elif args.only == "extreme_fwd":
             res = pack_bench("extreme", args.steps, args.warmup, backward=False)
         else:

@@ -366,9 +366,10 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
 }
 
 // final pass over partial slots: 16 waves per (kind, sample, column chunk);
-// wave w adds the sample's slots w, w+32, ... and w+16, w+48, ... in two
-// chains (two loads in flight), then wave 0 adds the sixteen wave sums in
-// order (a fixed order: deterministic).  Slot layout [slot][kind][C].
+// wave w adds the sample's slots w + 16 j in eight chains j mod 8 (eight loads
+// in flight: with two, the longest sample's pass waited out ~14 dependent
+// loads per wave), then the chains and wave 0 the sixteen wave sums, always
+// in the same order (deterministic).  Slot layout [slot][kind][C].
 __global__ __launch_bounds__(1024) void seg_final_slots_kernel(
     const int32_t* __restrict__ cu, int n_samples, int C, int R, int kinds,
     const float* __restrict__ partial, float* __restrict__ out0, float* __restrict__ out1) {
@@ -381,16 +382,25 @@ __global__ __launch_bounds__(1024) void seg_final_slots_kernel(
   const int col = chunk * kColChunk + lane * 8;
   const bool active = col < C;
   const int nsl = (cu[s + 1] - cu[s] + R - 1) / R;
-  f32x8 acc = {}, acc2 = {};
+  f32x8 acc = {};
   if (active) {
     const float* p = partial + ((size_t)slot_base(cu, s, R) * kinds + kind) * C + col;
+    const size_t stride = (size_t)kinds * C;
+    f32x8 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = f32x8{};
     int k = wave;
-    for (; k + 16 < nsl; k += 32) {
-      acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * kinds * C);
-      acc2 += *reinterpret_cast<const f32x8*>(p + (size_t)(k + 16) * kinds * C);
+    for (; k + 7 * 16 < nsl; k += 8 * 16) {
+      f32x8 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x8*>(p + (size_t)(k + 16 * j) * stride);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] += v[j];
     }
-    if (k < nsl) acc += *reinterpret_cast<const f32x8*>(p + (size_t)k * kinds * C);
-    acc += acc2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k + 16 * j < nsl) a[j] += *reinterpret_cast<const f32x8*>(p + (size_t)(k + 16 * j) * stride);
+    acc = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
@@ -461,6 +471,7 @@ __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
     const int32_t* __restrict__ cu, int n_samples, int C, int R, const T* __restrict__ dout,
     const T* __restrict__ y, const T* __restrict__ gate, T* __restrict__ dy,
     float* __restrict__ partial) {
+  typedef typename Vec8<T>::type V8;
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   const int chunk = blockIdx.x % nchunk;
   const int slot = blockIdx.x / nchunk;
@@ -470,40 +481,40 @@ __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
   if (lo >= hi || col >= C) return;
   f32x8 acc[2] = {};
   const f32x8 w = ld8f(gate + (size_t)s * C + col);
-  // four rows' loads go out before their stores
-  int r = lo;
-  for (; r + 4 <= hi; r += 4) {
-    f32x8 va[4], vb[4];
+  // four rows per step in two alternating register sets: the next four rows'
+  // loads are in flight while this step computes and stores (rows past the
+  // slot's end re-read its last row, so no branch hides the loads from the
+  // waits; they are neither summed nor stored)
+  V8 a0[4], b0[4], a1[4], b1[4];
+  auto fetch = [&](V8 (&a)[4], V8 (&b)[4], int r0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const size_t o = (size_t)(r + k) * C + col;
-      va[k] = ld8f(dout + o);
-      vb[k] = ld8f(y + o);
+      const size_t o = (size_t)min(r0 + k, hi - 1) * C + col;
+      a[k] = load8<T>(dout + o);
+      b[k] = load8<T>(y + o);
     }
-    // (without this fence the scheduler sinks each load to its first use and
-    // waits for it there: one request in flight per wave)
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto use = [&](const V8 (&a)[4], const V8 (&b)[4], int r0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      f32x8 d;
+      if (r0 + k < hi) {
+        const f32x8 va = to_f32x8(a[k]), vb = to_f32x8(b[k]);
+        f32x8 d;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[k & 1][e] += va[k][e] * vb[k][e];
-        d[e] = w[e] * va[k][e];
+        for (int e = 0; e < 8; ++e) {
+          acc[k & 1][e] += va[e] * vb[e];
+          d[e] = w[e] * va[e];
+        }
+        st8nt<T>(dy + (size_t)(r0 + k) * C + col, d);
       }
-      st8nt<T>(dy + (size_t)(r + k) * C + col, d);
     }
-  }
-  for (; r < hi; ++r) {
-    const size_t o = (size_t)r * C + col;
-    const f32x8 va = ld8f(dout + o), vb = ld8f(y + o);
-    f32x8 d;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[0][e] += va[e] * vb[e];
-      d[e] = w[e] * va[e];
-    }
-    st8nt<T>(dy + o, d);
+  };
+  fetch(a0, b0, lo);
+  for (int r = lo; r < hi; r += 8) {
+    fetch(a1, b1, r + 4);
+    use(a0, b0, r);
+    fetch(a0, b0, r + 8);
+    use(a1, b1, r + 4);
   }
   *reinterpret_cast<f32x8*>(partial + (size_t)slot * C + col) = acc[0] + acc[1];
 }
