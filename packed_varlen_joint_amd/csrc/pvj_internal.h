@@ -21,14 +21,14 @@ constexpr size_t kMetaAlign = 256;  // alignment of every metadata section
 constexpr int kMaxLatentSide = 32767;  // h_lat, w_lat, n_frames limit (bounds the RoPE tables)
 
 // Rows of one attention work item.  Forward: query rows per workgroup.
-// Backward: key rows per workgroup.
+// Backward dK/dV: key rows per workgroup (bf16 8 waves x 32, fp32 4 x 32).
 inline int fwd_tile_rows(int dtype, int head_dim) {
   (void)head_dim;
   return dtype == PVJ_BF16 ? 256 : 128;
 }
 inline int bwd_tile_rows(int dtype, int head_dim) {
-  (void)dtype; (void)head_dim;
-  return 128;
+  (void)head_dim;
+  return dtype == PVJ_BF16 ? 256 : 128;
 }
 
 struct Item {  // one attention work item; sample < 0 marks an idle slot
