@@ -365,41 +365,171 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
   }
 }
 
-// final pass over partial slots: 16 waves per (kind, sample, column chunk);
-// wave w adds the sample's slots w + 16 j in eight chains j mod 8 (eight loads
-// in flight: with two, the longest sample's pass waited out ~14 dependent
-// loads per wave), then the chains and wave 0 the sixteen wave sums, always
-// in the same order (deterministic).  Slot layout [slot][kind][C].
+// The same for rows of 2,561-3,072 columns with two waves per slot, each
+// holding half of every row (three units per lane): the row statistics are
+// summed across the pair through LDS, wave 0's half first so both waves hold
+// the same bits.  Half the registers per wave (one wave alone needs ~350, one
+// per SIMD, and waits out its dependent passes) let two waves share a SIMD.
+template <typename T>
+__global__ __launch_bounds__(128) void adaln_bwd_pair_kernel(
+    const int32_t* __restrict__ cu, int n_samples, int C, int R, int n_slots,
+    const T* __restrict__ x, const T* __restrict__ scale, const T* __restrict__ dy,
+    T* __restrict__ dx, float* __restrict__ partial, float eps) {
+  typedef typename Vec8<T>::type V8;
+  constexpr int NU = 3;
+  __shared__ float xch[2][3][2][2];  // [row parity][stage][wave][value]
+  const int slot = blockIdx.x;
+  if (slot >= n_slots) return;
+  int i, r0, r1;
+  slot_rows(cu, n_samples, R, slot, i, r0, r1);
+  if (r0 >= r1) return;  // (the whole workgroup: no barrier is left waiting)
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int upr = C / 8;
+  const float inv_c = 1.f / C;
+  V8 sc[NU];
+  f32x8 acc0[NU], acc1[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = w * 192 + lane + 64 * k;
+    V8 z = {};
+    sc[k] = u < upr ? load8<T>(scale + (size_t)i * C + u * 8) : z;
+    acc0[k] = f32x8{};
+    acc1[k] = f32x8{};
+  }
+  // the next row's x and dy are loaded while this row is computed (two rows
+  // ahead measured the same)
+  V8 xn[NU], dn[NU];
+  auto fetch = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = w * 192 + lane + 64 * k;
+      V8 z = {};
+      xn[k] = u < upr ? load8<T>(x + (size_t)r * C + u * 8) : z;
+      dn[k] = u < upr ? load8<T>(dy + (size_t)r * C + u * 8) : z;
+    }
+  };
+  // the pair's total of one statistic (each wave's sum in LDS, then both halves
+  // in wave order)
+  auto pair_sum = [&](int par, int stage, int e, float v) {
+    if (lane == 0) xch[par][stage][w][e] = v;
+  };
+  auto row = [&](int r) __attribute__((always_inline)) {
+    const int par = (r - r0) & 1;
+    const size_t ro = (size_t)r * C;
+    f32x8 v[NU];
+    V8 d[NU];
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      v[k] = to_f32x8(xn[k]);
+      d[k] = dn[k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += v[k][e];
+    }
+    if (r + 1 < r1) fetch(r + 1);
+    pair_sum(par, 0, 0, wave_sum(sum));
+    __syncthreads();
+    const float mean = (xch[par][0][0][0] + xch[par][0][1][0]) * inv_c;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = w * 192 + lane + 64 * k;
+      if (u < upr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = v[k][e] - mean;
+          ss += t * t;
+        }
+      }
+    }
+    pair_sum(par, 1, 0, wave_sum(ss));
+    __syncthreads();
+    const float rstd =
+        1.0f / __builtin_sqrtf((xch[par][1][0][0] + xch[par][1][1][0]) * inv_c + eps);
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = w * 192 + lane + 64 * k;
+      if (u < upr) {
+        const f32x8 dd = to_f32x8(d[k]), a = to_f32x8(sc[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[k][e] = (v[k][e] - mean) * rstd;  // xhat from here on
+          const float g = dd[e] * (1.f + a[e]);
+          sg += g;
+          sgx += g * v[k][e];
+          acc0[k][e] += dd[e];
+          acc1[k][e] += dd[e] * v[k][e];
+        }
+      }
+    }
+    pair_sum(par, 2, 0, wave_sum(sg));
+    pair_sum(par, 2, 1, wave_sum(sgx));
+    __syncthreads();
+    const float mg = (xch[par][2][0][0] + xch[par][2][1][0]) * inv_c;
+    const float mgx = (xch[par][2][0][1] + xch[par][2][1][1]) * inv_c;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = w * 192 + lane + 64 * k;
+      if (u < upr) {
+        const f32x8 dd = to_f32x8(d[k]), a = to_f32x8(sc[k]);
+        f32x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rstd * (dd[e] * (1.f + a[e]) - mg - v[k][e] * mgx);
+        st8nt<T>(dx + ro + u * 8, o);
+      }
+    }
+  };
+  fetch(r0);
+  for (int r = r0; r < r1; ++r) row(r);
+  float* p0 = partial + (size_t)slot * 2 * C;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = w * 192 + lane + 64 * k;
+    if (u < upr) {
+      *reinterpret_cast<f32x8*>(p0 + u * 8) = acc0[k];
+      *reinterpret_cast<f32x8*>(p0 + C + u * 8) = acc1[k];
+    }
+  }
+}
+
+// final pass over partial slots: 16 waves per (kind, sample, 128-column
+// chunk; two columns per lane); wave w adds the sample's slots w + 16 j in
+// eight chains j mod 8 (eight loads in flight), then the chains and wave 0 the
+// sixteen wave sums, always in the same order (deterministic).  Narrow chunks
+// spread the pass over the whole chip (512-column chunks left a few dozen
+// workgroups each reading ~650 KB: up to 16 us).  Slot layout [slot][kind][C].
+constexpr int kFinalCols = 128;
 __global__ __launch_bounds__(1024) void seg_final_slots_kernel(
     const int32_t* __restrict__ cu, int n_samples, int C, int R, int kinds,
     const float* __restrict__ partial, float* __restrict__ out0, float* __restrict__ out1) {
-  __shared__ f32x8 red[15][64];
-  const int nchunk = (C + kColChunk - 1) / kColChunk;
+  __shared__ f32x2 red[15][64];
+  const int nchunk = (C + kFinalCols - 1) / kFinalCols;
   const int chunk = blockIdx.x % nchunk;
   const int s = (blockIdx.x / nchunk) % n_samples;
   const int kind = blockIdx.x / (nchunk * n_samples);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = chunk * kColChunk + lane * 8;
+  const int col = chunk * kFinalCols + lane * 2;
   const bool active = col < C;
   const int nsl = (cu[s + 1] - cu[s] + R - 1) / R;
-  f32x8 acc = {};
+  f32x2 acc = {};
   if (active) {
     const float* p = partial + ((size_t)slot_base(cu, s, R) * kinds + kind) * C + col;
     const size_t stride = (size_t)kinds * C;
-    f32x8 a[8];
+    f32x2 a[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = f32x8{};
+    for (int j = 0; j < 8; ++j) a[j] = f32x2{};
     int k = wave;
     for (; k + 7 * 16 < nsl; k += 8 * 16) {
-      f32x8 v[8];
+      f32x2 v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x8*>(p + (size_t)(k + 16 * j) * stride);
+      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x2*>(p + (size_t)(k + 16 * j) * stride);
 #pragma unroll
       for (int j = 0; j < 8; ++j) a[j] += v[j];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (k + 16 * j < nsl) a[j] += *reinterpret_cast<const f32x8*>(p + (size_t)(k + 16 * j) * stride);
+      if (k + 16 * j < nsl) a[j] += *reinterpret_cast<const f32x2*>(p + (size_t)(k + 16 * j) * stride);
     acc = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
   if (wave > 0) red[wave - 1][lane] = acc;
@@ -407,7 +537,7 @@ __global__ __launch_bounds__(1024) void seg_final_slots_kernel(
   if (wave == 0 && active) {
 #pragma unroll
     for (int w = 0; w < 15; ++w) acc += red[w][lane];
-    *reinterpret_cast<f32x8*>((kind ? out1 : out0) + (size_t)s * C + col) = acc;
+    *reinterpret_cast<f32x2*>((kind ? out1 : out0) + (size_t)s * C + col) = acc;
   }
 }
 
@@ -577,10 +707,13 @@ static bool one_pass(int C) { return units_per_lane(C) <= 6; }
 // follow the kernel's register use per row width (one wave per SIMD at
 // six units per lane, two at four, three at two, four at one); at least 4
 // rows per wave.  Correctness does not depend on it.
+static bool pair_rows(int C) { return units_per_lane(C) >= 5; }  // adaln_bwd_pair_kernel
 static int rows_per_wave(int rows, int n_samples, int C) {
   const int nu = units_per_lane(C);
-  const int per_simd = nu >= 6 ? 1 : (nu >= 4 ? 2 : (nu >= 2 ? 3 : 4));
-  const int slots = 256 * 4 * per_simd - n_samples - 1;
+  // slots that fit at once: waves per SIMD x 1024 SIMDs / waves per slot (the
+  // pair kernel: two per SIMD at ~180 registers, two per slot)
+  const int per_simd = nu >= 5 ? 2 : (nu >= 4 ? 2 : (nu >= 2 ? 3 : 4));
+  const int slots = 256 * 4 * per_simd / (nu >= 5 ? 2 : 1) - n_samples - 1;
   const int r = (rows + slots - 1) / slots;
   return r < 4 ? 4 : r;
 }
@@ -693,17 +826,29 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
     const int R = rows_per_wave(rows, B, C), ns = n_slots(rows, B, R);
     float* partial = static_cast<float*>(ws);
     if (rows > 0) {
-      const dim3 g((ns + 3) / 4);
-      if (bf)
-        PVJ_NU_DISPATCH6(adaln_bwd_1p_t, bf16, g, st, cu, B, C, R, ns, x, scale, dy, dx, partial,
-                         eps);
-      else
-        PVJ_NU_DISPATCH6(adaln_bwd_1p_t, float, g, st, cu, B, C, R, ns, x, scale, dy, dx, partial,
-                         eps);
+      if (pair_rows(C)) {
+        if (bf)
+          adaln_bwd_pair_kernel<bf16><<<ns, 128, 0, st>>>(cu, B, C, R, ns, (const bf16*)x,
+                                                          (const bf16*)scale, (const bf16*)dy,
+                                                          (bf16*)dx, partial, eps);
+        else
+          adaln_bwd_pair_kernel<float><<<ns, 128, 0, st>>>(cu, B, C, R, ns, (const float*)x,
+                                                           (const float*)scale,
+                                                           (const float*)dy, (float*)dx,
+                                                           partial, eps);
+      } else {
+        const dim3 g((ns + 3) / 4);
+        if (bf)
+          PVJ_NU_DISPATCH6(adaln_bwd_1p_t, bf16, g, st, cu, B, C, R, ns, x, scale, dy, dx,
+                           partial, eps);
+        else
+          PVJ_NU_DISPATCH6(adaln_bwd_1p_t, float, g, st, cu, B, C, R, ns, x, scale, dy, dx,
+                           partial, eps);
+      }
     }
-    const int nchunk = (C + kColChunk - 1) / kColChunk;
-    seg_final_slots_kernel<<<2 * B * nchunk, 1024, 0, st>>>(cu, B, C, R, 2, partial, dshift,
-                                                             dscale);
+    const int nfin = (C + kFinalCols - 1) / kFinalCols;
+    seg_final_slots_kernel<<<2 * B * nfin, 1024, 0, st>>>(cu, B, C, R, 2, partial, dshift,
+                                                           dscale);
     return hipGetLastError();
   }
   const size_t part = (size_t)2 * B * splits * C * sizeof(float);
@@ -747,7 +892,8 @@ hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, c
           cu, B, C, R, (const float*)dout, (const float*)y, (const float*)gate, (float*)dy,
           partial);
   }
-  seg_final_slots_kernel<<<B * nchunk, 1024, 0, st>>>(cu, B, C, R, 1, partial, dgate, nullptr);
+  const int nfin = (C + kFinalCols - 1) / kFinalCols;
+  seg_final_slots_kernel<<<B * nfin, 1024, 0, st>>>(cu, B, C, R, 1, partial, dgate, nullptr);
   return hipGetLastError();
 }
 
