@@ -120,6 +120,67 @@ class PackStep:
         self.plan = plan
 
 
+class StreamMajorStep:
+    """The same pass with every token tensor in the stream-major layout: the
+    text stream's rows and then the image stream's rows of Q, K, V, dO (and of
+    O, dQ, dK, dV) are two views of one allocation, which the attention reads
+    and writes directly, so no pack or unpack pass runs; RoPE is a standalone
+    pass on Q and K, and the backward unrotates dQ', dK' in its epilogues.
+    The outputs are bitwise those of PackStep's for the same stream inputs."""
+
+    def __init__(self, wl, seed):
+        import torch
+        import packed_varlen_joint_amd as pvj
+        self.pvj = pvj
+        self.wl = wl
+        self.backward = wl.backward
+        H, D = wl.n_heads, wl.head_dim
+        probe = pvj.Plan(wl.samples, H, D, wl.dtype)
+        nt, T = probe.n_text, wl.n_tokens
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        mk = lambda: torch.randn(T, H, D, device="cuda", generator=g).to(torch.bfloat16)
+        self.t = {x: mk() for x in ("q", "k", "v", "do")}
+        for x in ("qr", "kr", "o", "dq", "dk", "dv"):
+            self.t[x] = torch.empty(T, H, D, device="cuda", dtype=torch.bfloat16)
+        # the streams a model's projections write and read: views of the tensors
+        self.streams = {x: (y[:nt], y[nt:]) for x, y in self.t.items()}
+        self.lse = torch.empty(H, T, device="cuda", dtype=torch.float32)
+        self.ws = torch.empty(max(256, probe.bwd_workspace_bytes()), device="cuda",
+                              dtype=torch.uint8)
+        self.plan = None
+
+    def __call__(self):
+        pvj, wl, t = self.pvj, self.wl, self.t
+        plan = pvj.Plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype).upload()
+        pvj.rope2d_apply(plan, t["q"], t["qr"], stream_major=True)
+        pvj.rope2d_apply(plan, t["k"], t["kr"], stream_major=True)
+        pvj.varlen_attn_fwd(plan, t["qr"], t["kr"], t["v"], out=t["o"], lse=self.lse,
+                            stream_major=True)
+        if self.backward:
+            pvj.varlen_attn_bwd(plan, t["qr"], t["kr"], t["v"], t["o"], self.lse, t["do"],
+                                rope_prerotated=True, dq=t["dq"], dk=t["dk"], dv=t["dv"],
+                                workspace=self.ws, stream_major=True)
+        self.plan = plan
+
+
+def stream_major_bench(wl, steps, warmup, seed=0):
+    """The training step in the stream-major layout (StreamMajorStep)."""
+    step = StreamMajorStep(wl, seed)
+    ms, kms = time_step(step, steps, warmup)
+    S2 = _sum_len_sq(step.plan, len(wl.samples))
+    f = (14.0 if step.backward else 4.0) * wl.n_heads * wl.head_dim * S2
+    kt = sum(kms.values())
+    out = {"workload": wl.name, "seed": seed, "layout": "stream-major",
+           "step": "plan+rope Q,K+attn fwd" + ("+attn bwd" if step.backward else ""),
+           "ms_per_step": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+           "tokens_per_s": round(wl.n_tokens / (ms * 1e-3), 1),
+           "attn_kernel_ms": round(kt, 4) if kt else None}
+    for k, v in kms.items():
+        out[k + "_ms"] = round(v, 4)
+    out["median_of_50_steps"] = median_steps(step, 50)
+    return out
+
+
 def _sum_len_sq(plan, n):
     cu = plan.cu_seqlens
     return float(sum((cu[i + 1] - cu[i]) ** 2 for i in range(n)))
@@ -483,7 +544,8 @@ def main():
                     help="only run a plain 512 MiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     ap.add_argument("--only", choices=("rope", "cfg_1024", "single_1024", "infer_multi",
-                                       "extreme_fwd", "chains", "projections"),
+                                       "extreme_fwd", "chains", "projections",
+                                       "stream_major"),
                     help="run just this measurement (for profiling) and print its JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -512,6 +574,9 @@ def main():
             res = chain_bench(workload(args.workload, args.seed), 10)
         elif args.only == "projections":
             res = proj_bench(workload(args.workload, args.seed), 5)
+        elif args.only == "stream_major":
+            res = stream_major_bench(workload(args.workload, args.seed), args.steps,
+                                     args.warmup, args.seed)
         elif args.only == "extreme_fwd":
             res = pack_bench("extreme", args.steps, args.warmup, backward=False)
         else:
@@ -610,6 +675,12 @@ def main():
     out["median_of_50_steps"] = median_steps(step, 50)
     del step
     torch.cuda.empty_cache()
+    if wl.dtype == "bf16" and args.rope == "pack":
+        # the same step with the token tensors in the stream-major layout
+        sm = stream_major_bench(wl, args.steps, args.warmup, args.seed)
+        sm["over_joint_step_time"] = round(sm["ms_per_step"] / ms_step, 4)
+        out["stream_major_step"] = sm
+        torch.cuda.empty_cache()
     if not args.no_chains:
         out["chains"] = chain_bench(wl, 10)
         out["rope_standalone"] = rope_bench(wl, 20)

@@ -70,7 +70,9 @@ typedef enum pvj_status {
 enum { PVJ_BF16 = 0, PVJ_F32 = 1 };          /* pvj_plan_desc_t.dtype */
 enum { PVJ_ROPE_INTERLEAVED = 0 };           /* pvj_plan_desc_t.rope_pairing */
 enum { PVJ_FLAG_ROPE_FUSED = 1u,             /* attention flags */
-       PVJ_FLAG_ROPE_PREROTATED = 2u };      /* backward only */
+       PVJ_FLAG_ROPE_PREROTATED = 2u,        /* backward only */
+       PVJ_FLAG_STREAM_MAJOR = 4u };         /* token tensors in stream-major order (see
+                                                pvj_rope2d_apply_stream_major) */
 
 typedef struct pvj_sample {
   int32_t h_lat;  /* latent rows    (image pixels / 16), 0 .. 32767 */
@@ -189,6 +191,33 @@ PVJ_API pvj_status_t pvj_unpack_rope(const pvj_plan_t* plan, const void* joint, 
  */
 PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* plan, const void* x, void* y,
                                       int32_t inverse, void* stream);
+
+/* ---- stream-major layout -------------------------------------------------------
+ * Review page, "Native-Resolution MMDiT": the modality-specific layers keep
+ * text and image as two streams, and only the joint attention sees a sample's
+ * text and image tokens together; "Kernel fusion": each tensor of the
+ * memory-bound work is read and written once.  A stream-major token tensor is
+ * [T, H, D] holding the text stream's n_text rows (sample order) and then the
+ * image stream's n_image rows: the two stream tensors of pvj_pack placed one
+ * after the other in one allocation.  With PVJ_FLAG_STREAM_MAJOR the attention
+ * calls read and write every token tensor (q, k, v, o, dout, dq, dk, dv) in
+ * this layout and index LSE [H, T] (and the backward's Delta) by the same row
+ * order, so the streams' projections feed the attention, and take its output,
+ * with no pack or unpack pass.  Each sample still attends over its own text
+ * and image tokens only, in the order text then image, and every value is
+ * bitwise what the joint layout gives for the same rows (the kernels and the
+ * order of every sum are the same; only the row addresses differ).
+ * Conditions (else UNSUPPORTED, before anything is enqueued): a bf16 plan; no
+ * PVJ_FLAG_ROPE_FUSED (rotate Q and K with pvj_rope2d_apply_stream_major, call
+ * the forward without RoPE flags and the backward with
+ * PVJ_FLAG_ROPE_PREROTATED); (T + 256) * H * D * 2 < 2^31 (32-bit row
+ * offsets).
+ * pvj_rope2d_apply_stream_major: pvj_rope2d_apply for a stream-major x, y
+ * (each row rotated by its own token's position; bitwise the same values as
+ * the joint-layout call; any plan dtype; x == y allowed, else no overlap).
+ */
+PVJ_API pvj_status_t pvj_rope2d_apply_stream_major(const pvj_plan_t* plan, const void* x,
+                                                   void* y, int32_t inverse, void* stream);
 
 /* ---- attention forward -------------------------------------------------------
  * For every sample i and head h: O_i = softmax(s * Q'_i K'_i^T) V_i over the

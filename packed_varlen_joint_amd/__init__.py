@@ -21,7 +21,8 @@ import ctypes
 import os
 from typing import Iterable, Optional, Sequence, Tuple
 
-__all__ = ["Plan", "PvjError", "pack", "unpack", "rope2d_apply", "varlen_attn_fwd",
+__all__ = ["Plan", "PvjError", "pack", "unpack", "rope2d_apply", "stream_major_rows",
+           "varlen_attn_fwd",
            "varlen_attn_bwd", "varlen_attn_bwd_noalloc", "library_path", "load_library",
            "profile_enable", "profile_read"]
 
@@ -34,6 +35,8 @@ PVJ_F32 = 1
 PVJ_ROPE_INTERLEAVED = 0
 PVJ_FLAG_ROPE_FUSED = 1
 PVJ_FLAG_ROPE_PREROTATED = 2
+# token tensors hold all text rows (sample order), then all image rows
+PVJ_FLAG_STREAM_MAJOR = 4
 
 KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
            "attn_bwd_dq": 6, "chain_fwd": 7, "chain_bwd": 8, "proj": 9}
@@ -97,6 +100,7 @@ def load_library():
         "pvj_pack_rope": (I32, [P, P, P, P, I32, P]),
         "pvj_unpack_rope": (I32, [P, P, P, P, I32, P]),
         "pvj_rope2d_apply": (I32, [P, P, P, I32, P]),
+        "pvj_rope2d_apply_stream_major": (I32, [P, P, P, I32, P]),
         "pvj_varlen_attn_fwd": (I32, [P, P, P, P, P, P, F, U32, P]),
         "pvj_varlen_attn_bwd_workspace": (I32, [P, ctypes.POINTER(SZ)]),
         "pvj_varlen_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, F, U32, P]),
@@ -358,19 +362,43 @@ def unpack(plan: Plan, joint, text=None, image=None, rope: bool = False, inverse
     return text, image
 
 
-def rope2d_apply(plan: Plan, x, y=None, inverse: bool = False):
-    """Per-sample 2D RoPE of x [T,H,D] into y (y is x: in place)."""
+def rope2d_apply(plan: Plan, x, y=None, inverse: bool = False, stream_major: bool = False):
+    """Per-sample 2D RoPE of x [T,H,D] into y (y is x: in place).
+
+    ``stream_major``: x and y hold all text rows, then all image rows."""
     _check_tokens(plan, "x", x)
     y = _empty_tokens(plan, x) if y is None else y
     _check_tokens(plan, "y", y)
-    _check(load_library().pvj_rope2d_apply(plan.handle, _ptr(x), _ptr(y), int(bool(inverse)),
-                                           _stream()))
+    lib = load_library()
+    fn = lib.pvj_rope2d_apply_stream_major if stream_major else lib.pvj_rope2d_apply
+    _check(fn(plan.handle, _ptr(x), _ptr(y), int(bool(inverse)), _stream()))
     return y
 
 
+def stream_major_rows(plan: Plan):
+    """Row of every token of the joint layout in the stream-major layout: an
+    int64 CPU tensor ``perm`` with ``sm[perm] == joint`` row for row (text rows
+    of all samples first, then their image rows, each in sample order)."""
+    torch = _torch()
+    cu = plan.cu_seqlens
+    perm = torch.empty(plan.n_tokens, dtype=torch.int64)
+    t_off, i_off = 0, plan.n_text
+    for i, smp in enumerate(plan.samples):
+        a, b, lt = int(cu[i]), int(cu[i + 1]), int(smp[2])
+        perm[a:a + lt] = torch.arange(t_off, t_off + lt)
+        n_img = b - a - lt
+        perm[a + lt:b] = torch.arange(i_off, i_off + n_img)
+        t_off += lt
+        i_off += n_img
+    return perm
+
+
 def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused: bool = False,
-                    out=None, lse=None, want_lse: bool = True):
-    """Packed varlen joint attention forward; returns (O [T,H,D], LSE fp32 [H,T] or None)."""
+                    out=None, lse=None, want_lse: bool = True, stream_major: bool = False):
+    """Packed varlen joint attention forward; returns (O [T,H,D], LSE fp32 [H,T] or None).
+
+    ``stream_major``: every token tensor (and LSE's columns) in the stream-major
+    row order (all text rows, then all image rows; bf16 plans, no ``rope_fused``)."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_tokens(plan, n, t)
@@ -380,7 +408,8 @@ def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused:
         lse = torch.empty((plan.n_heads, plan.n_tokens), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_lse(plan, lse)
-    flags = PVJ_FLAG_ROPE_FUSED if rope_fused else 0
+    flags = (PVJ_FLAG_ROPE_FUSED if rope_fused else 0) | (
+        PVJ_FLAG_STREAM_MAJOR if stream_major else 0)
     _check(load_library().pvj_varlen_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                               _ptr(lse), float(softmax_scale), flags, _stream()))
     return out, lse
@@ -388,11 +417,12 @@ def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused:
 
 def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.0,
                     rope_fused: bool = False, dq=None, dk=None, dv=None, workspace=None,
-                    rope_prerotated: bool = False):
+                    rope_prerotated: bool = False, stream_major: bool = False):
     """Packed varlen joint attention backward; returns (dQ, dK, dV).
 
     ``rope_prerotated``: q and k already hold R Q and R K (``pack(..., rope=True)``);
-    dQ and dK still come back with respect to the un-rotated Q and K."""
+    dQ and dK still come back with respect to the un-rotated Q and K.
+    ``stream_major``: as in ``varlen_attn_fwd``."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tokens(plan, n, t)
@@ -409,7 +439,8 @@ def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.
           or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous uint8 device tensor")
     flags = (PVJ_FLAG_ROPE_FUSED if rope_fused else 0) | (
-        PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0)
+        PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0) | (
+        PVJ_FLAG_STREAM_MAJOR if stream_major else 0)
     _check(load_library().pvj_varlen_attn_bwd(
         plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), float(softmax_scale), flags,
@@ -418,7 +449,8 @@ def varlen_attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale: float = 0.
 
 
 def varlen_attn_bwd_noalloc(plan: Plan, q, k, v, o, lse, dout, dq, dk, dv,
-                            softmax_scale: float = 0.0, rope_prerotated: bool = False):
+                            softmax_scale: float = 0.0, rope_prerotated: bool = False,
+                            stream_major: bool = False):
     """``varlen_attn_bwd`` without any device allocation: the library keeps the
     backward's scratch (Delta) in a fixed static device buffer (16 MiB per GPU,
     so H * T <= 4,194,304) and the caller passes every tensor, outputs
@@ -429,7 +461,8 @@ def varlen_attn_bwd_noalloc(plan: Plan, q, k, v, o, lse, dout, dq, dk, dv,
                  ("dk", dk), ("dv", dv)):
         _check_tokens(plan, n, t)
     _check_lse(plan, lse)
-    flags = PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0
+    flags = (PVJ_FLAG_ROPE_PREROTATED if rope_prerotated else 0) | (
+        PVJ_FLAG_STREAM_MAJOR if stream_major else 0)
     _check(load_library().pvj_varlen_attn_bwd_noalloc(
         plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
         _ptr(dk), _ptr(dv), float(softmax_scale), flags, _stream()))

@@ -368,7 +368,7 @@ __device__ __forceinline__ void bwd_pp_sched() {
   bwd_pp_sched_ops<0, N, NP, NC>();
 }
 
-template <int D>
+template <int D, bool SM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ K,
                         const bf16* __restrict__ V, const bf16* __restrict__ dO,
@@ -398,6 +398,11 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
   const int L = si.len;
   const size_t RS = (size_t)m.n_heads * D;
   const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+  const size_t hb = (size_t)it.head * D;  // a token's row r is at hb + r * RS
+  // stream-major copies: from the head's base to the sample's last image row
+  const int tbytes = SM ? sm_bytes<D>(si, RS) : 0;
+  const uint32_t rsb = (uint32_t)(RS * sizeof(bf16));
+  (void)tbytes, (void)rsb;
   const int kv0 = it.tile * BN;
 
   const int tid = threadIdx.x;
@@ -412,7 +417,9 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     bf16x8 z = {};
-    kf[ks] = my_key < L ? load8<bf16>(K + base + (size_t)my_key * RS + (2 * ks + hi) * 8) : z;
+    kf[ks] = my_key < L ? load8<bf16>(K + hb + (size_t)token_row<SM>(si, my_key) * RS +
+                                      (2 * ks + hi) * 8)
+                        : z;
   }
   // the 256 keys' V rows, natural order, swizzled units
   {
@@ -423,7 +430,8 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
       const int row = e / UPR, u = e % UPR;
       bf16x8 z = {};
       const bf16x8 x =
-          kv0 + row < L ? load8<bf16>(V + base + (size_t)(kv0 + row) * RS + u * 8) : z;
+          kv0 + row < L ? load8<bf16>(V + hb + (size_t)token_row<SM>(si, kv0 + row) * RS + u * 8)
+                        : z;
       store8<bf16>(v_t + toff<D>(row, u * 8), x);
     }
   }
@@ -434,8 +442,9 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
   constexpr int NC = 2 * DT::PER;  // copy instructions per tile and thread
   const DT dma(RS);
   const typename DT::Src rq = DT::src(Q + base, RS, L), rg = DT::src(dO + base, RS, L);
-  const float* lse_h = LSE + (size_t)it.head * m.n_tokens + si.start;
-  const float* del_h = DELTA + (size_t)it.head * m.n_tokens + si.start;
+  // LSE and Delta are [H, T] in the token tensors' row order
+  const float* lse_h = LSE + (size_t)it.head * m.n_tokens;
+  const float* del_h = DELTA + (size_t)it.head * m.n_tokens;
   float lr = 0.f, dr = 0.f;
   auto qbuf = [&](auto bc) -> bf16* {
     constexpr int B = decltype(bc)::value;
@@ -450,15 +459,21 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
   // sample end gets an empty buffer resource and reads zeros, into a buffer
   // no later product reads)
   auto copy_part = [&](int j, auto bc, int c) __attribute__((always_inline)) {
-    if (c < DT::PER) dma.part(qbuf(bc), rq, RS, j * BQ, c);
-    else dma.part(gbuf(bc), rg, RS, j * BQ, c - DT::PER);
+    if constexpr (SM) {
+      if (c < DT::PER) dma.part_sm(qbuf(bc), Q + hb, tbytes, rsb, si, j * BQ, c);
+      else dma.part_sm(gbuf(bc), dO + hb, tbytes, rsb, si, j * BQ, c - DT::PER);
+    } else {
+      if (c < DT::PER) dma.part(qbuf(bc), rq, RS, j * BQ, c);
+      else dma.part(gbuf(bc), rg, RS, j * BQ, c - DT::PER);
+    }
   };
   auto load_ld = [&](int j) __attribute__((always_inline)) {
     if (tid < BQ) {
       const int qq = j * BQ + tid;
       // queries past the end: LSE = +inf makes P = 0 (their rows read as zeros)
-      lr = qq < L ? lse_h[qq] : INFINITY;
-      dr = qq < L ? del_h[qq] : 0.f;
+      const int trow = qq < L ? token_row<SM>(si, qq) : 0;
+      lr = qq < L ? lse_h[trow] : INFINITY;
+      dr = qq < L ? del_h[trow] : 0.f;
     }
   };
   auto store_ld = [&](auto bc) __attribute__((always_inline)) {
@@ -690,7 +705,8 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
           f32x8 x = *reinterpret_cast<const f32x8*>(stage + row * D + unit * 8);
           if (rope && pass == 0)
             x = rope_unit(x, unit, axis_pos(token_pos3(kk, si), unit_axis(unit, m)), m, true);
-          store8<bf16>(out + base + (size_t)kk * RS + unit * 8, from_f32x8<bf16>(x));
+          store8<bf16>(out + hb + (size_t)token_row<SM>(si, kk) * RS + unit * 8,
+                       from_f32x8<bf16>(x));
         }
       }
       __syncthreads();
@@ -709,26 +725,31 @@ static hipError_t launch_dkdv_t(const Meta& m, const void* q, const void* k, con
   return hipGetLastError();
 }
 
+template <int D, bool SM>
+static hipError_t launch_dkdv_pp(const Meta& m, const void* q, const void* k, const void* v,
+                                 const void* dout, const float* lse, const float* delta, void* dk,
+                                 void* dv, float scale, bool rope, hipStream_t stream) {
+  attn_bwd_dkdv_pp_kernel<D, SM><<<dim3(m.n_bwd), dim3(512), 0, stream>>>(
+      m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta,
+      (bf16*)dk, (bf16*)dv, scale, scale * 1.4426950408889634f, rope ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const void* q,
                            const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dq, void* dk, void* dv, float scale,
-                           bool rope, hipStream_t stream) {
+                           bool rope, bool sm, hipStream_t stream) {
   if (which != 0)
-    return launch_attn_bwd_dq(p, m, q, k, v, dout, lse, delta, dq, scale, rope, stream);
+    return launch_attn_bwd_dq(p, m, q, k, v, dout, lse, delta, dq, scale, rope, sm, stream);
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int D = p->desc.head_dim;
-  if (bf) {  // 256-key work items
+  if (bf) {  // 256-key work items (the stream-major layout is bf16 only; the caller checks)
     if (m.n_bwd == 0) return hipSuccess;
-    const float sl2 = scale * 1.4426950408889634f;
-    if (D == 128)
-      attn_bwd_dkdv_pp_kernel<128><<<dim3(m.n_bwd), dim3(512), 0, stream>>>(
-          m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta,
-          (bf16*)dk, (bf16*)dv, scale, sl2, rope ? 1 : 0);
-    else
-      attn_bwd_dkdv_pp_kernel<64><<<dim3(m.n_bwd), dim3(512), 0, stream>>>(
-          m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta,
-          (bf16*)dk, (bf16*)dv, scale, sl2, rope ? 1 : 0);
-    return hipGetLastError();
+    if (sm)
+      return D == 128 ? launch_dkdv_pp<128, true>(m, q, k, v, dout, lse, delta, dk, dv, scale, rope, stream)
+                      : launch_dkdv_pp<64, true>(m, q, k, v, dout, lse, delta, dk, dv, scale, rope, stream);
+    return D == 128 ? launch_dkdv_pp<128, false>(m, q, k, v, dout, lse, delta, dk, dv, scale, rope, stream)
+                    : launch_dkdv_pp<64, false>(m, q, k, v, dout, lse, delta, dk, dv, scale, rope, stream);
   }
 #define PVJ_BWD(TT, DD) \
   return launch_dkdv_t<TT, DD>(m, q, k, v, dout, lse, delta, dk, dv, scale, rope, stream)

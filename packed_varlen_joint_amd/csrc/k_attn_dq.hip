@@ -37,7 +37,7 @@ struct DqCfg {
 };
 
 // bf16 runs two waves per SIMD (one 8-wave workgroup per CU, 64 KB of LDS)
-template <typename T, int D>
+template <typename T, int D, bool SM>
 __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves_per_eu(
     sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_bwd_dq_kernel(
     Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -58,23 +58,30 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   const int L = si.len;
   const size_t RS = (size_t)m.n_heads * D;
   const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+  const size_t hb = (size_t)it.head * D;  // a token's row r is at hb + r * RS
+  // stream-major copies (bf16 only): from the head's base to the sample's last image row
+  const int tbytes = SM ? sm_bytes<D>(si, RS) : 0;
+  const uint32_t rsb = (uint32_t)(RS * sizeof(T));
+  (void)tbytes, (void)rsb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int qi = it.tile * C::BM + wave * 32 + l32;  // this lane's query
+  const int qrow = qi < L ? token_row<SM>(si, qi) : 0;
 
   V8 qf[KS], gf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int unit = 2 * ks + hi;
     V8 z = {};
-    qf[ks] = qi < L ? load8<T>(Q + base + (size_t)qi * RS + unit * 8) : z;
-    gf[ks] = qi < L ? load8<T>(dO + base + (size_t)qi * RS + unit * 8) : z;
+    qf[ks] = qi < L ? load8<T>(Q + hb + (size_t)qrow * RS + unit * 8) : z;
+    gf[ks] = qi < L ? load8<T>(dO + hb + (size_t)qrow * RS + unit * 8) : z;
   }
-  const float lse2 = qi < L ? LSE[(size_t)it.head * m.n_tokens + si.start + qi] *
-                                  1.4426950408889634f : INFINITY;
-  const float delta = qi < L ? DELTA[(size_t)it.head * m.n_tokens + si.start + qi] : 0.f;
+  // LSE and Delta are [H, T] in the token tensors' row order
+  const float lse2 = qi < L ? LSE[(size_t)it.head * m.n_tokens + qrow] * 1.4426950408889634f
+                            : INFINITY;
+  const float delta = qi < L ? DELTA[(size_t)it.head * m.n_tokens + qrow] : 0.f;
 
   const int k_unit = tid % UPR;
   const int k_row0 = tid / UPR;
@@ -86,7 +93,13 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   const DT dma(RS);
   const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
   auto load_kv = [&](int kv0, int b) {
-    if constexpr (DMA) {
+    if constexpr (DMA && SM) {
+#pragma unroll
+      for (int c = 0; c < DT::PER; ++c) {
+        dma.part_sm(ks_of(b), reinterpret_cast<const bf16*>(K) + hb, tbytes, rsb, si, kv0, c);
+        dma.part_sm(vs_of(b), reinterpret_cast<const bf16*>(V) + hb, tbytes, rsb, si, kv0, c);
+      }
+    } else if constexpr (DMA) {
       dma.copy(ks_of(b), rk, RS, kv0);
       dma.copy(vs_of(b), rv, RS, kv0);
     } else {
@@ -247,7 +260,7 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   // ---- epilogue: dQ = R^T (s dQ'); lane holds query qi, d = 32db + 8g + 4hi + e ----
   if (qi < L) {
     const RopePos qp = rope ? token_pos3(qi, si) : RopePos{0, 0, 0};
-    T* row = dQ + base + (size_t)qi * RS;
+    T* row = dQ + hb + (size_t)qrow * RS;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -284,12 +297,12 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool SM>
 static hipError_t launch_dq_t(const Meta& m, const void* q, const void* k, const void* v,
                               const void* dout, const float* lse, const float* delta, void* dq,
                               float scale, bool rope, hipStream_t stream) {
   if (m.n_dq > 0)
-    attn_bwd_dq_kernel<T, D><<<dim3(m.n_dq), dim3(DqCfg<T, D>::THREADS), 0, stream>>>(
+    attn_bwd_dq_kernel<T, D, SM><<<dim3(m.n_dq), dim3(DqCfg<T, D>::THREADS), 0, stream>>>(
         m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
         scale * 1.4426950408889634f, rope ? 1 : 0);
   return hipGetLastError();
@@ -297,16 +310,19 @@ static hipError_t launch_dq_t(const Meta& m, const void* q, const void* k, const
 
 hipError_t launch_attn_bwd_dq(const pvj_plan* p, const Meta& m, const void* q, const void* k,
                               const void* v, const void* dout, const float* lse,
-                              const float* delta, void* dq, float scale, bool rope,
+                              const float* delta, void* dq, float scale, bool rope, bool sm,
                               hipStream_t stream) {
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int D = p->desc.head_dim;
-#define PVJ_DQ(TT, DD) \
-  return launch_dq_t<TT, DD>(m, q, k, v, dout, lse, delta, dq, scale, rope, stream)
-  if (bf && D == 128) PVJ_DQ(bf16, 128);
-  if (bf && D == 64) PVJ_DQ(bf16, 64);
-  if (!bf && D == 128) PVJ_DQ(float, 128);
-  PVJ_DQ(float, 64);
+#define PVJ_DQ(TT, DD, SMV) \
+  return launch_dq_t<TT, DD, SMV>(m, q, k, v, dout, lse, delta, dq, scale, rope, stream)
+  // (the stream-major layout is bf16 only; the caller checks)
+  if (bf && sm && D == 128) PVJ_DQ(bf16, 128, true);
+  if (bf && sm) PVJ_DQ(bf16, 64, true);
+  if (bf && D == 128) PVJ_DQ(bf16, 128, false);
+  if (bf) PVJ_DQ(bf16, 64, false);
+  if (D == 128) PVJ_DQ(float, 128, false);
+  PVJ_DQ(float, 64, false);
 #undef PVJ_DQ
 }
 

@@ -429,7 +429,7 @@ __global__ __launch_bounds__((FwdTile<T, D>::THREADS)) __attribute__((amdgpu_wav
 // ---------------------------------------------------------------------------
 constexpr int kPpAhead = 4;  // operand fragments in flight ahead of the products
 
-template <int D>
+template <int D, bool SM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
@@ -448,6 +448,11 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   const int L = si.len;
   const size_t RS = (size_t)m.n_heads * D;
   const size_t base = (size_t)si.start * RS + (size_t)it.head * D;
+  const size_t hb = (size_t)it.head * D;  // a token's row r is at hb + r * RS
+  // stream-major copies: from the head's base to the sample's last image row
+  const int tbytes = SM ? sm_bytes<D>(si, RS) : 0;
+  const uint32_t rsb = (uint32_t)(RS * sizeof(bf16));
+  (void)tbytes, (void)rsb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -459,7 +464,7 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     bf16x8 v = {};
-    if (qi < L) v = load8<bf16>(Q + base + (size_t)qi * RS + (2 * ks + hi) * 8);
+    if (qi < L) v = load8<bf16>(Q + hb + (size_t)token_row<SM>(si, qi) * RS + (2 * ks + hi) * 8);
     qf[ks] = v;
   }
 
@@ -484,8 +489,13 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   // product reads).
   auto copy_part = [&](int k, auto bc, int c) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    if (c < DT::PER) dma.part(B ? k_b1 : k_b0, rk, RS, k * kFwdBN, c);
-    else dma.part(B ? v_b1 : v_b0, rv, RS, (k - 1) * kFwdBN, c - DT::PER);
+    if constexpr (SM) {
+      if (c < DT::PER) dma.part_sm(B ? k_b1 : k_b0, K + hb, tbytes, rsb, si, (kt0 + k) * kFwdBN, c);
+      else dma.part_sm(B ? v_b1 : v_b0, V + hb, tbytes, rsb, si, (kt0 + k - 1) * kFwdBN, c - DT::PER);
+    } else {
+      if (c < DT::PER) dma.part(B ? k_b1 : k_b0, rk, RS, k * kFwdBN, c);
+      else dma.part(B ? v_b1 : v_b0, rv, RS, (k - 1) * kFwdBN, c - DT::PER);
+    }
   };
 
   // per-lane LDS byte offsets of the operand reads (see the kernel above)
@@ -704,7 +714,8 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   }
   if (qi < L) {
     const float inv = 1.f / l_tot;
-    bf16* orow = O + base + (size_t)qi * RS;
+    const int trow = token_row<SM>(si, qi);
+    bf16* orow = O + hb + (size_t)trow * RS;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -716,8 +727,7 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
         *reinterpret_cast<bf16x4*>(orow + d) = w;
       }
     if (hi == 0 && LSE)
-      LSE[(size_t)it.head * m.n_tokens + si.start + qi] =
-          (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      LSE[(size_t)it.head * m.n_tokens + trow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
@@ -727,7 +737,7 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
 // and LSE = (M + log2 sum_j w_j l_j) ln 2 (the online-softmax combination of
 // disjoint key ranges).  Grid: (split tile, 32 columns of the head dim); one
 // thread per query of the tile.
-template <int D>
+template <int D, bool SM>
 __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(Meta m, bf16* __restrict__ O,
                                                              float* __restrict__ LSE) {
   constexpr size_t PS = (size_t)(D + 2) * 256;  // floats per slot
@@ -757,7 +767,8 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(Meta m, bf16* __res
     for (int i = 0; i < 32; ++i) acc[i] += wj * x[i];
   }
   const float inv = 1.f / lt;
-  bf16* orow = O + (size_t)(si.start + qi) * m.n_heads * D + (size_t)st.head * D + d0;
+  const int trow = token_row<SM>(si, qi);
+  bf16* orow = O + (size_t)trow * m.n_heads * D + (size_t)st.head * D + d0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     bf16x8 o8;
@@ -766,7 +777,7 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(Meta m, bf16* __res
     *reinterpret_cast<bf16x8*>(orow + 8 * c) = o8;
   }
   if (blockIdx.y == 0 && LSE)
-    LSE[(size_t)st.head * m.n_tokens + si.start + qi] = (M + __log2f(lt)) * 0.69314718055994531f;
+    LSE[(size_t)st.head * m.n_tokens + trow] = (M + __log2f(lt)) * 0.69314718055994531f;
 }
 
 template <typename T, int D, bool ROPE>
@@ -777,8 +788,20 @@ static hipError_t launch_fwd_t(const Meta& m, const void* q, const void* k, cons
   return hipGetLastError();
 }
 
+template <int D, bool SM>
+static hipError_t launch_fwd_pp(const Meta& m, const void* q, const void* k, const void* v,
+                                void* o, float* lse, float sl2, hipStream_t stream) {
+  attn_fwd_pp_kernel<D, SM><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
+      m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
+  hipError_t e = hipGetLastError();
+  // split tiles: combine their parts
+  if (e != hipSuccess || m.n_split == 0) return e;
+  attn_fwd_merge_kernel<D, SM><<<dim3(m.n_split, D / 32), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
-                           const void* v, void* o, float* lse, float scale, bool rope,
+                           const void* v, void* o, float* lse, float scale, bool rope, bool sm,
                            hipStream_t stream) {
   if (m.n_fwd == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
@@ -787,26 +810,22 @@ hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, cons
 #define PVJ_FWD(TT, DD)                                                                    \
   (rope ? launch_fwd_t<TT, DD, true>(m, q, k, v, o, lse, sl2, stream)                      \
         : launch_fwd_t<TT, DD, false>(m, q, k, v, o, lse, sl2, stream))
-  hipError_t e = hipSuccess;
+  // (the stream-major layout is accepted for bf16 without RoPE on load only;
+  // the caller checks)
   if (bf && !rope) {
-    if (D == 128)
-      attn_fwd_pp_kernel<128><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
-          m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
-    else
-      attn_fwd_pp_kernel<64><<<dim3(m.n_fwd), dim3(512), 0, stream>>>(
-          m, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, sl2);
-    e = hipGetLastError();
-  } else if (bf) {
-    e = D == 128 ? PVJ_FWD(bf16, 128) : PVJ_FWD(bf16, 64);
-  } else {
-    return D == 128 ? PVJ_FWD(float, 128) : PVJ_FWD(float, 64);
+    if (sm) return D == 128 ? launch_fwd_pp<128, true>(m, q, k, v, o, lse, sl2, stream)
+                            : launch_fwd_pp<64, true>(m, q, k, v, o, lse, sl2, stream);
+    return D == 128 ? launch_fwd_pp<128, false>(m, q, k, v, o, lse, sl2, stream)
+                    : launch_fwd_pp<64, false>(m, q, k, v, o, lse, sl2, stream);
   }
+  if (!bf) return D == 128 ? PVJ_FWD(float, 128) : PVJ_FWD(float, 64);
+  hipError_t e = D == 128 ? PVJ_FWD(bf16, 128) : PVJ_FWD(bf16, 64);
   // split tiles (bf16 plans only): combine their parts
   if (e != hipSuccess || m.n_split == 0) return e;
   if (D == 128)
-    attn_fwd_merge_kernel<128><<<dim3(m.n_split, 4), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
+    attn_fwd_merge_kernel<128, false><<<dim3(m.n_split, 4), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
   else
-    attn_fwd_merge_kernel<64><<<dim3(m.n_split, 2), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
+    attn_fwd_merge_kernel<64, false><<<dim3(m.n_split, 2), dim3(256), 0, stream>>>(m, (bf16*)o, lse);
   return hipGetLastError();
 #undef PVJ_FWD
 }

@@ -68,6 +68,15 @@ __device__ __forceinline__ RopePos packed_pos(const Meta& m, int tok) {
   const SampleInfo si = m.sinfo[find_sample(m.cu, m.n_samples, tok)];
   return token_pos3(tok - si.start, si);
 }
+// RoPE position of row `row` of a stream-major tensor (all text rows, then
+// all image rows): text tokens sit at (0, 0, 0)
+__device__ __forceinline__ RopePos stream_major_pos(const Meta& m, int row) {
+  if (row < m.n_text) return RopePos{0, 0, 0};
+  const int q = row - m.n_text;
+  const int i = find_sample(m.cu_img, m.n_samples, q);
+  const SampleInfo si = m.sinfo[i];
+  return token_pos3(si.l_text + (q - m.cu_img[i]), si);
+}
 
 // ---------------------------------------------------------------------------
 // pack / unpack: joint row j of sample i <-> text row cu_text[i] + j (j < t_i)
@@ -183,7 +192,7 @@ hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const
 // review page, "Kernel fusion": RoPE application is a memory-bound op; the
 // editing plans' third, frame axis comes from the same tables).
 // ---------------------------------------------------------------------------
-template <typename T, int kBatch>
+template <typename T, int kBatch, bool SM>
 __global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const T* x, T* y, int rpb,
                                                         int inverse) {
   __shared__ int s_pos[3][kMaxRowsPerBlock];  // row, col, frame of each row's token
@@ -194,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const T* x, T* y
   const int row0 = blockIdx.x * rpb;
   const int nrows = min(rpb, m.n_tokens - row0);
   if ((int)threadIdx.x < nrows) {
-    const RopePos rp = packed_pos(m, row0 + threadIdx.x);
+    const RopePos rp =
+        SM ? stream_major_pos(m, row0 + threadIdx.x) : packed_pos(m, row0 + threadIdx.x);
     s_pos[0][threadIdx.x] = rp.r;
     s_pos[1][threadIdx.x] = rp.c;
     s_pos[2][threadIdx.x] = rp.f;
@@ -221,27 +231,33 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(Meta m, const T* x, T* y
   }
 }
 
-template <typename T>
+template <typename T, bool SM>
 static void rope_b(const Meta& m, BlockShape bs, dim3 grid, const void* x, void* y, int inv,
                    hipStream_t stream) {
   const T* xi = (const T*)x;
   T* yo = (T*)y;
   switch (bs.batch) {
-    case 1: rope_kernel<T, 1><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv); break;
-    case 2: rope_kernel<T, 2><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv); break;
-    case 3: rope_kernel<T, 3><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv); break;
-    default: rope_kernel<T, 4><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv);
+    case 1: rope_kernel<T, 1, SM><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv); break;
+    case 2: rope_kernel<T, 2, SM><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv); break;
+    case 3: rope_kernel<T, 3, SM><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv); break;
+    default: rope_kernel<T, 4, SM><<<grid, kThreads, 0, stream>>>(m, xi, yo, bs.rows, inv);
   }
 }
 
 hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* y, bool inverse,
-                         hipStream_t stream) {
+                         bool sm, hipStream_t stream) {
   if (m.n_tokens == 0) return hipSuccess;
   const bool bf = p->desc.dtype == PVJ_BF16;
   const BlockShape bs = block_shape(m, bf ? 2 : 4);
   const dim3 grid((m.n_tokens + bs.rows - 1) / bs.rows);
-  if (bf) rope_b<bf16>(m, bs, grid, x, y, inverse ? 1 : 0, stream);
-  else rope_b<float>(m, bs, grid, x, y, inverse ? 1 : 0, stream);
+  const int inv = inverse ? 1 : 0;
+  if (bf) {
+    if (sm) rope_b<bf16, true>(m, bs, grid, x, y, inv, stream);
+    else rope_b<bf16, false>(m, bs, grid, x, y, inv, stream);
+  } else {
+    if (sm) rope_b<float, true>(m, bs, grid, x, y, inv, stream);
+    else rope_b<float, false>(m, bs, grid, x, y, inv, stream);
+  }
   return hipGetLastError();
 }
 

@@ -109,10 +109,33 @@ namespace pvj {
 
 size_t attn_bwd_delta_bytes(const pvj_plan* p) { return ws_delta_bytes(p); }
 
+// The stream-major layout (PVJ_FLAG_STREAM_MAJOR) is served by the bf16
+// kernels that read Q and K already rotated; their per-copy source offsets
+// address the whole tensor with 32 bits.
+pvj_status_t check_stream_major(const pvj_plan* p, uint32_t flags) {
+  if (!(flags & PVJ_FLAG_STREAM_MAJOR)) return PVJ_OK;
+  if (p->desc.dtype != PVJ_BF16)
+    return fail(PVJ_ERR_UNSUPPORTED, "the stream-major layout needs a bf16 plan");
+  if (flags & PVJ_FLAG_ROPE_FUSED)
+    return fail(PVJ_ERR_UNSUPPORTED, "the stream-major layout takes rotated Q, K (no ROPE_FUSED)");
+  // the kernels form 32-bit byte offsets of rows up to a tile past a sample's end
+  if (((int64_t)p->n_tokens + 256) * p->desc.n_heads * p->desc.head_dim * 2 >= (int64_t(1) << 31))
+    return fail(PVJ_ERR_UNSUPPORTED,
+                "stream-major token tensors need (tokens + 256) * n_heads * head_dim * 2 < 2^31");
+  return PVJ_OK;
+}
+
 pvj_status_t check_attn_bwd_args(const pvj_plan* p, const void* q, const void* k, const void* v,
                                  const void* o, const float* lse, const void* dout,
                                  const void* dq, const void* dk, const void* dv,
                                  float softmax_scale, uint32_t flags) {
+  // flags first: host-only checks, before anything touches HIP
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (flags & ~(PVJ_FLAG_ROPE_FUSED | PVJ_FLAG_ROPE_PREROTATED | PVJ_FLAG_STREAM_MAJOR))
+    return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & PVJ_FLAG_ROPE_FUSED) && (flags & PVJ_FLAG_ROPE_PREROTATED))
+    return fail(PVJ_ERR_INVALID_ARG, "ROPE_FUSED and ROPE_PREROTATED exclude each other");
+  PVJ_TRY(check_stream_major(p, flags));
   PVJ_TRY(check_plan(p));
   const bool need = p->n_tokens > 0;
   PVJ_TRY(check_ptr(q, "q", need));
@@ -124,10 +147,6 @@ pvj_status_t check_attn_bwd_args(const pvj_plan* p, const void* q, const void* k
   PVJ_TRY(check_ptr(dq, "dq", need));
   PVJ_TRY(check_ptr(dk, "dk", need));
   PVJ_TRY(check_ptr(dv, "dv", need));
-  if (flags & ~(PVJ_FLAG_ROPE_FUSED | PVJ_FLAG_ROPE_PREROTATED))
-    return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  if ((flags & PVJ_FLAG_ROPE_FUSED) && (flags & PVJ_FLAG_ROPE_PREROTATED))
-    return fail(PVJ_ERR_INVALID_ARG, "ROPE_FUSED and ROPE_PREROTATED exclude each other");
   if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
   return PVJ_OK;
 }
@@ -143,6 +162,7 @@ pvj_status_t run_attn_bwd(const pvj_plan* p, const void* q, const void* k, const
   // Either way the epilogues rotate dQ' and dK' back (dX = R^T dX').
   const bool rope = (flags & PVJ_FLAG_ROPE_FUSED) != 0;
   const bool unrotate = rope || (flags & PVJ_FLAG_ROPE_PREROTATED) != 0;
+  const bool sm = (flags & PVJ_FLAG_STREAM_MAJOR) != 0;
   const float scale = resolve_scale(p, softmax_scale);
   {
     KernelTimer t(PVJ_KERNEL_BWD_PRE, s);
@@ -154,12 +174,12 @@ pvj_status_t run_attn_bwd(const pvj_plan* p, const void* q, const void* k, const
   {
     KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
     PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, 0, qq, kk, v, dout, lse, delta, dq, dk, dv,
-                                            scale, unrotate, s)),
+                                            scale, unrotate, sm, s)),
                      "varlen_attn_bwd dK/dV"));
   }
   KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
   return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
-                                         unrotate, s)),
+                                         unrotate, sm, s)),
                   "varlen_attn_bwd dQ");
 }
 
@@ -234,8 +254,8 @@ PVJ_API pvj_status_t pvj_unpack_rope(const pvj_plan_t* p, const void* joint, voi
                   "unpack_rope");
 }
 
-PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* p, const void* x, void* y,
-                                      int32_t inverse, void* stream) {
+static pvj_status_t rope2d(const pvj_plan_t* p, const void* x, void* y, int32_t inverse, bool sm,
+                           void* stream) {
   PVJ_TRY(check_plan(p));
   PVJ_TRY(check_ptr(x, "x", p->n_tokens > 0));
   PVJ_TRY(check_ptr(y, "y", p->n_tokens > 0));
@@ -245,14 +265,29 @@ PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* p, const void* x, void* 
     if (a < b + n && b < a + n) return fail(PVJ_ERR_INVALID_ARG, "x and y partially overlap");
   }
   KernelTimer t(PVJ_KERNEL_ROPE, static_cast<hipStream_t>(stream));
-  return launched(t.done(launch_rope2d(p, device_meta(p), x, y, inverse != 0,
+  return launched(t.done(launch_rope2d(p, device_meta(p), x, y, inverse != 0, sm,
                                        static_cast<hipStream_t>(stream))),
                   "rope2d_apply");
+}
+
+PVJ_API pvj_status_t pvj_rope2d_apply(const pvj_plan_t* p, const void* x, void* y,
+                                      int32_t inverse, void* stream) {
+  return rope2d(p, x, y, inverse, false, stream);
+}
+
+PVJ_API pvj_status_t pvj_rope2d_apply_stream_major(const pvj_plan_t* p, const void* x, void* y,
+                                                   int32_t inverse, void* stream) {
+  return rope2d(p, x, y, inverse, true, stream);
 }
 
 PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* p, const void* q, const void* k,
                                          const void* v, void* o, float* lse,
                                          float softmax_scale, uint32_t flags, void* stream) {
+  // flags first: host-only checks, before anything touches HIP
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (flags & ~(PVJ_FLAG_ROPE_FUSED | PVJ_FLAG_STREAM_MAJOR))
+    return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  PVJ_TRY(check_stream_major(p, flags));
   PVJ_TRY(check_plan(p));
   const bool need = p->n_tokens > 0;
   PVJ_TRY(check_ptr(q, "q", need));
@@ -260,12 +295,12 @@ PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* p, const void* q, con
   PVJ_TRY(check_ptr(v, "v", need));
   PVJ_TRY(check_ptr(o, "o", need));
   if (lse && !aligned16(lse)) return fail(PVJ_ERR_INVALID_ARG, "lse is not 16-byte aligned");
-  if (flags & ~PVJ_FLAG_ROPE_FUSED) return fail(PVJ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!std::isfinite(softmax_scale)) return fail(PVJ_ERR_INVALID_ARG, "softmax_scale not finite");
   KernelTimer t(PVJ_KERNEL_ATTN_FWD, static_cast<hipStream_t>(stream));
   return launched(t.done(launch_attn_fwd(p, device_meta(p), q, k, v, o, lse,
                                          resolve_scale(p, softmax_scale),
                                          (flags & PVJ_FLAG_ROPE_FUSED) != 0,
+                                         (flags & PVJ_FLAG_STREAM_MAJOR) != 0,
                                          static_cast<hipStream_t>(stream))),
                   "varlen_attn_fwd");
 }

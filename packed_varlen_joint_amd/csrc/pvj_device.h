@@ -86,6 +86,16 @@ __device__ __forceinline__ int find_sample(const int32_t* cu, int n_samples, int
   return lo - 1;
 }
 
+// Row of a sample's token (local index j in [0, L)) in a token tensor: the
+// joint layout keeps a sample's rows together (text, then image); the
+// stream-major layout keeps all text rows first, then all image rows, each in
+// sample order.
+template <bool SM>
+__device__ __forceinline__ int token_row(const SampleInfo& si, int j) {
+  if constexpr (SM) return j < si.l_text ? si.text_row + j : si.img_row + (j - si.l_text);
+  else return si.start + j;
+}
+
 // RoPE position (row, col, frame) of local token j of a sample: text tokens
 // first at (0, 0, 0), then the image grids frame after frame, each row-major
 // (a plain sample has one frame, so frame = 0).
@@ -228,8 +238,16 @@ template <int D, int ROWS, int THREADS = kTileThreads>
 struct DmaTile {
   static constexpr int UPR = D / 8;
   static constexpr int PER = ROWS * UPR / THREADS;
+  // copy instruction i of a thread moves tile row STRIDE * i + rb (source
+  // order), unit ub: the swizzle and sigma only touch row bits 0-3
+  static constexpr int STRIDE = THREADS / UPR;
+  static_assert(STRIDE % 16 == 0, "copy rows of one thread differ in bits 4 and up only");
   uint32_t off[PER];
   int wave;
+  // byte offset of copy 0 inside a tile whose first row is at offset 0:
+  // rb * RS * 2 + ub for source row rb < STRIDE and unit offset ub < D * 2
+  // (kept for the stream-major copies only; 32-bit there)
+  uint32_t c0;
   __device__ __forceinline__ explicit DmaTile(size_t RS) {
     wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -240,6 +258,9 @@ struct DmaTile {
       const int u = (slot % UPR) ^ tsw<D>(rho);
       off[i] = (uint32_t)(((size_t)bsigma(rho) * RS + (size_t)u * 8) * sizeof(bf16));
     }
+    const int rho0 = (wave * 64 + lane) / UPR;
+    const uint32_t ub = (uint32_t)((((wave * 64 + lane) % UPR) ^ tsw<D>(rho0)) * 8 * sizeof(bf16));
+    c0 = (uint32_t)bsigma(rho0) * (uint32_t)(RS * sizeof(bf16)) + ub;
   }
   // source: the head whose row 0 is at g, rows 0 .. L-1 (the buffer resource
   // is built where it is used: only device code handles the resource type)
@@ -256,6 +277,13 @@ struct DmaTile {
   // only the i-th of the PER copy instructions of that tile, so a kernel can
   // spread one tile's copies over its instruction stream
   __device__ __forceinline__ void part(void* tile, Src sr, size_t RS, int row0, int i) const;
+  // the same for a stream-major tensor (token_row<true>): the tile's rows
+  // row0 .. of the sample lie in two runs (text, image), so each lane picks
+  // one of two run bases per copy; g is the tensor's head base and `bytes`
+  // (sm_bytes) ends at the sample's last image row, so rows at or past the
+  // sample end (always on the image side) read as zeros
+  __device__ __forceinline__ void part_sm(void* tile, const bf16* g, int bytes, uint32_t rsb,
+                                          const SampleInfo& si, int row0, int i) const;
 };
 
 // The resource-building copy is a free function template: kept out of the
@@ -299,6 +327,32 @@ __device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::copy(void* tile, Src 
   const int left = sr.L - row0;
   const int bytes = left > 0 ? (int)(((size_t)(left - 1) * RS + D) * sizeof(bf16)) : 0;
   dma_copy<D, ROWS, THREADS>(off, wave, tile, sr.g + (size_t)row0 * RS, bytes);
+}
+// Resource size for stream-major copies of one sample from a tensor's head
+// base: up to the end of the sample's last image row.  Every text row of the
+// tensor lies below every image row, and the rows past the sample's end that a
+// tile covers map past its image run (to the next sample's rows or past the
+// tensor), so they fall outside and read as zeros.
+template <int D>
+__device__ __forceinline__ int sm_bytes(const SampleInfo& si, size_t RS) {
+  const int end = si.img_row + (si.len - si.l_text);  // one past the last image row
+  return end > 0 ? (int)(((size_t)(end - 1) * RS + D) * sizeof(bf16)) : 0;
+}
+// 32-bit offsets: the caller keeps (tokens + 256) * RS * 2 below 2^31, so no
+// sum below wraps.  Row rr + rb of copy i is a text row iff rb < x (x = text
+// rows left in the copy's STRIDE rows, clamped to [0, STRIDE]), and since
+// ub < rsb that is c0 < x * rsb: one compare against a uniform value.
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::part_sm(void* tile, const bf16* g,
+                                                                  int bytes, uint32_t rsb,
+                                                                  const SampleInfo& si, int row0,
+                                                                  int i) const {
+  const int rr = row0 + STRIDE * i;
+  const int x = min(max(si.l_text - rr, 0), STRIDE);
+  const uint32_t a = (uint32_t)(si.text_row + rr) * rsb;
+  const uint32_t b = (uint32_t)(si.img_row - si.l_text + rr) * rsb;
+  const uint32_t o = c0 + (c0 < (uint32_t)x * rsb ? a : b);
+  dma_copy_one<D, ROWS, THREADS>(o, wave, i, tile, g, bytes);
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -73,7 +73,10 @@ struct SampleInfo {  // per-sample metadata read by the kernels
   int32_t l_text;  // text rows at the start of the sample
   int32_t w_lat;   // latent grid width
   int32_t hw;      // h_lat * w_lat: image token p is at ((p % hw) / w, p % w, p / hw)
-  int32_t pad[3];
+  // rows of the sample in a stream-major token tensor (all samples' text rows,
+  // then all their image rows): its text at text_row .., its image at img_row ..
+  int32_t text_row, img_row;
+  int32_t pad;
 };
 
 // Device view of an uploaded plan (pointers into the caller's metadata buffer).
@@ -139,6 +142,8 @@ Meta device_meta(const pvj_plan* p);
 // workspace), and the enqueue of preprocess, dK/dV and dQ with Delta at
 // `delta` ([H, T] fp32) and, with PVJ_FLAG_ROPE_FUSED, Q' and K' at qr, kr
 size_t attn_bwd_delta_bytes(const pvj_plan* p);
+// PVJ_FLAG_STREAM_MAJOR's conditions (bf16 plan, no ROPE_FUSED, tensors < 2 GiB)
+pvj_status_t check_stream_major(const pvj_plan* p, uint32_t flags);
 pvj_status_t check_attn_bwd_args(const pvj_plan* p, const void* q, const void* k, const void* v,
                                  const void* o, const float* lse, const void* dout,
                                  const void* dq, const void* dk, const void* dv,

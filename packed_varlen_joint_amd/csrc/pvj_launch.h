@@ -10,10 +10,12 @@ namespace pvj {
 
 hipError_t launch_pack(const pvj_plan* p, const Meta& m, const void* text, const void* image,
                        void* joint, bool unpack, bool rope, bool inverse, hipStream_t stream);
+// sm: x, y in the stream-major layout (all text rows, then all image rows)
 hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* y, bool inverse,
-                         hipStream_t stream);
+                         bool sm, hipStream_t stream);
+// sm: the token tensors (and LSE's token order) in the stream-major layout
 hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
-                           const void* v, void* o, float* lse, float scale, bool rope,
+                           const void* v, void* o, float* lse, float scale, bool rope, bool sm,
                            hipStream_t stream);
 // Delta = rowsum(dO * O) into delta [H, T]; with rope also Q' = R Q -> qr and
 // K' = R K -> kr (same layout as q, k)
@@ -25,11 +27,11 @@ hipError_t launch_bwd_pre(const pvj_plan* p, const Meta& m, const void* o, const
 hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const void* q,
                            const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dq, void* dk, void* dv, float scale,
-                           bool rope, hipStream_t stream);
+                           bool rope, bool sm, hipStream_t stream);
 // the dQ kernel alone (launch_attn_bwd with which = 1 calls it)
 hipError_t launch_attn_bwd_dq(const pvj_plan* p, const Meta& m, const void* q, const void* k,
                               const void* v, const void* dout, const float* lse,
-                              const float* delta, void* dq, float scale, bool rope,
+                              const float* delta, void* dq, float scale, bool rope, bool sm,
                               hipStream_t stream);
 
 // memory-bound chains on one stream (which: 0 text, 1 image) of C columns

@@ -210,7 +210,7 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
     cu[i + 1] = (int32_t)T;
     cu_text[i + 1] = (int32_t)nt;
     cu_img[i + 1] = (int32_t)ni;
-    sinfo[i] = {cu[i], (int32_t)L, t, w, (int32_t)hw, {0, 0, 0}};
+    sinfo[i] = {cu[i], (int32_t)L, t, w, (int32_t)hw, cu_text[i], cu_img[i], 0};
     max_len = std::max(max_len, (int32_t)L);
     if (img > 0) {
       max_side = std::max(max_side, std::max(h, w));
@@ -218,6 +218,7 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
     }
   }
 
+  for (int i = 0; i < B; ++i) sinfo[i].img_row += (int32_t)nt;  // image rows follow all text rows
   pvj_plan* p = new (std::nothrow) pvj_plan();
   if (!p) return fail(PVJ_ERR_INVALID_ARG, "out of host memory");
   const int D = desc->head_dim;

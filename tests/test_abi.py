@@ -307,3 +307,51 @@ def test_noalloc_bwd_limits_before_any_device_call(lib):
     assert lib.pvj_varlen_attn_bwd_noalloc(fits.handle, *p, 0.0, 1, None) == 2   # ROPE_FUSED
     assert lib.pvj_varlen_attn_bwd_noalloc(fits.handle, *p, 0.0, 0, None) == 4   # not uploaded
     assert lib.pvj_varlen_attn_bwd_noalloc(None, *p, 0.0, 0, None) == 1
+
+
+def test_stream_major_conditions_before_any_device_call(lib):
+    # the stream-major layout (flag 4): bf16 plans, no RoPE on load, and
+    # (T + 256) * H * D * 2 < 2^31; all checked before touching HIP
+    SM, FUSED, PRE = 4, 1, 2
+    f32 = _plan([(2, 2, 1)], 1, 64, "f32")
+    bf = _plan([(2, 2, 1)], 1, 64, "bf16")
+    p = [16] * 9
+    assert lib.pvj_varlen_attn_fwd(f32.handle, 16, 16, 16, 16, None, 0.0, SM, None) == 2
+    assert lib.pvj_varlen_attn_fwd(bf.handle, 16, 16, 16, 16, None, 0.0, SM | FUSED, None) == 2
+    assert lib.pvj_varlen_attn_fwd(bf.handle, 16, 16, 16, 16, None, 0.0, SM, None) == 4
+    assert lib.pvj_varlen_attn_fwd(bf.handle, 16, 16, 16, 16, None, 0.0, 8, None) == 1
+    bwd = lambda plan, fl: lib.pvj_varlen_attn_bwd(plan.handle, 16, 16, 16, 16, 16, 16, 16, 16,
+                                                   16, 256, 1 << 20, 0.0, fl, None)
+    assert bwd(f32, SM | PRE) == 2
+    assert bwd(bf, SM | FUSED) == 2
+    assert bwd(bf, SM | PRE) == 4
+    assert lib.pvj_varlen_attn_bwd_noalloc(f32.handle, *p, 0.0, SM, None) == 2
+    assert lib.pvj_varlen_attn_bwd_noalloc(bf.handle, *p, 0.0, SM | PRE, None) == 4
+    assert lib.pvj_rope2d_apply_stream_major(bf.handle, 16, 16, 0, None) == 4
+    assert lib.pvj_rope2d_apply_stream_major(f32.handle, 16, 16, 0, None) == 4
+    # 64 heads x 128 dims: 16 KiB per token, so T + 256 must stay below 131,072
+    big = _plan([(256, 256, 0), (255, 256, 0)], 64, 128, "bf16")    # T = 130,816
+    ok = _plan([(255, 256, 0), (256, 255, 0)], 64, 128, "bf16")     # T = 130,560
+    assert lib.pvj_varlen_attn_fwd(big.handle, 16, 16, 16, 16, None, 0.0, SM, None) == 2
+    assert "2^31" in lib.pvj_last_error().decode()
+    assert lib.pvj_varlen_attn_fwd(big.handle, 16, 16, 16, 16, None, 0.0, 0, None) == 4
+    assert lib.pvj_varlen_attn_fwd(ok.handle, 16, 16, 16, 16, None, 0.0, SM, None) == 4
+
+
+def test_stream_major_row_map():
+    # the binding's joint -> stream-major row map: text rows of all samples,
+    # then image rows, each in sample order (zero-length parts included)
+    import packed_varlen_joint_amd as pvj
+    samples = [(2, 3, 5), (0, 0, 4), (1, 2, 0), (2, 2, 3), (0, 0, 0)]
+    plan = pvj.Plan(samples, 2, 64, "bf16")
+    perm = pvj.stream_major_rows(plan).tolist()
+    want_text, want_img = [], []
+    pos = 0
+    for h, w, lt in samples:
+        want_text += list(range(pos, pos + lt))
+        want_img += list(range(pos + lt, pos + lt + h * w))
+        pos += lt + h * w
+    order = want_text + want_img   # joint row of each stream-major row
+    assert sorted(perm) == list(range(plan.n_tokens))
+    assert [order[r] for r in perm] == list(range(plan.n_tokens))
+    assert plan.n_text == len(want_text) and plan.n_image == len(want_img)
