@@ -441,6 +441,8 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
   typedef DmaTile<D, BQ, THREADS / 2> DT;
   constexpr int NC = 2 * DT::PER;  // copy instructions per tile and thread
   const DT dma(RS);
+  const uint32_t c1 = SM ? dma.sm_c1(si, rsb) : 0u;  // stream-major image-row offset
+  (void)c1;
   const typename DT::Src rq = DT::src(Q + base, RS, L), rg = DT::src(dO + base, RS, L);
   // LSE and Delta are [H, T] in the token tensors' row order
   const float* lse_h = LSE + (size_t)it.head * m.n_tokens;
@@ -460,8 +462,8 @@ attn_bwd_dkdv_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restri
   // no later product reads)
   auto copy_part = [&](int j, auto bc, int c) __attribute__((always_inline)) {
     if constexpr (SM) {
-      if (c < DT::PER) dma.part_sm(qbuf(bc), Q + hb, tbytes, rsb, si, j * BQ, c);
-      else dma.part_sm(gbuf(bc), dO + hb, tbytes, rsb, si, j * BQ, c - DT::PER);
+      if (c < DT::PER) dma.part_sm(qbuf(bc), Q + hb, tbytes, rsb, c1, si, j * BQ, c);
+      else dma.part_sm(gbuf(bc), dO + hb, tbytes, rsb, c1, si, j * BQ, c - DT::PER);
     } else {
       if (c < DT::PER) dma.part(qbuf(bc), rq, RS, j * BQ, c);
       else dma.part(gbuf(bc), rg, RS, j * BQ, c - DT::PER);

@@ -91,13 +91,15 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   // direct copies (K and V tiles share one layout; rows past the end are zeros)
   typedef DmaTile<D, kDqBN, C::THREADS> DT;
   const DT dma(RS);
+  const uint32_t c1 = SM ? dma.sm_c1(si, rsb) : 0u;  // stream-major image-row offset
+  (void)c1;
   const typename DT::Src rk = DT::src(K + base, RS, L), rv = DT::src(V + base, RS, L);
   auto load_kv = [&](int kv0, int b) {
     if constexpr (DMA && SM) {
 #pragma unroll
       for (int c = 0; c < DT::PER; ++c) {
-        dma.part_sm(ks_of(b), reinterpret_cast<const bf16*>(K) + hb, tbytes, rsb, si, kv0, c);
-        dma.part_sm(vs_of(b), reinterpret_cast<const bf16*>(V) + hb, tbytes, rsb, si, kv0, c);
+        dma.part_sm(ks_of(b), reinterpret_cast<const bf16*>(K) + hb, tbytes, rsb, c1, si, kv0, c);
+        dma.part_sm(vs_of(b), reinterpret_cast<const bf16*>(V) + hb, tbytes, rsb, c1, si, kv0, c);
       }
     } else if constexpr (DMA) {
       dma.copy(ks_of(b), rk, RS, kv0);

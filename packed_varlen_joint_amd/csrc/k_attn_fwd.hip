@@ -472,6 +472,8 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   typedef DmaTile<D, kFwdBN, THREADS / 2> DT;
   constexpr int NC = 2 * DT::PER;  // copy instructions per set and wave
   const DT dma(RS);
+  const uint32_t c1 = SM ? dma.sm_c1(si, rsb) : 0u;  // stream-major image-row offset
+  (void)c1;
   // key tiles kt0 .. kt1 - 1 of the sample: all of them, or one part of a split
   // tile.  Keys are counted from the first one of the part (k below counts
   // tiles from kt0): Lk keys of the sample lie at or after it.
@@ -490,8 +492,8 @@ attn_fwd_pp_kernel(Meta m, const bf16* __restrict__ Q, const bf16* __restrict__ 
   auto copy_part = [&](int k, auto bc, int c) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
     if constexpr (SM) {
-      if (c < DT::PER) dma.part_sm(B ? k_b1 : k_b0, K + hb, tbytes, rsb, si, (kt0 + k) * kFwdBN, c);
-      else dma.part_sm(B ? v_b1 : v_b0, V + hb, tbytes, rsb, si, (kt0 + k - 1) * kFwdBN, c - DT::PER);
+      if (c < DT::PER) dma.part_sm(B ? k_b1 : k_b0, K + hb, tbytes, rsb, c1, si, (kt0 + k) * kFwdBN, c);
+      else dma.part_sm(B ? v_b1 : v_b0, V + hb, tbytes, rsb, c1, si, (kt0 + k - 1) * kFwdBN, c - DT::PER);
     } else {
       if (c < DT::PER) dma.part(B ? k_b1 : k_b0, rk, RS, k * kFwdBN, c);
       else dma.part(B ? v_b1 : v_b0, rv, RS, (k - 1) * kFwdBN, c - DT::PER);

@@ -283,7 +283,12 @@ struct DmaTile {
   // (sm_bytes) ends at the sample's last image row, so rows at or past the
   // sample end (always on the image side) read as zeros
   __device__ __forceinline__ void part_sm(void* tile, const bf16* g, int bytes, uint32_t rsb,
-                                          const SampleInfo& si, int row0, int i) const;
+                                          uint32_t c1, const SampleInfo& si, int row0,
+                                          int i) const;
+  // c1 of part_sm: copy 0's offset for an image row, relative to the text run
+  __device__ __forceinline__ uint32_t sm_c1(const SampleInfo& si, uint32_t rsb) const {
+    return c0 + (uint32_t)(si.img_row - si.l_text - si.text_row) * rsb;
+  }
 };
 
 // The resource-building copy is a free function template: kept out of the
@@ -338,21 +343,31 @@ __device__ __forceinline__ int sm_bytes(const SampleInfo& si, size_t RS) {
   const int end = si.img_row + (si.len - si.l_text);  // one past the last image row
   return end > 0 ? (int)(((size_t)(end - 1) * RS + D) * sizeof(bf16)) : 0;
 }
-// 32-bit offsets: the caller keeps (tokens + 256) * RS * 2 below 2^31, so no
-// sum below wraps.  Row rr + rb of copy i is a text row iff rb < x (x = text
-// rows left in the copy's STRIDE rows, clamped to [0, STRIDE]), and since
-// ub < rsb that is c0 < x * rsb: one compare against a uniform value.
+// The resource of copy i starts at text-run row rr = row0 + STRIDE i of the
+// sample (a uniform base, so only the range check needs the lane's row): a
+// text row's lane reads at c0 from there, an image row's lane at c1 = c0 +
+// (img_row - l_text - text_row) rsb (>= c0: every text row lies below the
+// sample's image rows).  Row rr + rb is a text row iff rb < l_text - rr, and
+// since 0 <= ub < rsb that is c0 < (l_text - rr) rsb (signed): a uniform
+// threshold, then a compare and a select per lane.  32-bit offsets: the caller
+// keeps (tokens + 256) * RS * 2 below 2^31, so neither the offsets nor the
+// threshold wrap.  A copy whose base is past `bytes` has only rows past the
+// sample's end (an image lane's offset is at least the base) and gets an
+// empty resource.
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void DmaTile<D, ROWS, THREADS>::part_sm(void* tile, const bf16* g,
                                                                   int bytes, uint32_t rsb,
+                                                                  uint32_t c1,
                                                                   const SampleInfo& si, int row0,
                                                                   int i) const {
   const int rr = row0 + STRIDE * i;
-  const int x = min(max(si.l_text - rr, 0), STRIDE);
   const uint32_t a = (uint32_t)(si.text_row + rr) * rsb;
-  const uint32_t b = (uint32_t)(si.img_row - si.l_text + rr) * rsb;
-  const uint32_t o = c0 + (c0 < (uint32_t)x * rsb ? a : b);
-  dma_copy_one<D, ROWS, THREADS>(o, wave, i, tile, g, bytes);
+  const int thr = __builtin_amdgcn_readfirstlane((si.l_text - rr) * (int)rsb);
+  const uint32_t o = (int)c0 < thr ? c0 : c1;
+  const int left = bytes - (int)a;
+  dma_copy_one<D, ROWS, THREADS>(
+      o, wave, i, tile,
+      reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(g) + a), left > 0 ? left : 0);
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
