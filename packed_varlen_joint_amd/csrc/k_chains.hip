@@ -8,15 +8,16 @@
 //    (LayerNorm without affine, population variance); one wave per row, the
 //    row held in registers (two-pass mean / variance in fp32).
 //  * gate_fwd: out = x + gate_i * y, one wave per row.
-//  * adaln_bwd (rows up to 3072 columns): one pass per row range.  Each wave
-//    owns R consecutive rows of one sample (R sized so the stream's waves
-//    fill the chip) and, per row, computes dx = r (g - mean(g) - xhat
-//    mean(g xhat)) with g = dy (1 + scale_i), while it keeps the per-sample
-//    parameter gradients' column sums (dshift = sum dy, dscale = sum dy xhat)
-//    for its rows in registers; it writes them as one partial per wave, so x
-//    and dy are read once.  Sample i owns partial slots cu_i / R + i ..
-//    + ceil(L_i / R) - 1 (disjoint, increasing), and seg_final_slots adds a
-//    sample's partials in a fixed order.
+//  * adaln_bwd (rows up to 3072 columns): one pass per row set.  Each wave
+//    owns up to R rows of one sample, every S-th row of it (R sized so the
+//    stream's waves fill the chip) and, per row, computes
+//    dx = r (g - mean(g) - xhat mean(g xhat)) with g = dy (1 + scale_i),
+//    while it keeps the per-sample parameter gradients' column sums
+//    (dshift = sum dy, dscale = sum dy xhat) for its rows in registers; it
+//    writes them as one partial per wave, so x and dy are read once.  Sample
+//    i owns partial slots cu_i / R + i .. + ceil(L_i / R) - 1 (disjoint,
+//    increasing), and seg_final_slots adds a sample's partials in a fixed
+//    order.
 //  * wider rows, and the gate backward: adaln_bwd_rows writes dx and the
 //    row's mean and 1/std; the column sums (dshift, dscale; dgate = sum dout
 //    y, with dy = gate_i * dout written by the same pass) come from
@@ -246,10 +247,15 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_rows_kernel(
 // first partial slot of sample i (rows per wave R)
 __device__ __forceinline__ int slot_base(const int32_t* cu, int i, int R) { return cu[i] / R + i; }
 
-// the rows [r0, r1) of partial slot `slot` and their sample i (empty when the
-// slot lies past its sample's rows; such slots are never read)
-__device__ __forceinline__ void slot_rows(const int32_t* cu, int n_samples, int R, int slot, int& i,
-                                          int& r0, int& r1) {
+// Sample i owns slots slot_base(i) .. slot_base(i + 1) - 1; the first
+// S = ceil(L_i / R) of them (the ones the final pass reads) take rows
+// cu_i + j, cu_i + j + S, ... (at most R each), so a sample's slots sweep its
+// rows together (DRAM pages are shared by the concurrent rows: measured 5%
+// faster than R consecutive rows per slot); later slots are empty.  The
+// sample i of `slot`, its first row r0, stride st and end r1 (empty when
+// r0 >= r1; such slots are never read).
+__device__ __forceinline__ void slot_rows_strided(const int32_t* cu, int n_samples, int R,
+                                                  int slot, int& i, int& r0, int& st, int& r1) {
   int lo = 0, hi = n_samples - 1;  // the last i with slot_base(i) <= slot
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -257,8 +263,10 @@ __device__ __forceinline__ void slot_rows(const int32_t* cu, int n_samples, int 
     else hi = mid - 1;
   }
   i = lo;
-  r0 = cu[i] + (slot - slot_base(cu, i, R)) * R;
-  r1 = min(r0 + R, cu[i + 1]);
+  const int j = slot - slot_base(cu, i, R);
+  st = (cu[i + 1] - cu[i] + R - 1) / R;
+  r1 = cu[i + 1];
+  r0 = j < st ? cu[i] + j : r1;
 }
 
 template <typename T, int NU>
@@ -269,8 +277,8 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
   typedef typename Vec8<T>::type V8;
   const int slot = blockIdx.x * (kChainThreads / 64) + (threadIdx.x >> 6);
   if (slot >= n_slots) return;
-  int i, r0, r1;
-  slot_rows(cu, n_samples, R, slot, i, r0, r1);
+  int i, r0, st, r1;
+  slot_rows_strided(cu, n_samples, R, slot, i, r0, st, r1);
   if (r0 >= r1) return;
   const int lane = threadIdx.x & 63;
   const int upr = C / 8;
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
     }
   };
   fetch(r0);
-  for (int r = r0; r < r1; ++r) {
+  for (int r = r0; r < r1; r += st) {
     const size_t ro = (size_t)r * C;
     f32x8 v[NU];
     V8 d[NU];
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum += v[k][e];
     }
-    if (r + 1 < r1) fetch(r + 1);
+    if (r + st < r1) fetch(r + st);
     const float mean = wave_sum(sum) * inv_c;
     float ss = 0.f;
 #pragma unroll
@@ -370,6 +378,10 @@ __global__ __launch_bounds__(kChainThreads) void adaln_bwd_kernel(
 // summed across the pair through LDS, wave 0's half first so both waves hold
 // the same bits.  Half the registers per wave (one wave alone needs ~350, one
 // per SIMD, and waits out its dependent passes) let two waves share a SIMD.
+// Two exchanges per row: sum x, sum g and sum g x first (sum g xhat =
+// r (sum g x - mean sum g) needs no statistic), then sum (x - mean)^2 (two
+// passes for the variance).  1 + scale_i is formed once per slot in fp32.
+// Only a lane's third unit in wave 1 can lie past the row (C >= 2,561).
 template <typename T>
 __global__ __launch_bounds__(128) void adaln_bwd_pair_kernel(
     const int32_t* __restrict__ cu, int n_samples, int C, int R, int n_slots,
@@ -377,118 +389,110 @@ __global__ __launch_bounds__(128) void adaln_bwd_pair_kernel(
     T* __restrict__ dx, float* __restrict__ partial, float eps) {
   typedef typename Vec8<T>::type V8;
   constexpr int NU = 3;
-  __shared__ float xch[2][3][2][2];  // [row parity][stage][wave][value]
+  __shared__ float xch[2][2][2][3];  // [row parity][exchange][wave][value]
   const int slot = blockIdx.x;
   if (slot >= n_slots) return;
-  int i, r0, r1;
-  slot_rows(cu, n_samples, R, slot, i, r0, r1);
+  int i, r0, st, r1;
+  slot_rows_strided(cu, n_samples, R, slot, i, r0, st, r1);
   if (r0 >= r1) return;  // (the whole workgroup: no barrier is left waiting)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int upr = C / 8;
   const float inv_c = 1.f / C;
-  V8 sc[NU];
-  f32x8 acc0[NU], acc1[NU];
+  const int ub = w * 192 + lane;  // unit of k = 0; unit k is ub + 64 k
+  const bool ok2 = ub + 128 < upr;
+  auto ok = [&](int k) { return k < 2 || ok2; };
+  f32x8 sp[NU], acc0[NU], acc1[NU];
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
-    const int u = w * 192 + lane + 64 * k;
-    V8 z = {};
-    sc[k] = u < upr ? load8<T>(scale + (size_t)i * C + u * 8) : z;
+    const f32x8 a = ok(k) ? ld8f<T>(scale + (size_t)i * C + (ub + 64 * k) * 8) : f32x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sp[k][e] = 1.f + a[e];
     acc0[k] = f32x8{};
     acc1[k] = f32x8{};
   }
-  // the next row's x and dy are loaded while this row is computed (two rows
-  // ahead measured the same)
-  V8 xn[NU], dn[NU];
-  auto fetch = [&](int r) __attribute__((always_inline)) {
+  // x and dy of the rows in two register sets: row r + 2 is loaded into the
+  // set of row r as soon as row r is converted, so a load has the rest of its
+  // row and all of the next to arrive (no copies between sets); units past
+  // the row read as zeros
+  V8 xa[NU], da[NU], xb[NU], db[NU];
+  auto fetch = [&](V8 (&xs)[NU], V8 (&ds)[NU], int r) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-      const int u = w * 192 + lane + 64 * k;
       V8 z = {};
-      xn[k] = u < upr ? load8<T>(x + (size_t)r * C + u * 8) : z;
-      dn[k] = u < upr ? load8<T>(dy + (size_t)r * C + u * 8) : z;
+      xs[k] = ok(k) ? load8<T>(x + (size_t)r * C + (ub + 64 * k) * 8) : z;
+      ds[k] = ok(k) ? load8<T>(dy + (size_t)r * C + (ub + 64 * k) * 8) : z;
     }
   };
-  // the pair's total of one statistic (each wave's sum in LDS, then both halves
-  // in wave order)
-  auto pair_sum = [&](int par, int stage, int e, float v) {
-    if (lane == 0) xch[par][stage][w][e] = v;
-  };
-  auto row = [&](int r) __attribute__((always_inline)) {
-    const int par = (r - r0) & 1;
-    const size_t ro = (size_t)r * C;
-    f32x8 v[NU];
-    V8 d[NU];
-    float sum = 0.f;
+  auto row = [&](int r, V8 (&xs)[NU], V8 (&ds)[NU], int par) __attribute__((always_inline)) {
+    f32x8 v[NU], d[NU];
+    float s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-      v[k] = to_f32x8(xn[k]);
-      d[k] = dn[k];
+      v[k] = to_f32x8(xs[k]);
+      d[k] = to_f32x8(ds[k]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += v[k][e];
-    }
-    if (r + 1 < r1) fetch(r + 1);
-    pair_sum(par, 0, 0, wave_sum(sum));
-    __syncthreads();
-    const float mean = (xch[par][0][0][0] + xch[par][0][1][0]) * inv_c;
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = w * 192 + lane + 64 * k;
-      if (u < upr) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = v[k][e] - mean;
-          ss += t * t;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float g = d[k][e] * sp[k][e];
+        s1 += v[k][e];
+        s2 += g;
+        s3 += g * v[k][e];
       }
     }
-    pair_sum(par, 1, 0, wave_sum(ss));
+    if (r + 2 * st < r1) fetch(xs, ds, r + 2 * st);
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    s3 = wave_sum(s3);
+    if (lane == 0) {
+      xch[par][0][w][0] = s1;
+      xch[par][0][w][1] = s2;
+      xch[par][0][w][2] = s3;
+    }
+    __syncthreads();
+    const float mean = (xch[par][0][0][0] + xch[par][0][1][0]) * inv_c;
+    const float sg = xch[par][0][0][1] + xch[par][0][1][1];
+    const float sgx = xch[par][0][0][2] + xch[par][0][1][2];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NU; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = v[k][e] - mean;
+        v[k][e] = ok(k) ? t : 0.f;  // x - mean from here on
+        ss += v[k][e] * v[k][e];
+      }
+    ss = wave_sum(ss);
+    if (lane == 0) xch[par][1][w][0] = ss;
     __syncthreads();
     const float rstd =
         1.0f / __builtin_sqrtf((xch[par][1][0][0] + xch[par][1][1][0]) * inv_c + eps);
-    float sg = 0.f, sgx = 0.f;
+    const float mg = sg * inv_c;
+    const float mgx = rstd * ((sgx - mean * sg) * inv_c);
+    const size_t ro = (size_t)r * C;
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-      const int u = w * 192 + lane + 64 * k;
-      if (u < upr) {
-        const f32x8 dd = to_f32x8(d[k]), a = to_f32x8(sc[k]);
+      f32x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[k][e] = (v[k][e] - mean) * rstd;  // xhat from here on
-          const float g = dd[e] * (1.f + a[e]);
-          sg += g;
-          sgx += g * v[k][e];
-          acc0[k][e] += dd[e];
-          acc1[k][e] += dd[e] * v[k][e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float xh = v[k][e] * rstd;
+        acc0[k][e] += d[k][e];
+        acc1[k][e] += d[k][e] * xh;
+        o[e] = rstd * (d[k][e] * sp[k][e] - mg - xh * mgx);
       }
-    }
-    pair_sum(par, 2, 0, wave_sum(sg));
-    pair_sum(par, 2, 1, wave_sum(sgx));
-    __syncthreads();
-    const float mg = (xch[par][2][0][0] + xch[par][2][1][0]) * inv_c;
-    const float mgx = (xch[par][2][0][1] + xch[par][2][1][1]) * inv_c;
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = w * 192 + lane + 64 * k;
-      if (u < upr) {
-        const f32x8 dd = to_f32x8(d[k]), a = to_f32x8(sc[k]);
-        f32x8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = rstd * (dd[e] * (1.f + a[e]) - mg - v[k][e] * mgx);
-        st8nt<T>(dx + ro + u * 8, o);
-      }
+      if (ok(k)) st8nt<T>(dx + ro + (ub + 64 * k) * 8, o);
     }
   };
-  fetch(r0);
-  for (int r = r0; r < r1; ++r) row(r);
+  fetch(xa, da, r0);
+  if (r0 + st < r1) fetch(xb, db, r0 + st);
+  for (int r = r0; r < r1; r += 2 * st) {
+    row(r, xa, da, 0);
+    if (r + st < r1) row(r + st, xb, db, 1);
+  }
   float* p0 = partial + (size_t)slot * 2 * C;
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
-    const int u = w * 192 + lane + 64 * k;
-    if (u < upr) {
-      *reinterpret_cast<f32x8*>(p0 + u * 8) = acc0[k];
-      *reinterpret_cast<f32x8*>(p0 + C + u * 8) = acc1[k];
+    if (ok(k)) {
+      *reinterpret_cast<f32x8*>(p0 + (ub + 64 * k) * 8) = acc0[k];
+      *reinterpret_cast<f32x8*>(p0 + C + (ub + 64 * k) * 8) = acc1[k];
     }
   }
 }
@@ -595,7 +599,8 @@ __global__ __launch_bounds__(64) void seg_partial_kernel(
 
 // gate + residual backward, rows in slots (the slots of the one-pass
 // LayerNorm backward): wave (slot, 512-column chunk) writes dy = gate_s * dout
-// for its R rows and the partial sum of dout * y over them
+// for its rows (at most R, interleaved with the sample's other slots) and the
+// partial sum of dout * y over them
 template <typename T>
 __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
     const int32_t* __restrict__ cu, int n_samples, int C, int R, const T* __restrict__ dout,
@@ -605,10 +610,11 @@ __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   const int chunk = blockIdx.x % nchunk;
   const int slot = blockIdx.x / nchunk;
-  int s, lo, hi;
-  slot_rows(cu, n_samples, R, slot, s, lo, hi);
+  int s, r0, st, r1;
+  slot_rows_strided(cu, n_samples, R, slot, s, r0, st, r1);
   const int col = chunk * kColChunk + threadIdx.x * 8;
-  if (lo >= hi || col >= C) return;
+  if (r0 >= r1 || col >= C) return;
+  const int n = (r1 - r0 + st - 1) / st;  // the slot's rows r0 + t st, t < n
   f32x8 acc[2] = {};
   const f32x8 w = ld8f(gate + (size_t)s * C + col);
   // four rows per step in two alternating register sets: the next four rows'
@@ -616,18 +622,18 @@ __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
   // slot's end re-read its last row, so no branch hides the loads from the
   // waits; they are neither summed nor stored)
   V8 a0[4], b0[4], a1[4], b1[4];
-  auto fetch = [&](V8 (&a)[4], V8 (&b)[4], int r0) {
+  auto fetch = [&](V8 (&a)[4], V8 (&b)[4], int t0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const size_t o = (size_t)min(r0 + k, hi - 1) * C + col;
+      const size_t o = (size_t)(r0 + min(t0 + k, n - 1) * st) * C + col;
       a[k] = load8<T>(dout + o);
       b[k] = load8<T>(y + o);
     }
   };
-  auto use = [&](const V8 (&a)[4], const V8 (&b)[4], int r0) {
+  auto use = [&](const V8 (&a)[4], const V8 (&b)[4], int t0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (r0 + k < hi) {
+      if (t0 + k < n) {
         const f32x8 va = to_f32x8(a[k]), vb = to_f32x8(b[k]);
         f32x8 d;
 #pragma unroll
@@ -635,16 +641,16 @@ __global__ __launch_bounds__(64) void gate_bwd_slots_kernel(
           acc[k & 1][e] += va[e] * vb[e];
           d[e] = w[e] * va[e];
         }
-        st8nt<T>(dy + (size_t)(r0 + k) * C + col, d);
+        st8nt<T>(dy + (size_t)(r0 + (t0 + k) * st) * C + col, d);
       }
     }
   };
-  fetch(a0, b0, lo);
-  for (int r = lo; r < hi; r += 8) {
-    fetch(a1, b1, r + 4);
-    use(a0, b0, r);
-    fetch(a0, b0, r + 8);
-    use(a1, b1, r + 4);
+  fetch(a0, b0, 0);
+  for (int t = 0; t < n; t += 8) {
+    fetch(a1, b1, t + 4);
+    use(a0, b0, t);
+    fetch(a0, b0, t + 8);
+    use(a1, b1, t + 4);
   }
   *reinterpret_cast<f32x8*>(partial + (size_t)slot * C + col) = acc[0] + acc[1];
 }
