@@ -142,6 +142,13 @@ PVJ_API pvj_status_t pvj_plan_info(const pvj_plan_t* plan, int64_t* n_tokens, in
  * may be NULL. */
 PVJ_API pvj_status_t pvj_plan_streams(const pvj_plan_t* plan, int64_t* n_text, int64_t* n_image);
 
+/* The stream-major row of every token (see PVJ_FLAG_STREAM_MAJOR below): for
+ * the joint row t (sample i's local token j), rows[t] = the row of the same
+ * token when all samples' text rows come first and then all image rows, each
+ * in sample order.  rows: host int32 array of n = T entries, owned by the
+ * caller (n != T or rows NULL with T > 0: INVALID_ARG).  Pure host. */
+PVJ_API pvj_status_t pvj_plan_stream_major_rows(const pvj_plan_t* plan, int32_t* rows, int64_t n);
+
 /* Copy the plan's metadata into the caller-allocated device buffer `dev_meta`
  * (>= meta_bytes, 256-byte aligned) on `stream`, and record it in the plan.
  * Compute calls on this plan then read that buffer (and the forward writes its

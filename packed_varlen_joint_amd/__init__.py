@@ -93,6 +93,7 @@ def load_library():
         "pvj_plan_info": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I32),
                                 ctypes.POINTER(ctypes.POINTER(I32)), ctypes.POINTER(SZ)]),
         "pvj_plan_streams": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+        "pvj_plan_stream_major_rows": (I32, [P, ctypes.POINTER(I32), I64]),
         "pvj_plan_upload": (I32, [P, P, SZ, P]),
         "pvj_plan_destroy": (None, [P]),
         "pvj_pack": (I32, [P, P, P, P, P]),
@@ -376,21 +377,15 @@ def rope2d_apply(plan: Plan, x, y=None, inverse: bool = False, stream_major: boo
 
 
 def stream_major_rows(plan: Plan):
-    """Row of every token of the joint layout in the stream-major layout: an
-    int64 CPU tensor ``perm`` with ``sm[perm] == joint`` row for row (text rows
-    of all samples first, then their image rows, each in sample order)."""
+    """Row of every token of the joint layout in the stream-major layout (from
+    the plan): an int64 CPU tensor ``perm`` with ``sm[perm] == joint`` row for
+    row (text rows of all samples first, then their image rows, each in sample
+    order)."""
     torch = _torch()
-    cu = plan.cu_seqlens
-    perm = torch.empty(plan.n_tokens, dtype=torch.int64)
-    t_off, i_off = 0, plan.n_text
-    for i, smp in enumerate(plan.samples):
-        a, b, lt = int(cu[i]), int(cu[i + 1]), int(smp[2])
-        perm[a:a + lt] = torch.arange(t_off, t_off + lt)
-        n_img = b - a - lt
-        perm[a + lt:b] = torch.arange(i_off, i_off + n_img)
-        t_off += lt
-        i_off += n_img
-    return perm
+    T = plan.n_tokens
+    buf = (ctypes.c_int32 * max(1, T))()
+    _check(load_library().pvj_plan_stream_major_rows(plan.handle, buf, T))
+    return torch.frombuffer(buf, dtype=torch.int32)[:T].to(torch.int64)
 
 
 def varlen_attn_fwd(plan: Plan, q, k, v, softmax_scale: float = 0.0, rope_fused: bool = False,

@@ -360,6 +360,21 @@ PVJ_API pvj_status_t pvj_plan_streams(const pvj_plan_t* p, int64_t* n_text, int6
   return PVJ_OK;
 }
 
+PVJ_API pvj_status_t pvj_plan_stream_major_rows(const pvj_plan_t* p, int32_t* rows,
+                                                int64_t n) {
+  if (!p) return fail(PVJ_ERR_INVALID_ARG, "plan is NULL");
+  if (n != p->n_tokens)
+    return fail(PVJ_ERR_INVALID_ARG, "rows holds %lld entries, the plan has %lld tokens",
+                (long long)n, (long long)p->n_tokens);
+  if (n > 0 && !rows) return fail(PVJ_ERR_INVALID_ARG, "rows is NULL");
+  const pvj::SampleInfo* si = pvj::host_section<pvj::SampleInfo>(p, p->off_sinfo);
+  for (int32_t i = 0; i < p->n_samples; ++i)
+    for (int32_t j = 0; j < si[i].len; ++j)
+      rows[si[i].start + j] = j < si[i].l_text ? si[i].text_row + j
+                                               : si[i].img_row + (j - si[i].l_text);
+  return PVJ_OK;
+}
+
 PVJ_API void pvj_plan_destroy(pvj_plan_t* p) {
   if (!p) return;
   std::free(p->image);

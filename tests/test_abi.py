@@ -355,3 +355,14 @@ def test_stream_major_row_map():
     assert sorted(perm) == list(range(plan.n_tokens))
     assert [order[r] for r in perm] == list(range(plan.n_tokens))
     assert plan.n_text == len(want_text) and plan.n_image == len(want_img)
+    lib = pvj.load_library()
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.pvj_plan_stream_major_rows(plan.handle, buf, plan.n_tokens + 1) == 1
+    assert lib.pvj_plan_stream_major_rows(None, buf, 0) == 1
+    empty = pvj.Plan([(0, 0, 0)], 1, 64, "bf16")
+    assert lib.pvj_plan_stream_major_rows(empty.handle, None, 0) == 0
+    # frames plans: each frame's grid follows the sample's text in the image rows
+    fr = pvj.Plan([(2, 3, 4, 2), (1, 2, 0, 3), (0, 0, 5, 1)], 2, 64, "bf16")
+    perm = pvj.stream_major_rows(fr).tolist()
+    assert perm == [0, 1, 2, 3, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20,
+                    21, 22, 23, 24, 25, 26, 4, 5, 6, 7, 8]
