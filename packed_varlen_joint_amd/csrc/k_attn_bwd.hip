@@ -737,12 +737,10 @@ static hipError_t launch_dkdv_pp(const Meta& m, const void* q, const void* k, co
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const void* q,
-                           const void* k, const void* v, const void* dout, const float* lse,
-                           const float* delta, void* dq, void* dk, void* dv, float scale,
-                           bool rope, bool sm, hipStream_t stream) {
-  if (which != 0)
-    return launch_attn_bwd_dq(p, m, q, k, v, dout, lse, delta, dq, scale, rope, sm, stream);
+hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
+                           const void* v, const void* dout, const float* lse,
+                           const float* delta, void* dk, void* dv, float scale, bool rope,
+                           bool sm, hipStream_t stream) {
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int D = p->desc.head_dim;
   if (bf) {  // 256-key work items (the stream-major layout is bf16 only; the caller checks)

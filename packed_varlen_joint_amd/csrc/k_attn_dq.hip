@@ -41,8 +41,8 @@ template <typename T, int D, bool SM>
 __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves_per_eu(
     sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1))) void attn_bwd_dq_kernel(
     Meta m, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    T* __restrict__ dQ, float scale, float scale_log2, int rope) {
+    const T* __restrict__ O, const T* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ DELTA, T* __restrict__ dQ, float scale, float scale_log2, int rope) {
   typedef typename Vec8<T>::type V8;
   typedef DqCfg<T, D> C;
   constexpr int KS = D / 16, DB = D / 32, UPR = C::UPR, NK = C::NK;
@@ -70,18 +70,18 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   const int qi = it.tile * C::BM + wave * 32 + l32;  // this lane's query
   const int qrow = qi < L ? token_row<SM>(si, qi) : 0;
 
-  V8 qf[KS], gf[KS];
+  V8 qf[KS], gf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int unit = 2 * ks + hi;
     V8 z = {};
     qf[ks] = qi < L ? load8<T>(Q + hb + (size_t)qrow * RS + unit * 8) : z;
     gf[ks] = qi < L ? load8<T>(dO + hb + (size_t)qrow * RS + unit * 8) : z;
+    of[ks] = qi < L ? load8<T>(O + hb + (size_t)qrow * RS + unit * 8) : z;
   }
   // LSE and Delta are [H, T] in the token tensors' row order
   const float lse2 = qi < L ? LSE[(size_t)it.head * m.n_tokens + qrow] * 1.4426950408889634f
                             : INFINITY;
-  const float delta = qi < L ? DELTA[(size_t)it.head * m.n_tokens + qrow] : 0.f;
 
   const int k_unit = tid % UPR;
   const int k_row0 = tid / UPR;
@@ -157,6 +157,23 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
   const int nkv = (L + kDqBN - 1) / kDqBN;
   load_kv(0, 0);
   store_kv(0);
+  // Delta = rowsum(dO * O) of this lane's query, formed here (this kernel
+  // visits each query once; it runs before the dK/dV kernel, which reads it)
+  // once the first tile's copies and the row loads are in: the lane pair l,
+  // l + 32 holds the even and odd units of the row, every lane adds the two
+  // halves in that order, and the first lane of the pair stores it.
+  float delta;
+  {
+    float half = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f32x8 a = to_f32x8(gf[ks]), b = to_f32x8(of[ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) half += a[e] * b[e];
+    }
+    delta = sum_pair32(half);
+    if (qi < L && hi == 0) DELTA[(size_t)it.head * m.n_tokens + qrow] = delta;
+  }
   __syncthreads();
   auto step = [&](int j, auto bc, auto mc) {
     constexpr int B = decltype(bc)::value;
@@ -301,23 +318,23 @@ __global__ __launch_bounds__((DqCfg<T, D>::THREADS)) __attribute__((amdgpu_waves
 
 template <typename T, int D, bool SM>
 static hipError_t launch_dq_t(const Meta& m, const void* q, const void* k, const void* v,
-                              const void* dout, const float* lse, const float* delta, void* dq,
-                              float scale, bool rope, hipStream_t stream) {
+                              const void* o, const void* dout, const float* lse, float* delta,
+                              void* dq, float scale, bool rope, hipStream_t stream) {
   if (m.n_dq > 0)
     attn_bwd_dq_kernel<T, D, SM><<<dim3(m.n_dq), dim3(DqCfg<T, D>::THREADS), 0, stream>>>(
-        m, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta, (T*)dq, scale,
-        scale * 1.4426950408889634f, rope ? 1 : 0);
+        m, (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse, delta,
+        (T*)dq, scale, scale * 1.4426950408889634f, rope ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dq(const pvj_plan* p, const Meta& m, const void* q, const void* k,
-                              const void* v, const void* dout, const float* lse,
-                              const float* delta, void* dq, float scale, bool rope, bool sm,
+                              const void* v, const void* o, const void* dout, const float* lse,
+                              float* delta, void* dq, float scale, bool rope, bool sm,
                               hipStream_t stream) {
   const bool bf = p->desc.dtype == PVJ_BF16;
   const int D = p->desc.head_dim;
 #define PVJ_DQ(TT, DD, SMV) \
-  return launch_dq_t<TT, DD, SMV>(m, q, k, v, dout, lse, delta, dq, scale, rope, stream)
+  return launch_dq_t<TT, DD, SMV>(m, q, k, v, o, dout, lse, delta, dq, scale, rope, stream)
   // (the stream-major layout is bf16 only; the caller checks)
   if (bf && sm && D == 128) PVJ_DQ(bf16, 128, true);
   if (bf && sm) PVJ_DQ(bf16, 64, true);

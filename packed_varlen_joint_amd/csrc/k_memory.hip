@@ -1,5 +1,5 @@
-// HBM-bound kernels: modality pack/unpack, standalone per-sample 2D RoPE and
-// the attention-backward preprocess (Delta, pre-rotated Q' and K').
+// HBM-bound kernels: modality pack/unpack and standalone per-sample 2D RoPE
+// (also the attention backward's rotation of Q and K with RoPE on load).
 //
 // Every kernel walks a block of whole packed rows.  A row is H*D contiguous
 // elements and the unit of work is 8 consecutive elements (one 16-byte bf16 or
@@ -257,204 +257,6 @@ hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* 
   } else {
     if (sm) rope_b<float, true>(m, bs, grid, x, y, inv, stream);
     else rope_b<float, false>(m, bs, grid, x, y, inv, stream);
-  }
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// backward preprocess: Delta[h, t] = sum_d dO[t,h,d] * O[t,h,d] (the row term
-// of the softmax backward).  With RoPE it also writes Q' = R Q and K' = R K
-// once, so the backward kernels stream pre-rotated operands instead of
-// rotating every tile again.  The D/8 lanes of one (token, head) are
-// consecutive and reduce with xor shuffles (all lanes of a group are in or
-// out of range together: totals are multiples of D/8 and batches start at
-// multiples of the block size).
-// ---------------------------------------------------------------------------
-template <typename T, bool ROPE, int kBatch>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(Meta m, const T* __restrict__ o,
-                                                           const T* __restrict__ dout,
-                                                           const T* __restrict__ q,
-                                                           const T* __restrict__ k,
-                                                           float* __restrict__ delta,
-                                                           T* __restrict__ qr,
-                                                           T* __restrict__ kr, int rpb) {
-  __shared__ int s_pos[3][kMaxRowsPerBlock];
-  const int cpr = m.head_dim / 8;
-  const int upr = m.n_heads * cpr;
-  const int chunk = threadIdx.x % cpr;
-  const int axis = unit_axis(chunk, m);
-  const int row0 = blockIdx.x * rpb;
-  const int nrows = min(rpb, m.n_tokens - row0);
-  if (ROPE && (int)threadIdx.x < nrows) {
-    const RopePos rp = packed_pos(m, row0 + threadIdx.x);
-    s_pos[0][threadIdx.x] = rp.r;
-    s_pos[1][threadIdx.x] = rp.c;
-    s_pos[2][threadIdx.x] = rp.f;
-  }
-  if (ROPE) __syncthreads();
-  const int total = nrows * upr;
-  for (int e0 = threadIdx.x; e0 < total; e0 += kBatch * kThreads) {
-    f32x8 a[kBatch], g[kBatch], x[kBatch], y[kBatch];
-    size_t off[kBatch];
-    int rows[kBatch], us[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int e = e0 + b * kThreads;
-      rows[b] = e / upr;
-      us[b] = e - rows[b] * upr;
-      off[b] = ((size_t)(row0 + rows[b]) * upr + us[b]) * 8;
-      if (e < total) {
-        a[b] = to_f32x8(load8<T>(o + off[b]));
-        g[b] = to_f32x8(load8<T>(dout + off[b]));
-        if (ROPE) {
-          x[b] = to_f32x8(load8<T>(q + off[b]));
-          y[b] = to_f32x8(load8<T>(k + off[b]));
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      if (e0 + b * kThreads >= total) continue;
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += a[b][i] * g[b][i];
-      for (int w = 1; w < cpr; w <<= 1) s += __shfl_xor(s, w, 64);
-      if ((us[b] % cpr) == 0)
-        delta[(size_t)(us[b] / cpr) * m.n_tokens + row0 + rows[b]] = s;
-      if (ROPE) {
-        const int pos = s_pos[axis][rows[b]];
-        store8_nt<T>(qr + off[b], from_f32x8<T>(rope_unit(x[b], chunk, pos, m, false)));
-        store8_nt<T>(kr + off[b], from_f32x8<T>(rope_unit(y[b], chunk, pos, m, false)));
-      }
-    }
-  }
-}
-
-// Delta alone (no RoPE): a plain streaming read of O and dO.  Each wave takes
-// NB consecutive groups of 64 units; the D/8 lanes of one (token, head) row
-// are consecutive and sum their dot products with DPP inside the 16-lane row
-// (no LDS); one lane per (token, head) stores Delta[h, t].  No per-row
-// bookkeeping: Delta does not depend on the sample.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// Delta = rowsum(O * dO) per (token, head) without RoPE: a block takes `tb`
-// consecutive tokens with all their heads (tb * H rows of D, contiguous in
-// HBM).  Each wave streams groups of 64 units (64 / (D/8) consecutive rows,
-// one 16-byte unit per lane) NB groups at a time, the next NB groups' loads
-// in flight while the current ones are reduced (DPP sums inside the row's
-// lanes), and leaves the row sums in LDS; the block then writes Delta [H, T]
-// as one run of tb floats per head (scattered 4-byte stores had been written
-// back as partial lines: 3.6x the bytes).
-template <typename T, int D, int NB>
-__global__ __launch_bounds__(kThreads) void delta_kernel(const T* __restrict__ o,
-                                                         const T* __restrict__ dout,
-                                                         float* __restrict__ delta, int n_tokens,
-                                                         int n_heads, int tb) {
-  typedef typename Vec8<T>::type V8;
-  constexpr int UPH = D / 8;     // units per (token, head) row: 16 or 8
-  constexpr int RPG = 64 / UPH;  // rows per group of 64 units
-  extern __shared__ float red[];  // [tb * n_heads] row sums, in row order
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * tb;
-  const int nt = min(tb, n_tokens - t0);
-  const int rows = nt * n_heads;
-  const int groups = (rows + RPG - 1) / RPG;
-  const size_t base = (size_t)t0 * n_heads * D + (size_t)(lane % UPH) * 8;
-  const int rl = lane / UPH;  // this lane's row inside a group
-  V8 a0[NB], b0[NB], a1[NB], b1[NB];
-  // rows past the block's end re-read its last row (no branch around the
-  // loads, so the waits count them exactly); their sums are not stored
-  auto fetch = [&](V8 (&a)[NB], V8 (&b)[NB], int g0) {
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int r = min((g0 + k * (kThreads / 64)) * RPG + rl, rows - 1);
-      a[k] = load8<T>(o + base + (size_t)r * D);
-      b[k] = load8<T>(dout + base + (size_t)r * D);
-    }
-  };
-  auto reduce = [&](const V8 (&a)[NB], const V8 (&b)[NB], int g0) {
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const f32x8 fa = to_f32x8(a[k]), fb = to_f32x8(b[k]);
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sum += fa[i] * fb[i];
-      sum += dpp_f<0xB1>(sum);    // quad_perm 1,0,3,2
-      sum += dpp_f<0x4E>(sum);    // quad_perm 2,3,0,1
-      sum += dpp_f<0x141>(sum);   // row_half_mirror: the other quad of 8 lanes
-      if (UPH == 16) sum += dpp_f<0x140>(sum);  // row_mirror: the other 8 of 16
-      const int r = (g0 + k * (kThreads / 64)) * RPG + rl;
-      if (lane % UPH == 0 && r < rows) red[r] = sum;
-    }
-  };
-  // wave w takes groups w, w + 4, ...: NB of them per step, two register sets
-  // alternating (unrolled by two so the set is a compile-time choice)
-  constexpr int STEP = NB * (kThreads / 64);
-  int g = wave;
-  fetch(a0, b0, g);
-  for (; g < groups; g += 2 * STEP) {
-    fetch(a1, b1, g + STEP);
-    reduce(a0, b0, g);
-    fetch(a0, b0, g + 2 * STEP);
-    reduce(a1, b1, g + STEP);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < rows; i += kThreads) {
-    const int h = i / nt, t = i - h * nt;
-    delta[(size_t)h * n_tokens + t0 + t] = red[t * n_heads + h];
-  }
-}
-
-template <typename T, bool ROPE>
-static void pre_b(const Meta& m, BlockShape bs, dim3 grid, const void* o, const void* dout,
-                  const void* q, const void* k, float* delta, void* qr, void* kr,
-                  hipStream_t stream) {
-#define PVJ_PRE(B)                                                                         \
-  bwd_pre_kernel<T, ROPE, B><<<grid, kThreads, 0, stream>>>(                               \
-      m, (const T*)o, (const T*)dout, (const T*)q, (const T*)k, delta, (T*)qr, (T*)kr, bs.rows)
-  switch (bs.batch) {
-    case 1: PVJ_PRE(1); break;
-    case 2: PVJ_PRE(2); break;
-    case 3: PVJ_PRE(3); break;
-    default: PVJ_PRE(4);
-  }
-#undef PVJ_PRE
-}
-
-hipError_t launch_bwd_pre(const pvj_plan* p, const Meta& m, const void* o, const void* dout,
-                          const void* q, const void* k, float* delta, void* qr, void* kr,
-                          bool rope, hipStream_t stream) {
-  if (m.n_tokens == 0) return hipSuccess;
-  const bool bf = p->desc.dtype == PVJ_BF16;
-  if (!rope) {
-    constexpr int NB = 4;  // groups of 64 units per wave and step
-    // 128 tokens per block (fewer with many heads: the row sums stay within 16
-    // KB of LDS), so each head's Delta is written as 512-byte runs and each wave
-    // streams ~200 KB.  Measured on the training pack (H = 24): 8-64 tokens per
-    // block 0.125-0.129 ms, 128 tokens 0.122 ms; 2, 4 or 8 groups per step alike
-    const int tb = std::max(1, std::min(128, 4096 / m.n_heads));
-    const dim3 g((unsigned)((m.n_tokens + tb - 1) / tb));
-    const size_t lds = (size_t)tb * m.n_heads * sizeof(float);
-#define PVJ_DELTA(TT, DD)                                                                    \
-  delta_kernel<TT, DD, NB><<<g, kThreads, lds, stream>>>((const TT*)o, (const TT*)dout, delta, \
-                                                          m.n_tokens, m.n_heads, tb)
-    if (bf && m.head_dim == 128) PVJ_DELTA(bf16, 128);
-    else if (bf) PVJ_DELTA(bf16, 64);
-    else if (m.head_dim == 128) PVJ_DELTA(float, 128);
-    else PVJ_DELTA(float, 64);
-#undef PVJ_DELTA
-    return hipGetLastError();
-  }
-  const BlockShape bs = block_shape(m, bf ? 2 : 4);
-  const dim3 grid((m.n_tokens + bs.rows - 1) / bs.rows);
-  if (bf) {
-    if (rope) pre_b<bf16, true>(m, bs, grid, o, dout, q, k, delta, qr, kr, stream);
-    else pre_b<bf16, false>(m, bs, grid, o, dout, q, k, delta, qr, kr, stream);
-  } else {
-    if (rope) pre_b<float, true>(m, bs, grid, o, dout, q, k, delta, qr, kr, stream);
-    else pre_b<float, false>(m, bs, grid, o, dout, q, k, delta, qr, kr, stream);
   }
   return hipGetLastError();
 }

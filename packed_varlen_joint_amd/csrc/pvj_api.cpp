@@ -164,23 +164,24 @@ pvj_status_t run_attn_bwd(const pvj_plan* p, const void* q, const void* k, const
   const bool unrotate = rope || (flags & PVJ_FLAG_ROPE_PREROTATED) != 0;
   const bool sm = (flags & PVJ_FLAG_STREAM_MAJOR) != 0;
   const float scale = resolve_scale(p, softmax_scale);
-  {
+  if (rope) {  // Q' = R Q, K' = R K (the standalone rotation, same bits)
     KernelTimer t(PVJ_KERNEL_BWD_PRE, s);
-    PVJ_TRY(launched(t.done(launch_bwd_pre(p, m, o, dout, q, k, delta, qr, kr, rope, s)),
-                     "bwd preprocess"));
+    hipError_t e = launch_rope2d(p, m, q, qr, false, false, s);
+    if (e == hipSuccess) e = launch_rope2d(p, m, k, kr, false, false, s);
+    PVJ_TRY(launched(t.done(e), "bwd RoPE of Q and K"));
   }
   const void* qq = rope ? qr : q;
   const void* kk = rope ? kr : k;
-  {
-    KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
-    PVJ_TRY(launched(t.done(launch_attn_bwd(p, m, 0, qq, kk, v, dout, lse, delta, dq, dk, dv,
-                                            scale, unrotate, sm, s)),
-                     "varlen_attn_bwd dK/dV"));
+  {  // dQ first: it also writes Delta = rowsum(dO * O), which dK/dV reads
+    KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
+    PVJ_TRY(launched(t.done(launch_attn_bwd_dq(p, m, qq, kk, v, o, dout, lse, delta, dq, scale,
+                                               unrotate, sm, s)),
+                     "varlen_attn_bwd dQ"));
   }
-  KernelTimer t(PVJ_KERNEL_ATTN_BWD_DQ, s);
-  return launched(t.done(launch_attn_bwd(p, m, 1, qq, kk, v, dout, lse, delta, dq, dk, dv, scale,
+  KernelTimer t(PVJ_KERNEL_ATTN_BWD, s);
+  return launched(t.done(launch_attn_bwd(p, m, qq, kk, v, dout, lse, delta, dk, dv, scale,
                                          unrotate, sm, s)),
-                  "varlen_attn_bwd dQ");
+                  "varlen_attn_bwd dK/dV");
 }
 
 }  // namespace pvj

@@ -17,22 +17,18 @@ hipError_t launch_rope2d(const pvj_plan* p, const Meta& m, const void* x, void* 
 hipError_t launch_attn_fwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
                            const void* v, void* o, float* lse, float scale, bool rope, bool sm,
                            hipStream_t stream);
-// Delta = rowsum(dO * O) into delta [H, T]; with rope also Q' = R Q -> qr and
-// K' = R K -> kr (same layout as q, k)
-hipError_t launch_bwd_pre(const pvj_plan* p, const Meta& m, const void* o, const void* dout,
-                          const void* q, const void* k, float* delta, void* qr, void* kr,
-                          bool rope, hipStream_t stream);
-// dK, dV (kernel 0) and dQ (kernel 1) from Q', K' (already rotated when rope),
-// V, dO, LSE, Delta; with rope the stored dK, dQ are rotated back by R^T
-hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, int which, const void* q,
-                           const void* k, const void* v, const void* dout, const float* lse,
-                           const float* delta, void* dq, void* dk, void* dv, float scale,
-                           bool rope, bool sm, hipStream_t stream);
-// the dQ kernel alone (launch_attn_bwd with which = 1 calls it)
+// dQ from Q', K' (already rotated when rope), V, O, dO, LSE; it also writes
+// Delta = rowsum(dO * O) [H, T], which the dK/dV kernel reads, so it runs first
 hipError_t launch_attn_bwd_dq(const pvj_plan* p, const Meta& m, const void* q, const void* k,
-                              const void* v, const void* dout, const float* lse,
-                              const float* delta, void* dq, float scale, bool rope, bool sm,
+                              const void* v, const void* o, const void* dout, const float* lse,
+                              float* delta, void* dq, float scale, bool rope, bool sm,
                               hipStream_t stream);
+// dK, dV from Q', K', V, dO, LSE and Delta; with rope the stored dK (and, in
+// the dQ kernel, dQ) are rotated back by R^T
+hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, const void* q, const void* k,
+                           const void* v, const void* dout, const float* lse,
+                           const float* delta, void* dk, void* dv, float scale, bool rope,
+                           bool sm, hipStream_t stream);
 
 // memory-bound chains on one stream (which: 0 text, 1 image) of C columns
 // row ranges per sample of the per-sample reductions, from the stream's
