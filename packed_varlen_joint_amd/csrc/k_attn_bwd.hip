@@ -5,10 +5,10 @@
 // per GPU).  Gradients of sum(O * dO), per sample and head:
 //   P = exp(s Q'K'^T - LSE); dV = P^T dO; dP = dO V^T; dS = P * (dP - Delta);
 //   dK' = s dS^T Q'; dQ' = s dS K'; with RoPE, dK = R^T dK' and dQ = R^T dQ'.
-// Two kernels, no atomics, fully deterministic: this file's dK/dV kernel and
-// the dQ kernel (k_attn_dq.hip).  With RoPE, the preprocess kernel writes
-// Q' = R Q and K' = R K once into the workspace, so both read pre-rotated
-// operands.
+// Two kernels, no atomics, fully deterministic: the dQ kernel
+// (k_attn_dq.hip), which also forms Delta, then this file's dK/dV kernel.
+// With RoPE on load, Q' = R Q and K' = R K are first written once into the
+// workspace by the standalone rotation, so both read pre-rotated operands.
 //
 // attn_bwd_dkdv_kernel: one workgroup per (sample, head, 128-key tile), 4
 // waves x 32 keys; bf16 fits two workgroups per CU (two waves per SIMD: 64.5

@@ -14,7 +14,9 @@
 // dQ'^T += K'^T dS^T takes dS^T straight from the accumulators and K'^T by
 // transposing reads.  The epilogue scales, applies R^T (rotation pairs are in
 // one lane) and stores dQ in the output dtype.  No atomics: each dQ row is
-// written by exactly one workgroup.
+// written by exactly one workgroup.  The kernel also forms Delta =
+// rowsum(dO * O) of its queries (it loads their O rows beside the dO rows)
+// and stores it for the dK/dV kernel, which runs after it.
 
 #include <type_traits>
 
