@@ -90,11 +90,17 @@ def test_sm_bitwise_equals_joint(D, pack):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("dt,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
-def test_sm_rope_bitwise_equals_joint(dt, D):
+# an editing pack: samples of several frames (3-axis RoPE: row, column, frame)
+FRAMES = [(3, 4, 5, 2), (0, 0, 7, 1), (2, 6, 0, 3), (5, 5, 33, 2), (1, 1, 1, 1)]
+
+
+@pytest.mark.parametrize("dt,D,pack", [("bf16", 128, "ragged"), ("bf16", 64, "ragged"),
+                                       ("f32", 64, "ragged"), ("bf16", 128, "frames")])
+def test_sm_rope_bitwise_equals_joint(dt, D, pack):
     H = 3
-    plan = _plan(RAGGED, H, D, dt)
-    say("stream-major rope dt=%s D=%d" % (dt, D))
+    samples = RAGGED if pack == "ragged" else FRAMES
+    plan = _plan(samples, H, D, dt)
+    say("stream-major rope dt=%s D=%d pack=%s" % (dt, D, pack))
     perm = pvj.stream_major_rows(plan).cuda()
     x, = draw_tensors(plan.n_tokens, H, D, dt, 5, n=1)
     xd = to_dev(x, dt)
