@@ -429,6 +429,25 @@ def proj_bench(wl, reps):
         torch.matmul(o_t.view(-1, HD), wo["text"].t(), out=ys["text"])
         torch.matmul(o_i.view(-1, HD), wo["image"].t(), out=ys["image"])
 
+    # the stream-major layout: the library GEMMs write Q, K, V straight into
+    # the text rows and the image rows of one tensor each, RoPE is one pass
+    # over Q and K in place, and the output GEMMs read O's two row ranges; no
+    # pack or unpack pass
+    nt = plan.n_text
+    sm = [torch.empty(plan.n_tokens, wl.n_heads, wl.head_dim, device="cuda",
+                      dtype=torch.bfloat16) for _ in range(3)]
+
+    def qkv_stream_major():
+        for w, rr in (("text", slice(0, nt)), ("image", slice(nt, None))):
+            for i in range(3):
+                torch.matmul(xs[w], wparts[w][i].t(), out=sm[i][rr].view(-1, HD))
+        pvj.rope2d_apply(plan, sm[0], sm[0], stream_major=True)
+        pvj.rope2d_apply(plan, sm[1], sm[1], stream_major=True)
+
+    def out_stream_major():
+        torch.matmul(sm[2][:nt].view(-1, HD), wo["text"].t(), out=ys["text"])
+        torch.matmul(sm[2][nt:].view(-1, HD), wo["image"].t(), out=ys["image"])
+
     ops = {
         "qkv_proj_pack": (2.0 * rows * C * 3 * HD, lambda: [pvj.qkv_proj_pack(
             plan, w, xs[w], wq[w], q=q, k=k, v=v, rope=True) for w in xs]),
@@ -436,6 +455,8 @@ def proj_bench(wl, reps):
             plan, w, q, wo[w], y=ys[w]) for w in xs]),
         "qkv_library_gemm_then_pack": (2.0 * rows * C * 3 * HD, qkv_unfused),
         "out_unpack_then_library_gemm": (2.0 * rows * HD * C, out_unfused),
+        "qkv_library_gemm_stream_major": (2.0 * rows * C * 3 * HD, qkv_stream_major),
+        "out_library_gemm_stream_major": (2.0 * rows * HD * C, out_stream_major),
     }
     out = {}
     for name, (flop, fn) in ops.items():
@@ -457,7 +478,9 @@ def proj_bench(wl, reps):
         "out": round(out["out_proj_unpack"]["ms"] / out["out_unpack_then_library_gemm"]["ms"], 3)}
     out["_note"] = ("both streams per call, hidden %d, %d rows; *_library_* = torch matmul "
                     "(hipBLASLt) per stream and projection plus the separate pack (+RoPE) or "
-                    "unpack pass" % (C, rows))
+                    "unpack pass; *_stream_major = the same GEMMs writing / reading the "
+                    "stream-major tensors' row ranges, RoPE one in-place pass over Q and K, "
+                    "no pack or unpack" % (C, rows))
     return out
 
 
