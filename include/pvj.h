@@ -243,6 +243,8 @@ PVJ_API pvj_status_t pvj_rope2d_apply_stream_major(const pvj_plan_t* plan, const
  * plan buffer's slots and are merged in a fixed order by a second kernel on
  * the same stream; so two forward calls on one uploaded plan must not run at
  * the same time (on different streams).
+ * flags: PVJ_FLAG_ROPE_FUSED, PVJ_FLAG_STREAM_MAJOR (token tensors and LSE's
+ * columns in the stream-major row order, above); others are INVALID_ARG.
  */
 PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* plan, const void* q, const void* k,
                                          const void* v, void* o, float* lse,
@@ -266,7 +268,9 @@ PVJ_API pvj_status_t pvj_varlen_attn_fwd(const pvj_plan_t* plan, const void* q, 
  * it holds Delta (fp32 [H, T]) and, with PVJ_FLAG_ROPE_FUSED, the rotated
  * Q' and K' (two [T, H, D] tensors in the plan dtype; the size always counts
  * them).  No atomics: dQ, dK
- * and dV are deterministic (the same inputs give the same bits).
+ * and dV are deterministic (the same inputs give the same bits).  Enqueued
+ * as: (RoPE on load only) the rotation of Q and K, the dQ pass, which also
+ * forms Delta, then the dK/dV pass.  PVJ_FLAG_STREAM_MAJOR as in the forward.
  */
 PVJ_API pvj_status_t pvj_varlen_attn_bwd_workspace(const pvj_plan_t* plan, size_t* bytes);
 PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* plan, const void* q, const void* k,
