@@ -201,3 +201,18 @@ def test_sm_bitwise_train_pack():
         got = b[:, perm] if name == "lse" else b[perm]
         say("   %s" % name)
         assert torch.equal(got, a), name + " differs from the joint layout"
+
+
+def test_sm_bitwise_inference_pack():
+    # the multi-prompt CFG inference pack (12 samples, ~87K tokens), forward
+    wl = workload("infer_multi", 0)
+    plan = _plan(wl.samples, wl.n_heads, wl.head_dim, wl.dtype)
+    say("stream-major vs joint infer_multi T=%d samples=%d" % (wl.n_tokens, len(wl.samples)))
+    perm = pvj.stream_major_rows(plan).cuda()
+    q, k, v = (to_dev(x, "bf16") for x in workload_tensors(wl, 3))
+    o, lse = pvj.varlen_attn_fwd(plan, q, k, v)
+    o_s, lse_s = pvj.varlen_attn_fwd(plan, *(_to_sm(x, perm) for x in (q, k, v)),
+                                     stream_major=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s[perm], o)
+    assert torch.equal(lse_s[:, perm], lse)
