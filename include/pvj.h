@@ -428,9 +428,9 @@ enum {
   PVJ_KERNEL_UNPACK = 1,
   PVJ_KERNEL_ROPE = 2,
   PVJ_KERNEL_ATTN_FWD = 3,
-  PVJ_KERNEL_BWD_PRE = 4,
+  PVJ_KERNEL_BWD_PRE = 4,          /* the backward's rotation of Q, K (RoPE on load only) */
   PVJ_KERNEL_ATTN_BWD = 5,         /* dK, dV */
-  PVJ_KERNEL_ATTN_BWD_DQ = 6,
+  PVJ_KERNEL_ATTN_BWD_DQ = 6,      /* dQ and Delta */
   PVJ_KERNEL_CHAIN_FWD = 7,        /* adaptive layer norm, gate + residual */
   PVJ_KERNEL_CHAIN_BWD = 8,        /* their backward passes */
   PVJ_KERNEL_PROJ = 9,             /* projections with the pack / unpack fused */
