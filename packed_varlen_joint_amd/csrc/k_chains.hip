@@ -724,12 +724,13 @@ static int rows_per_wave(int rows, int n_samples, int C) {
   return r < 4 ? 4 : r;
 }
 static int n_slots(int rows, int n_samples, int R) { return rows / R + n_samples + 1; }
-// rows per slot of the gate backward: one round of its waves (64-lane
-// workgroups, one per slot and 512-column chunk; about 8192 fit the chip at
-// once), at least 8 rows each
+// rows per slot of the gate backward (64-lane workgroups, one per slot and
+// 512-column chunk), at least 8 rows each: 2048 waves in all, two per SIMD
+// (four fit at its ~110 registers; measured on the training pack at hidden
+// 3072: 2048 waves 0.199 ms, 4096 0.201, 8192 (two rounds) 0.208, 1024 0.202)
 static int gate_rows_per_slot(int rows, int n_samples, int C) {
   const int nchunk = (C + kColChunk - 1) / kColChunk;
-  const int slots = 8192 / nchunk - n_samples - 1;
+  const int slots = 2048 / nchunk - n_samples - 1;
   const int r = slots > 0 ? (rows + slots - 1) / slots : rows;
   return r < 8 ? 8 : r;
 }
