@@ -62,11 +62,17 @@ def _run(plan, q, k, v, do, sm, prerot):
     return o, lse, g[0].t, g[1].t, g[2].t
 
 
-@pytest.mark.parametrize("D", [128, 64])
-@pytest.mark.parametrize("pack", ["ragged", "split"])
+# packs with an empty image stream or an empty text stream
+TEXT_ONLY = [(0, 0, 37), (0, 0, 300), (0, 0, 1)]
+IMAGE_ONLY = [(7, 9, 0), (16, 20, 0), (1, 1, 0)]
+PACKS = {"ragged": RAGGED, "split": SPLIT, "text_only": TEXT_ONLY, "image_only": IMAGE_ONLY}
+
+
+@pytest.mark.parametrize("D,pack", [(128, "ragged"), (64, "ragged"), (128, "split"),
+                                    (64, "split"), (128, "text_only"), (128, "image_only")])
 def test_sm_bitwise_equals_joint(D, pack):
-    samples = RAGGED if pack == "ragged" else SPLIT
-    H = 3 if pack == "ragged" else 2
+    samples = PACKS[pack]
+    H = 2 if pack == "split" else 3
     plan = _plan(samples, H, D)
     T = plan.n_tokens
     say("stream-major vs joint %s D=%d T=%d" % (pack, D, T))
@@ -95,10 +101,11 @@ FRAMES = [(3, 4, 5, 2), (0, 0, 7, 1), (2, 6, 0, 3), (5, 5, 33, 2), (1, 1, 1, 1)]
 
 
 @pytest.mark.parametrize("dt,D,pack", [("bf16", 128, "ragged"), ("bf16", 64, "ragged"),
-                                       ("f32", 64, "ragged"), ("bf16", 128, "frames")])
+                                       ("f32", 64, "ragged"), ("bf16", 128, "frames"),
+                                       ("bf16", 128, "text_only"), ("bf16", 128, "image_only")])
 def test_sm_rope_bitwise_equals_joint(dt, D, pack):
     H = 3
-    samples = RAGGED if pack == "ragged" else FRAMES
+    samples = FRAMES if pack == "frames" else PACKS[pack]
     plan = _plan(samples, H, D, dt)
     say("stream-major rope dt=%s D=%d pack=%s" % (dt, D, pack))
     perm = pvj.stream_major_rows(plan).cuda()
