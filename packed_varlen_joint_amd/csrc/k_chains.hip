@@ -144,12 +144,13 @@ __global__ __launch_bounds__(kChainThreads) void gate_fwd_kernel(
   }
   const int s = find_sample(cu, n_samples, row);
   const T* g = gate + (size_t)s * C;
-  // four units per lane at a time: all their loads go out before the stores
+  // six units per lane at a time (a 3,072-wide row in one batch; four per
+  // batch measured 1.4% slower): all their loads go out before the stores
   // (out may be x or y: every element is read before this lane writes it)
-  for (int u0 = lane; u0 < upr; u0 += 256) {
-    typename Vec8<T>::type a[4], b[4], w[4];
+  for (int u0 = lane; u0 < upr; u0 += 384) {
+    typename Vec8<T>::type a[6], b[6], w[6];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 6; ++k) {
       const int u = u0 + 64 * k;
       typename Vec8<T>::type z = {};
       a[k] = u < upr ? (u == lane ? x0 : load8<T>(x + ro + u * 8)) : z;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kChainThreads) void gate_fwd_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 6; ++k) {
       const int u = u0 + 64 * k;
       if (u < upr) {
         const f32x8 fa = to_f32x8(a[k]), fb = to_f32x8(b[k]), fw = to_f32x8(w[k]);
