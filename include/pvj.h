@@ -322,8 +322,17 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd_noalloc(const pvj_plan_t* plan, const v
  * the stream holds it.  Parameter gradients are fp32 [n_samples, hidden]
  * (zero for samples without rows in the stream).  Computation is fp32.
  * Deterministic: the per-sample sums are reduced in a fixed order.
+ *
+ * which = PVJ_STREAM_BOTH runs both streams in one call: row tensors are
+ * [n_text + n_image, hidden], the text stream's rows and then the image
+ * stream's (the stream-major row order above, at the model width), and every
+ * per-sample vector and parameter gradient is [2, n_samples, hidden], the
+ * text stream's parameters first.  Rows, and so y, out, dx and dy, get the
+ * same bits as the two one-stream calls; the parameter gradients add the same
+ * terms in another fixed order (the per-sample slots are cut from the joint
+ * row count), so they agree with the one-stream calls to fp32 rounding.
  */
-enum { PVJ_STREAM_TEXT = 0, PVJ_STREAM_IMAGE = 1 };
+enum { PVJ_STREAM_TEXT = 0, PVJ_STREAM_IMAGE = 1, PVJ_STREAM_BOTH = 2 };
 enum { PVJ_CHAIN_ADALN = 0, PVJ_CHAIN_GATE = 1 };
 
 /* y = LN(x) * (1 + scale_i) + shift_i, LN over hidden with `eps` (1e-6).
@@ -335,8 +344,9 @@ PVJ_API pvj_status_t pvj_adaln_modulate(const pvj_plan_t* plan, int32_t which, i
 PVJ_API pvj_status_t pvj_gate_residual(const pvj_plan_t* plan, int32_t which, int32_t hidden,
                                        const void* x, const void* y, const void* gate, void* out,
                                        void* stream);
-/* Workspace of a chain backward (op = PVJ_CHAIN_ADALN or PVJ_CHAIN_GATE):
- * per-sample partial sums, and for the layer norm the row statistics. */
+/* Workspace of a chain backward (op = PVJ_CHAIN_ADALN or PVJ_CHAIN_GATE) on
+ * stream `which` (PVJ_STREAM_BOTH included): per-sample partial sums, and for
+ * the layer norm the row statistics. */
 PVJ_API pvj_status_t pvj_chain_bwd_workspace(const pvj_plan_t* plan, int32_t op, int32_t which,
                                              int32_t hidden, size_t* bytes);
 /* Gradients of sum(y * dy): dx (plan dtype, rows x hidden), dshift_i = sum of

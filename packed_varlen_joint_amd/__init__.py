@@ -41,6 +41,9 @@ PVJ_FLAG_STREAM_MAJOR = 4
 KERNELS = {"pack": 0, "unpack": 1, "rope2d": 2, "attn_fwd": 3, "bwd_pre": 4, "attn_bwd": 5,
            "attn_bwd_dq": 6, "chain_fwd": 7, "chain_bwd": 8, "proj": 9}
 STREAMS = {"text": 0, "image": 1}
+# the chain ops also take both streams in one call: rows [n_text + n_image,
+# hidden] (text rows first), per-sample vectors [2 * n_samples, hidden]
+CHAIN_STREAMS = {"text": 0, "image": 1, "both": 2}
 CHAIN_ADALN, CHAIN_GATE = 0, 1
 
 
@@ -465,13 +468,23 @@ def varlen_attn_bwd_noalloc(plan: Plan, q, k, v, o, lse, dout, dq, dk, dv,
 
 
 # ---------------------------------------------------------------------------
-# memory-bound chains around the attention (one modality stream at a time)
+# memory-bound chains around the attention (one modality stream, or both)
 # ---------------------------------------------------------------------------
 
 def _stream_rows(plan: Plan, which: str) -> int:
     if which not in STREAMS:
         raise ValueError("stream must be 'text' or 'image'")
     return plan.n_text if which == "text" else plan.n_image
+
+
+def _chain_rows(plan: Plan, which: str):
+    """(rows, per-sample vector rows) of a chain call on `which`."""
+    if which not in CHAIN_STREAMS:
+        raise ValueError("stream must be 'text', 'image' or 'both'")
+    B = len(plan.samples)
+    if which == "both":
+        return plan.n_text + plan.n_image, 2 * B
+    return _stream_rows(plan, which), B
 
 
 def _check_2d(name, t, rows, cols, dtype):
@@ -483,35 +496,38 @@ def _check_2d(name, t, rows, cols, dtype):
 
 def chain_workspace_bytes(plan: Plan, op: int, which: str, hidden: int) -> int:
     b = ctypes.c_size_t()
-    _check(load_library().pvj_chain_bwd_workspace(plan.handle, op, STREAMS[which], int(hidden),
-                                                  ctypes.byref(b)))
+    _chain_rows(plan, which)
+    _check(load_library().pvj_chain_bwd_workspace(plan.handle, op, CHAIN_STREAMS[which],
+                                                  int(hidden), ctypes.byref(b)))
     return b.value
 
 
 def adaln_modulate(plan: Plan, which: str, x, shift, scale, y=None, eps: float = 1e-6):
-    """y = LN(x) (1 + scale_i) + shift_i on one stream ([rows, hidden])."""
-    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    """y = LN(x) (1 + scale_i) + shift_i on one stream ([rows, hidden]), or on
+    both (which="both": text rows then image rows, per-sample vectors
+    [2 * n_samples, hidden], the text stream's first)."""
+    (rows, nv), hidden = _chain_rows(plan, which), int(x.shape[-1])
     _check_2d("x", x, rows, hidden, plan.torch_dtype)
-    _check_2d("shift", shift, len(plan.samples), hidden, plan.torch_dtype)
-    _check_2d("scale", scale, len(plan.samples), hidden, plan.torch_dtype)
+    _check_2d("shift", shift, nv, hidden, plan.torch_dtype)
+    _check_2d("scale", scale, nv, hidden, plan.torch_dtype)
     y = _torch().empty_like(x) if y is None else y
     _check_2d("y", y, rows, hidden, plan.torch_dtype)
-    _check(load_library().pvj_adaln_modulate(plan.handle, STREAMS[which], hidden, _ptr(x),
+    _check(load_library().pvj_adaln_modulate(plan.handle, CHAIN_STREAMS[which], hidden, _ptr(x),
                                              _ptr(shift), _ptr(scale), _ptr(y), float(eps),
                                              _stream()))
     return y
 
 
 def gate_residual(plan: Plan, which: str, x, y, gate, out=None):
-    """out = x + gate_i * y on one stream."""
-    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    """out = x + gate_i * y on one stream, or on both (see adaln_modulate)."""
+    (rows, nv), hidden = _chain_rows(plan, which), int(x.shape[-1])
     for n, t in (("x", x), ("y", y)):
         _check_2d(n, t, rows, hidden, plan.torch_dtype)
-    _check_2d("gate", gate, len(plan.samples), hidden, plan.torch_dtype)
+    _check_2d("gate", gate, nv, hidden, plan.torch_dtype)
     out = _torch().empty_like(x) if out is None else out
     _check_2d("out", out, rows, hidden, plan.torch_dtype)
-    _check(load_library().pvj_gate_residual(plan.handle, STREAMS[which], hidden, _ptr(x), _ptr(y),
-                                            _ptr(gate), _ptr(out), _stream()))
+    _check(load_library().pvj_gate_residual(plan.handle, CHAIN_STREAMS[which], hidden, _ptr(x),
+                                            _ptr(y), _ptr(gate), _ptr(out), _stream()))
     return out
 
 
@@ -526,17 +542,17 @@ def adaln_modulate_bwd(plan: Plan, which: str, x, scale, dy, eps: float = 1e-6, 
                        workspace=None):
     """(dx, dshift fp32, dscale fp32) for ``adaln_modulate``."""
     torch = _torch()
-    rows, hidden = _stream_rows(plan, which), int(x.shape[-1])
+    (rows, nv), hidden = _chain_rows(plan, which), int(x.shape[-1])
     for n, t in (("x", x), ("dy", dy)):
         _check_2d(n, t, rows, hidden, plan.torch_dtype)
-    _check_2d("scale", scale, len(plan.samples), hidden, plan.torch_dtype)
+    _check_2d("scale", scale, nv, hidden, plan.torch_dtype)
     dx = torch.empty_like(x) if dx is None else dx
-    B = len(plan.samples)
-    dshift = torch.empty(B, hidden, dtype=torch.float32, device=x.device)
-    dscale = torch.empty(B, hidden, dtype=torch.float32, device=x.device)
+    _check_2d("dx", dx, rows, hidden, plan.torch_dtype)
+    dshift = torch.empty(nv, hidden, dtype=torch.float32, device=x.device)
+    dscale = torch.empty(nv, hidden, dtype=torch.float32, device=x.device)
     workspace = _ws(plan, CHAIN_ADALN, which, hidden, x, workspace)
     _check(load_library().pvj_adaln_modulate_bwd(
-        plan.handle, STREAMS[which], hidden, _ptr(x), _ptr(scale), _ptr(dy), _ptr(dx),
+        plan.handle, CHAIN_STREAMS[which], hidden, _ptr(x), _ptr(scale), _ptr(dy), _ptr(dx),
         _ptr(dshift), _ptr(dscale), float(eps), _ptr(workspace), workspace.numel(), _stream()))
     return dx, dshift, dscale
 
@@ -544,15 +560,16 @@ def adaln_modulate_bwd(plan: Plan, which: str, x, scale, dy, eps: float = 1e-6, 
 def gate_residual_bwd(plan: Plan, which: str, y, gate, dout, dy=None, workspace=None):
     """(dy, dgate fp32) for ``gate_residual``; the gradient of x is dout itself."""
     torch = _torch()
-    rows, hidden = _stream_rows(plan, which), int(y.shape[-1])
+    (rows, nv), hidden = _chain_rows(plan, which), int(y.shape[-1])
     for n, t in (("y", y), ("dout", dout)):
         _check_2d(n, t, rows, hidden, plan.torch_dtype)
-    _check_2d("gate", gate, len(plan.samples), hidden, plan.torch_dtype)
+    _check_2d("gate", gate, nv, hidden, plan.torch_dtype)
     dy = torch.empty_like(y) if dy is None else dy
-    dgate = torch.empty(len(plan.samples), hidden, dtype=torch.float32, device=y.device)
+    _check_2d("dy", dy, rows, hidden, plan.torch_dtype)
+    dgate = torch.empty(nv, hidden, dtype=torch.float32, device=y.device)
     workspace = _ws(plan, CHAIN_GATE, which, hidden, y, workspace)
     _check(load_library().pvj_gate_residual_bwd(
-        plan.handle, STREAMS[which], hidden, _ptr(y), _ptr(gate), _ptr(dout), _ptr(dy),
+        plan.handle, CHAIN_STREAMS[which], hidden, _ptr(y), _ptr(gate), _ptr(dout), _ptr(dy),
         _ptr(dgate), _ptr(workspace), workspace.numel(), _stream()))
     return dy, dgate
 

@@ -26,8 +26,10 @@
 //    ranges), one wave per (sample, range, 512-column chunk) writes a partial
 //    sum with four rows in flight, and seg_final adds the partials in a fixed
 //    order.
-// A row's sample i is found by binary search in the stream's cumulative
-// offsets (cu_text or cu_img of the plan).
+// A row's sample i is found by binary search in the call's segment offsets:
+// the stream's cumulative offsets (cu_text or cu_img of the plan), or, for
+// both streams in one call, 2B segments (sample i's text rows, then at B + i
+// its image rows), which also index the per-sample vectors [2, B, C].
 
 #include "pvj_device.h"
 #include "pvj_launch.h"
@@ -792,43 +794,43 @@ static void adaln_bwd_t(dim3 g, hipStream_t st, const int32_t* cu, int B, int ro
     else FN<T, 16>(__VA_ARGS__);                     \
   } while (0)
 
-hipError_t launch_adaln_fwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+hipError_t launch_adaln_fwd(const pvj_plan* p, int which, int C, const void* x,
                             const void* shift, const void* scale, void* y, float eps,
                             hipStream_t st) {
-  const int rows = which == 0 ? m.n_text : m.n_img;
+  const ChainRows r = chain_rows(p, which, false);
+  const int rows = r.rows;
   if (rows == 0) return hipSuccess;
-  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
   const dim3 g((rows + 3) / 4);
   if (p->desc.dtype == PVJ_BF16)
-    PVJ_NU_DISPATCH(adaln_fwd_t, bf16, g, st, cu, m.n_samples, rows, C, x, shift, scale, y, eps);
+    PVJ_NU_DISPATCH(adaln_fwd_t, bf16, g, st, r.cu, r.n_seg, rows, C, x, shift, scale, y, eps);
   else
-    PVJ_NU_DISPATCH(adaln_fwd_t, float, g, st, cu, m.n_samples, rows, C, x, shift, scale, y, eps);
+    PVJ_NU_DISPATCH(adaln_fwd_t, float, g, st, r.cu, r.n_seg, rows, C, x, shift, scale, y, eps);
   return hipGetLastError();
 }
 
-hipError_t launch_gate_fwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+hipError_t launch_gate_fwd(const pvj_plan* p, int which, int C, const void* x,
                            const void* y, const void* gate, void* out, hipStream_t st) {
-  const int rows = which == 0 ? m.n_text : m.n_img;
+  const ChainRows r = chain_rows(p, which, false);
+  const int rows = r.rows;
   if (rows == 0) return hipSuccess;
-  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
   const dim3 g((rows + 3) / 4);
   if (p->desc.dtype == PVJ_BF16)
-    gate_fwd_kernel<bf16><<<g, kChainThreads, 0, st>>>(cu, m.n_samples, rows, C, (const bf16*)x,
+    gate_fwd_kernel<bf16><<<g, kChainThreads, 0, st>>>(r.cu, r.n_seg, rows, C, (const bf16*)x,
                                                        (const bf16*)y, (const bf16*)gate, (bf16*)out);
   else
-    gate_fwd_kernel<float><<<g, kChainThreads, 0, st>>>(cu, m.n_samples, rows, C, (const float*)x,
+    gate_fwd_kernel<float><<<g, kChainThreads, 0, st>>>(r.cu, r.n_seg, rows, C, (const float*)x,
                                                         (const float*)y, (const float*)gate,
                                                         (float*)out);
   return hipGetLastError();
 }
 
-hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+hipError_t launch_adaln_bwd(const pvj_plan* p, int which, int C, const void* x,
                             const void* scale, const void* dy, void* dx, float* dshift,
                             float* dscale, float eps, int splits, void* ws, hipStream_t st) {
-  const int rows = which == 0 ? m.n_text : m.n_img;
-  const int B = m.n_samples;
+  const ChainRows r = chain_rows(p, which, false);
+  const int rows = r.rows, B = r.n_seg;
   if (B == 0) return hipSuccess;
-  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
+  const int32_t* cu = r.cu;
   const bool bf = p->desc.dtype == PVJ_BF16;
   if (one_pass(C)) {
     const int R = rows_per_wave(rows, B, C), ns = n_slots(rows, B, R);
@@ -880,13 +882,13 @@ hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, 
   return hipGetLastError();
 }
 
-hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, const void* y,
+hipError_t launch_gate_bwd(const pvj_plan* p, int which, int C, const void* y,
                            const void* gate, const void* dout, void* dy, float* dgate, int splits,
                            void* ws, hipStream_t st) {
-  const int B = m.n_samples;
+  const ChainRows r = chain_rows(p, which, false);
+  const int rows = r.rows, B = r.n_seg;
   if (B == 0) return hipSuccess;
-  const int32_t* cu = which == 0 ? m.cu_text : m.cu_img;
-  const int rows = which == 0 ? m.n_text : m.n_img;
+  const int32_t* cu = r.cu;
   float* partial = static_cast<float*>(ws);
   const int nchunk = (C + kColChunk - 1) / kColChunk;
   (void)splits;

@@ -335,13 +335,18 @@ PVJ_API pvj_status_t pvj_varlen_attn_bwd(const pvj_plan_t* p, const void* q, con
 
 // ---- memory-bound chains --------------------------------------------------
 
+static bool chain_stream(int32_t which) {
+  return which == PVJ_STREAM_TEXT || which == PVJ_STREAM_IMAGE || which == PVJ_STREAM_BOTH;
+}
+
 static pvj_status_t check_chain(const pvj_plan* p, int32_t which, int32_t hidden, int* rows) {
   PVJ_TRY(check_plan(p));
-  if (which != PVJ_STREAM_TEXT && which != PVJ_STREAM_IMAGE)
-    return fail(PVJ_ERR_INVALID_ARG, "stream must be PVJ_STREAM_TEXT or PVJ_STREAM_IMAGE");
+  if (!chain_stream(which))
+    return fail(PVJ_ERR_INVALID_ARG,
+                "stream must be PVJ_STREAM_TEXT, PVJ_STREAM_IMAGE or PVJ_STREAM_BOTH");
   if (hidden < 8 || hidden > 8192 || hidden % 8)
     return fail(PVJ_ERR_UNSUPPORTED, "hidden %d: need a multiple of 8 in [8, 8192]", hidden);
-  const int64_t n = which == PVJ_STREAM_TEXT ? p->n_text : p->n_img;
+  const int64_t n = chain_rows(p, which, true).rows;
   if (n * hidden * (int64_t)elt_size(p) >= (int64_t(1) << 40))
     return fail(PVJ_ERR_OVERFLOW, "stream tensor too large");
   *rows = (int)n;
@@ -359,7 +364,7 @@ PVJ_API pvj_status_t pvj_adaln_modulate(const pvj_plan_t* p, int32_t which, int3
   PVJ_TRY(check_ptr(scale, "scale", rows > 0));
   if (!(eps > 0.f) || !std::isfinite(eps)) return fail(PVJ_ERR_INVALID_ARG, "eps must be > 0");
   KernelTimer t(PVJ_KERNEL_CHAIN_FWD, static_cast<hipStream_t>(stream));
-  return launched(t.done(launch_adaln_fwd(p, device_meta(p), which, hidden, x, shift, scale, y,
+  return launched(t.done(launch_adaln_fwd(p, which, hidden, x, shift, scale, y,
                                           eps, static_cast<hipStream_t>(stream))),
                   "adaln_modulate");
 }
@@ -374,17 +379,16 @@ PVJ_API pvj_status_t pvj_gate_residual(const pvj_plan_t* p, int32_t which, int32
   PVJ_TRY(check_ptr(gate, "gate", rows > 0));
   PVJ_TRY(check_ptr(out, "out", rows > 0));
   KernelTimer t(PVJ_KERNEL_CHAIN_FWD, static_cast<hipStream_t>(stream));
-  return launched(t.done(launch_gate_fwd(p, device_meta(p), which, hidden, x, y, gate, out,
+  return launched(t.done(launch_gate_fwd(p, which, hidden, x, y, gate, out,
                                          static_cast<hipStream_t>(stream))),
                   "gate_residual");
 }
 
-// row ranges per sample of the chain reductions (from the stream's longest sample)
+// row ranges per sample of the chain reductions (from the call's longest segment)
 static int stream_splits(const pvj_plan* p, int32_t which) {
-  const int32_t* cu = host_section<int32_t>(p, which == PVJ_STREAM_TEXT ? p->off_cu_text
-                                                                        : p->off_cu_img);
+  const ChainRows r = chain_rows(p, which, true);
   int mx = 0;
-  for (int i = 0; i < p->n_samples; ++i) mx = std::max(mx, (int)(cu[i + 1] - cu[i]));
+  for (int i = 0; i < r.n_seg; ++i) mx = std::max(mx, (int)(r.cu[i + 1] - r.cu[i]));
   return chain_splits(mx);
 }
 
@@ -394,12 +398,13 @@ PVJ_API pvj_status_t pvj_chain_bwd_workspace(const pvj_plan_t* p, int32_t op, in
   if (!bytes) return fail(PVJ_ERR_INVALID_ARG, "bytes is NULL");
   if (op != PVJ_CHAIN_ADALN && op != PVJ_CHAIN_GATE)
     return fail(PVJ_ERR_INVALID_ARG, "op must be PVJ_CHAIN_ADALN or PVJ_CHAIN_GATE");
-  if (which != PVJ_STREAM_TEXT && which != PVJ_STREAM_IMAGE)
-    return fail(PVJ_ERR_INVALID_ARG, "stream must be PVJ_STREAM_TEXT or PVJ_STREAM_IMAGE");
+  if (!chain_stream(which))
+    return fail(PVJ_ERR_INVALID_ARG,
+                "stream must be PVJ_STREAM_TEXT, PVJ_STREAM_IMAGE or PVJ_STREAM_BOTH");
   if (hidden < 8 || hidden > 8192 || hidden % 8)
     return fail(PVJ_ERR_UNSUPPORTED, "hidden %d: need a multiple of 8 in [8, 8192]", hidden);
-  const int rows = which == PVJ_STREAM_TEXT ? p->n_text : p->n_img;
-  *bytes = chain_workspace_bytes(p->n_samples, hidden, rows, op == PVJ_CHAIN_ADALN ? 0 : 1,
+  const ChainRows r = chain_rows(p, which, true);
+  *bytes = chain_workspace_bytes(r.n_seg, hidden, r.rows, op == PVJ_CHAIN_ADALN ? 0 : 1,
                                  stream_splits(p, which));
   return PVJ_OK;
 }
@@ -432,7 +437,7 @@ PVJ_API pvj_status_t pvj_adaln_modulate_bwd(const pvj_plan_t* p, int32_t which, 
   if (!(eps > 0.f) || !std::isfinite(eps)) return fail(PVJ_ERR_INVALID_ARG, "eps must be > 0");
   PVJ_TRY(check_ws(p, PVJ_CHAIN_ADALN, which, hidden, workspace, ws_bytes));
   KernelTimer t(PVJ_KERNEL_CHAIN_BWD, static_cast<hipStream_t>(stream));
-  return launched(t.done(launch_adaln_bwd(p, device_meta(p), which, hidden, x, scale, dy, dx,
+  return launched(t.done(launch_adaln_bwd(p, which, hidden, x, scale, dy, dx,
                                           dshift, dscale, eps, stream_splits(p, which), workspace,
                                           static_cast<hipStream_t>(stream))),
                   "adaln_modulate_bwd");
@@ -451,7 +456,7 @@ PVJ_API pvj_status_t pvj_gate_residual_bwd(const pvj_plan_t* p, int32_t which, i
   PVJ_TRY(check_ptr(dgate, "dgate", p->n_samples > 0));
   PVJ_TRY(check_ws(p, PVJ_CHAIN_GATE, which, hidden, workspace, ws_bytes));
   KernelTimer t(PVJ_KERNEL_CHAIN_BWD, static_cast<hipStream_t>(stream));
-  return launched(t.done(launch_gate_bwd(p, device_meta(p), which, hidden, y, gate, dout, dy,
+  return launched(t.done(launch_gate_bwd(p, which, hidden, y, gate, dout, dy,
                                          dgate, stream_splits(p, which), workspace,
                                          static_cast<hipStream_t>(stream))),
                   "gate_residual_bwd");

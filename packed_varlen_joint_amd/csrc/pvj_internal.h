@@ -118,7 +118,8 @@ struct pvj_plan {
   // (off_part, part_bytes), which are not uploaded
   uint8_t* image;
   size_t image_bytes;
-  size_t off_cu, off_cu_text, off_cu_img, off_sinfo, off_cos, off_sin, off_fwd, off_bwd;
+  // off_cu_both: the 2B + 1 segment offsets of both streams as one row range
+  size_t off_cu, off_cu_text, off_cu_img, off_cu_both, off_sinfo, off_cos, off_sin, off_fwd, off_bwd;
   size_t off_dq, off_split, off_part, part_bytes;
   // device copy (set by pvj_plan_upload)
   void* dev_meta;
@@ -157,4 +158,16 @@ template <typename T>
 inline const T* host_section(const pvj_plan* p, size_t off) {
   return reinterpret_cast<const T*>(p->image + off);
 }
+
+// Rows of one chain call: the text stream, the image stream, or both as one
+// range (the text stream's rows, then the image stream's), cut into segments
+// that each take one row of the per-sample vectors: the plan's samples for one
+// stream; for both, 2B segments, sample i's text rows at i and its image rows
+// at B + i.  cu holds the n_seg + 1 segment offsets (device copy, or the host
+// image with `host`).
+struct ChainRows {
+  const int32_t* cu;
+  int rows, n_seg;
+};
+ChainRows chain_rows(const pvj_plan* p, int which, bool host);
 }  // namespace pvj

@@ -35,15 +35,15 @@ hipError_t launch_attn_bwd(const pvj_plan* p, const Meta& m, const void* q, cons
 // longest sample; workspace for mode 0 (adaln) or 1 (gate)
 int chain_splits(int max_sample_rows);
 size_t chain_workspace_bytes(int n_samples, int C, int rows, int mode, int splits);
-hipError_t launch_adaln_fwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+hipError_t launch_adaln_fwd(const pvj_plan* p, int which, int C, const void* x,
                             const void* shift, const void* scale, void* y, float eps,
                             hipStream_t stream);
-hipError_t launch_gate_fwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+hipError_t launch_gate_fwd(const pvj_plan* p, int which, int C, const void* x,
                            const void* y, const void* gate, void* out, hipStream_t stream);
-hipError_t launch_adaln_bwd(const pvj_plan* p, const Meta& m, int which, int C, const void* x,
+hipError_t launch_adaln_bwd(const pvj_plan* p, int which, int C, const void* x,
                             const void* scale, const void* dy, void* dx, float* dshift,
                             float* dscale, float eps, int splits, void* ws, hipStream_t stream);
-hipError_t launch_gate_bwd(const pvj_plan* p, const Meta& m, int which, int C, const void* y,
+hipError_t launch_gate_bwd(const pvj_plan* p, int which, int C, const void* y,
                            const void* gate, const void* dout, void* dy, float* dgate, int splits,
                            void* ws, hipStream_t stream);
 

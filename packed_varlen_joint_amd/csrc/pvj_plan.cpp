@@ -99,6 +99,18 @@ static std::vector<Item> build_items(const std::vector<int32_t>& len, int n_head
   return out;
 }
 
+ChainRows chain_rows(const pvj_plan* p, int which, bool host) {
+  const uint8_t* b = host ? p->image : static_cast<const uint8_t*>(p->dev_meta);
+  const size_t off = which == PVJ_STREAM_TEXT    ? p->off_cu_text
+                     : which == PVJ_STREAM_IMAGE ? p->off_cu_img
+                                                 : p->off_cu_both;
+  const int rows = which == PVJ_STREAM_TEXT    ? p->n_text
+                   : which == PVJ_STREAM_IMAGE ? p->n_img
+                                               : p->n_text + p->n_img;
+  const int n_seg = which == PVJ_STREAM_BOTH ? 2 * p->n_samples : p->n_samples;
+  return {reinterpret_cast<const int32_t*>(b + off), rows, n_seg};
+}
+
 Meta device_meta(const pvj_plan* p) {
   const uint8_t* b = static_cast<const uint8_t*>(p->dev_meta);
   Meta m;
@@ -273,6 +285,7 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
   p->off_cu = section((B + 1) * sizeof(int32_t));
   p->off_cu_text = section((B + 1) * sizeof(int32_t));
   p->off_cu_img = section((B + 1) * sizeof(int32_t));
+  p->off_cu_both = section((2 * B + 1) * sizeof(int32_t));
   p->off_sinfo = section(B * sizeof(SampleInfo));
   p->off_cos = section(tab);
   p->off_sin = section(tab);
@@ -291,6 +304,11 @@ static pvj_status_t create_plan(const int32_t* hwtf, int32_t n_samples, int axes
   std::memcpy(p->image + p->off_cu, cu.data(), (B + 1) * sizeof(int32_t));
   std::memcpy(p->image + p->off_cu_text, cu_text.data(), (B + 1) * sizeof(int32_t));
   std::memcpy(p->image + p->off_cu_img, cu_img.data(), (B + 1) * sizeof(int32_t));
+  {
+    int32_t* cb = reinterpret_cast<int32_t*>(p->image + p->off_cu_both);
+    for (int i = 0; i <= B; ++i) cb[i] = cu_text[i];
+    for (int i = 1; i <= B; ++i) cb[B + i] = cu_text[B] + cu_img[i];
+  }
   if (B) std::memcpy(p->image + p->off_sinfo, sinfo.data(), B * sizeof(SampleInfo));
   // RoPE tables: pair k belongs to axis part a; as pair j of that part its angle
   // is pos * theta^(-j / (d_a/2)), computed in double and rounded to float once

@@ -297,6 +297,27 @@ def test_bwd_workspace_size(lib):
         assert p.bwd_workspace_bytes() == al(T * H * 4) + 2 * al(T * H * D * elt)
 
 
+def test_chain_workspace_streams(lib):
+    # text, image and both streams in one call (the host-side query only)
+    p = _plan([(3, 3, 2), (0, 0, 5), (4, 2, 0)], 2, 64, "bf16")
+    sizes = {}
+    for op in (0, 1):
+        for which in (0, 1, 2):
+            b = ctypes.c_size_t()
+            assert lib.pvj_chain_bwd_workspace(p.handle, op, which, 3072, ctypes.byref(b)) == 0
+            assert b.value > 0 and b.value % 256 == 0
+            sizes[op, which] = b.value
+        b = ctypes.c_size_t()
+        assert lib.pvj_chain_bwd_workspace(p.handle, op, 3, 3072, ctypes.byref(b)) == 1
+        assert lib.pvj_chain_bwd_workspace(p.handle, op, 2, 12, ctypes.byref(b)) == 2
+    # both streams hold every row and twice the segments: no smaller than either
+    for op in (0, 1):
+        assert sizes[op, 2] >= max(sizes[op, 0], sizes[op, 1])
+    # a both-streams call on a plan not yet uploaded is refused before any device call
+    q = _plan([(3, 3, 2)], 1, 64, "bf16")
+    assert lib.pvj_gate_residual(q.handle, 2, 64, 16, 16, 16, 16, None) == 4
+
+
 def test_noalloc_bwd_limits_before_any_device_call(lib):
     # the allocation-free backward checks its fixed scratch size and flags
     # before touching HIP (the plan is not even uploaded here)

@@ -193,5 +193,73 @@ def test_chain_errors():
     with pytest.raises(pvj.PvjError):   # hidden not a multiple of 8
         pvj.adaln_modulate(plan, "image", x, v, v)
     lib = pvj.load_library()
-    assert lib.pvj_adaln_modulate(plan.handle, 2, 64, 16, 16, 16, 16, 1e-6, None) == 1
+    # stream selector 3 is refused before any launch (0, 1, 2: text, image, both)
+    assert lib.pvj_adaln_modulate(plan.handle, 3, 64, 16, 16, 16, 16, 1e-6, None) == 1
     assert lib.pvj_gate_residual(plan.handle, 0, 16384, 16, 16, 16, 16, None) == 2
+
+
+# both streams in one call: (dtype, hidden, pack); the hidden sizes take the
+# paired LayerNorm backward (3072), the one-wave ones (520, 64) and the wide
+# rows' range-split sums (8192)
+BOTH_CASES = [("bf16", 3072, "mixed"), ("bf16", 520, "mixed"), ("f32", 64, "mixed"),
+              ("bf16", 8192, "mixed"), ("bf16", 3072, "text_only"),
+              ("bf16", 3072, "image_only")]
+BOTH_PACKS = {"mixed": PACK, "text_only": [(0, 0, 37), (0, 0, 5)],
+              "image_only": [(7, 9, 0), (3, 4, 0), (0, 0, 0)]}
+
+
+@pytest.mark.parametrize("dt,C,pack", BOTH_CASES)
+def test_chains_both_streams(dt, C, pack):
+    # one call over [text rows; image rows] with per-sample vectors [2B, C]:
+    # the row outputs equal the two one-stream calls bit for bit; the
+    # parameter gradients hold the oracle's sums (another fixed order) and
+    # repeat bit for bit
+    samples = BOTH_PACKS[pack]
+    say("chains both streams dt=%s hidden=%d pack=%s" % (dt, C, pack))
+    plan = pvj.Plan(samples, 2, 64, dt).upload()
+    nt, ni, B = plan.n_text, plan.n_image, len(samples)
+    x, xn = _draw(nt + ni, C, dt, 41, 2.0, 0.5)
+    y, yn = _draw(nt + ni, C, dt, 42)
+    dy, dyn = _draw(nt + ni, C, dt, 43)
+    sh, shn = _draw(2 * B, C, dt, 44, 0.5)
+    sc, scn = _draw(2 * B, C, dt, 45, 0.5)
+    g, gn = _draw(2 * B, C, dt, 46)
+    parts = (("text", slice(0, nt), slice(0, B), chains.TEXT),
+             ("image", slice(nt, nt + ni), slice(B, 2 * B), chains.IMAGE))
+
+    a = pvj.adaln_modulate(plan, "both", x, sh, sc)
+    o = pvj.gate_residual(plan, "both", x, y, g)
+    dx, dsh, dsc = pvj.adaln_modulate_bwd(plan, "both", x, sc, dy)
+    gy, dg = pvj.gate_residual_bwd(plan, "both", y, g, dy)
+    torch.cuda.synchronize()
+    for name, rs, vs, st in parts:
+        if rs.stop == rs.start:
+            continue
+        say("  %s stream" % name)
+        xs, ys, ds = x[rs].contiguous(), y[rs].contiguous(), dy[rs].contiguous()
+        assert torch.equal(a[rs], pvj.adaln_modulate(plan, name, xs, sh[vs].contiguous(),
+                                                     sc[vs].contiguous()))
+        assert torch.equal(o[rs], pvj.gate_residual(plan, name, xs, ys, g[vs].contiguous()))
+        ref_dx, _, _ = pvj.adaln_modulate_bwd(plan, name, xs, sc[vs].contiguous(), ds)
+        ref_gy, _ = pvj.gate_residual_bwd(plan, name, ys, g[vs].contiguous(), ds)
+        torch.cuda.synchronize()
+        assert torch.equal(dx[rs], ref_dx)
+        assert torch.equal(gy[rs], ref_gy)
+        # the parameter gradients against the oracle
+        xn_s, yn_s, dn_s = xn[rs], yn[rs], dyn[rs]
+        _, rdsh, rdsc = chains.adaln_modulate_bwd(xn_s, scn[vs], dn_s, samples, st)
+        _, _, rdg = chains.gate_residual_bwd(yn_s, gn[vs], dn_s, samples, st)
+        si = chains.stream_sample_index(samples, st)
+        xhat = chains.layer_norm_rows(xn_s)
+        _sum_bound(to_np(dsh[vs]), rdsh, _seg_sum(np.abs(dn_s), si, B))
+        _sum_bound(to_np(dsc[vs]), rdsc, _seg_sum(np.abs(dn_s * xhat), si, B))
+        _sum_bound(to_np(dg[vs]), rdg, _seg_sum(np.abs(dn_s * yn_s), si, B))
+    # segments without rows get zero gradients
+    for name, rs, vs, st in parts:
+        if rs.stop == rs.start:
+            assert not bool(dsh[vs].any()) and not bool(dsc[vs].any()) and not bool(dg[vs].any())
+    dx2, dsh2, dsc2 = pvj.adaln_modulate_bwd(plan, "both", x, sc, dy)
+    gy2, dg2 = pvj.gate_residual_bwd(plan, "both", y, g, dy)
+    torch.cuda.synchronize()
+    for u, w in ((dx, dx2), (dsh, dsh2), (dsc, dsc2), (gy, gy2), (dg, dg2)):
+        assert torch.equal(u, w)
