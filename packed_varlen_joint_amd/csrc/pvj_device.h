@@ -128,10 +128,8 @@ __device__ __forceinline__ int axis_pos(const RopePos& p, int axis) {
 // Rotate the 8 dims of unit u (pairs 4u .. 4u+3) at axis position pos with the
 // plan's cos/sin tables ([pos][D/2 pairs]); pairs (2k, 2k+1) turn as
 // (a, b) -> (a cos - b sin, a sin + b cos); inverse turns by -angle.
-__device__ __forceinline__ f32x8 rope_unit(f32x8 x, int u, int pos, const Meta& m, bool inverse) {
-  const size_t to = (size_t)pos * m.n_pairs + 4 * u;
-  const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
-  f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
+// the rotation of one unit by its table entries (cos, sin of the unit's four pairs)
+__device__ __forceinline__ f32x8 rope_rotate(f32x8 x, f32x4 cs, f32x4 sn, bool inverse) {
   if (inverse) sn = -sn;
   // explicit fma order, so every kernel that rotates rounds the same way
   f32x8 y;
@@ -142,6 +140,12 @@ __device__ __forceinline__ f32x8 rope_unit(f32x8 x, int u, int pos, const Meta& 
     y[2 * q + 1] = __builtin_fmaf(a, sn[q], b * cs[q]);
   }
   return y;
+}
+__device__ __forceinline__ f32x8 rope_unit(f32x8 x, int u, int pos, const Meta& m, bool inverse) {
+  const size_t to = (size_t)pos * m.n_pairs + 4 * u;
+  const f32x4 cs = *reinterpret_cast<const f32x4*>(m.cos_tab + to);
+  const f32x4 sn = *reinterpret_cast<const f32x4*>(m.sin_tab + to);
+  return rope_rotate(x, cs, sn, inverse);
 }
 
 // ---------------------------------------------------------------------------
