@@ -143,6 +143,21 @@ def test_pack_large_bit_exact():
     assert torch.equal(joint, torch.cat(parts))
     t2, i2 = pvj.unpack(plan, joint)
     assert torch.equal(t2, text) and torch.equal(i2, image)
+    # with RoPE at full size (most blocks lie inside one sample): the one-pass
+    # kernels equal pack then the standalone rotation, bit for bit, and the
+    # standalone rotation matches the oracle on sampled rows
+    say("pack/unpack with RoPE train_64k seed 1")
+    jr = pvj.rope2d_apply(plan, joint)
+    assert torch.equal(pvj.pack(plan, text, image, rope=True), jr)
+    t3, i3 = pvj.unpack(plan, jr, rope=True, inverse=True)
+    t4, i4 = pvj.unpack(plan, pvj.rope2d_apply(plan, jr, inverse=True))
+    assert torch.equal(t3, t4) and torch.equal(i3, i4)
+    rows = np.random.default_rng(3).choice(plan.n_tokens, 512, replace=False)
+    rows.sort()
+    pos = oracle.token_positions(wl.samples)[rows]
+    ref = oracle.rope2d_at(to_np(joint[torch.as_tensor(rows, device="cuda")]), pos)
+    got = to_np(jr[torch.as_tensor(rows, device="cuda")])
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
 
 
 # ----------------------------------------------------------------------------
