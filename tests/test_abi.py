@@ -387,3 +387,26 @@ def test_stream_major_row_map():
     perm = pvj.stream_major_rows(fr).tolist()
     assert perm == [0, 1, 2, 3, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20,
                     21, 22, 23, 24, 25, 26, 4, 5, 6, 7, 8]
+
+
+def test_chain_binding_checks_before_any_device_call(lib):
+    # the binding refuses a bad stream name and tensors of the wrong shape or
+    # device for the one-call form over both streams, before the library is
+    # called (CPU tensors here: no device is touched)
+    torch = pytest.importorskip("torch")
+    p = _plan([(3, 3, 2), (0, 0, 5), (4, 2, 0)], 2, 64, "bf16")
+    B, C = 3, 64
+    rows = p.n_text + p.n_image
+    x = torch.zeros(rows, C, dtype=torch.bfloat16)
+    v2 = torch.zeros(2 * B, C, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pvj.adaln_modulate(p, "bogus", x, v2, v2)
+    with pytest.raises(ValueError):   # per-sample vectors must be [2B, C] for both streams
+        pvj.adaln_modulate(p, "both", x, v2[:B], v2[:B])
+    with pytest.raises(ValueError):   # rows must be n_text + n_image
+        pvj.gate_residual(p, "both", x[:-1], x[:-1], v2)
+    with pytest.raises(ValueError):   # CPU tensors are refused
+        pvj.gate_residual(p, "both", x, x, v2)
+    assert pvj.chain_workspace_bytes(p, pvj.CHAIN_GATE, "both", C) > 0
+    with pytest.raises(ValueError):
+        pvj.chain_workspace_bytes(p, pvj.CHAIN_GATE, "neither", C)
