@@ -203,9 +203,11 @@ def test_chain_errors():
 # rows' range-split sums (8192)
 BOTH_CASES = [("bf16", 3072, "mixed"), ("bf16", 520, "mixed"), ("f32", 64, "mixed"),
               ("bf16", 8192, "mixed"), ("bf16", 3072, "text_only"),
-              ("bf16", 3072, "image_only")]
+              ("bf16", 3072, "image_only"), ("bf16", 2568, "frames")]
 BOTH_PACKS = {"mixed": PACK, "text_only": [(0, 0, 37), (0, 0, 5)],
-              "image_only": [(7, 9, 0), (3, 4, 0), (0, 0, 0)]}
+              "image_only": [(7, 9, 0), (3, 4, 0), (0, 0, 0)],
+              # an editing pack: samples of 0 to 3 frames
+              "frames": [(3, 5, 7, 2), (0, 0, 3, 0), (2, 4, 0, 3), (4, 4, 9, 1)]}
 
 
 @pytest.mark.parametrize("dt,C,pack", BOTH_CASES)
