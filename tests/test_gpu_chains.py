@@ -4,7 +4,9 @@ through the C ABI.
 
 Row outputs are compared element by element; the per-sample parameter
 gradients (fp32 sums over a sample's rows) against a bound scaled by the sum
-of the absolute terms, since their error is fp32 summation error.  Packs hold
+of the absolute terms, since their error is fp32 summation error.  Both
+streams in one call give the rows of the one-stream calls bit for bit, and
+NaN rows of one sample reach no other sample's rows or sums.  Packs hold
 empty, text-only and image-only samples and editing samples with frames; the
 hidden sizes span the minimum (8), a ragged 8-column tail of a 512-column
 reduction chunk, the backbone width (24 heads x 128 = 3072) and the maximum
@@ -265,3 +267,54 @@ def test_chains_both_streams(dt, C, pack):
     torch.cuda.synchronize()
     for u, w in ((dx, dx2), (dsh, dsh2), (dsc, dsc2), (gy, gy2), (dg, dg2)):
         assert torch.equal(u, w)
+
+
+@pytest.mark.parametrize("which", ["both", "image"])
+def test_chain_nan_rows_stay_in_their_sample(which):
+    # Sample 1's rows are NaN: every other sample's rows and parameter
+    # gradients must be finite and bitwise those of the same call with
+    # sample 1 finite (a slot's sums hold the rows of one sample only)
+    samples = [(9, 17, 33), (3, 4, 50), (0, 0, 70), (5, 7, 60), (6, 6, 0)]
+    C, B = 3072, len(samples)
+    plan = pvj.Plan(samples, 2, 64, "bf16").upload()
+    nt, ni = plan.n_text, plan.n_image
+    say("chain NaN isolation stream=%s" % which)
+    rows, nv = (nt + ni, 2 * B) if which == "both" else (ni, B)
+    x, _ = _draw(rows, C, "bf16", 51, 2.0, 0.5)
+    y, _ = _draw(rows, C, "bf16", 52)
+    dy, _ = _draw(rows, C, "bf16", 53)
+    sc, _ = _draw(nv, C, "bf16", 54, 0.5)
+    g, _ = _draw(nv, C, "bf16", 55)
+    # rows of sample 1 in this call's row order, and the rows of the others
+    tcu = np.concatenate([[0], np.cumsum([s[2] for s in samples])])
+    icu = np.concatenate([[0], np.cumsum([s[0] * s[1] for s in samples])])
+    def rows_of(i):
+        img = np.arange(icu[i], icu[i + 1]) + (nt if which == "both" else 0)
+        txt = np.arange(tcu[i], tcu[i + 1]) if which == "both" else np.arange(0)
+        return np.concatenate([txt, img]).astype(np.int64)
+    bad = torch.as_tensor(rows_of(1), device="cuda")
+    good = [i for i in range(B) if i != 1]
+    vec = lambda i: [i, B + i] if which == "both" else [i]
+
+    def run(poison):
+        xs, ys, ds = x.clone(), y.clone(), dy.clone()
+        if poison:
+            for t in (xs, ys, ds):
+                t[bad] = float("nan")
+        dx, dsh, dsc = pvj.adaln_modulate_bwd(plan, which, xs, sc, ds)
+        gy, dg = pvj.gate_residual_bwd(plan, which, ys, g, ds)
+        a = pvj.adaln_modulate(plan, which, xs, sc, sc)
+        o = pvj.gate_residual(plan, which, xs, ys, g)
+        torch.cuda.synchronize()
+        return (dx, gy, a, o), (dsh, dsc, dg)
+
+    (r0, p0), (r1, p1) = run(False), run(True)
+    for i in good:
+        rr = torch.as_tensor(rows_of(i), device="cuda")
+        for a, b in zip(r0, r1):
+            assert bool(torch.isfinite(b[rr].float()).all())
+            assert torch.equal(a[rr], b[rr])
+        for a, b in zip(p0, p1):
+            for j in vec(i):
+                assert bool(torch.isfinite(b[j]).all())
+                assert torch.equal(a[j], b[j])
